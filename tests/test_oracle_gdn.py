@@ -1,0 +1,133 @@
+"""Pins for the Gated DeltaNet oracle (CPU only)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import gdn as og
+from hybrid_model_ssm_amd import synth
+
+
+def _rand_step(rng, Bt, HV, HK, dk, dv):
+    q = rng.standard_normal((Bt, HK, dk))
+    k = rng.standard_normal((Bt, HK, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    return dict(q=q, k=k, v=rng.standard_normal((Bt, HV, dv)),
+                alpha=np.exp(-np.log1p(np.exp(rng.standard_normal((Bt, HV)) - 2))),
+                beta=1 / (1 + np.exp(-rng.standard_normal((Bt, HV)))))
+
+
+def test_hand_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "gdn_hand.json")))
+    S = np.array(g["S0"])[None, None]
+    rep = og.GDNReplay(S, g["buffer_len"], 1, scale=g["scale"])
+    for i, st in enumerate(g["steps"]):
+        q = np.array(st["q"])[None, None]
+        k = np.array(st["k"])[None, None]
+        v = np.array(st["v"])[None, None]
+        al = np.array([[st["alpha"]]])
+        be = np.array([[st["beta"]]])
+        S, o = og.conventional_step(S, q, k, v, al, be, scale=g["scale"])
+        assert np.allclose(S[0, 0], np.array(st["S"]), atol=1e-12)
+        assert np.allclose(o[0, 0], np.array(st["o"]), atol=1e-12)
+        ro, fl = rep.step(q, k, v, al, be)
+        assert np.allclose(ro[0, 0], np.array(st["o"]), atol=1e-12)
+        if fl[0]:
+            assert np.allclose(rep.ckpt[0, 0], np.array(st["S"]), atol=1e-12)
+
+
+def test_value_heads_share_key_heads():
+    kq = np.arange(2 * 3, dtype=float).reshape(1, 2, 3)
+    e = og.heads_of_kgroups(kq, 4)
+    assert np.array_equal(e[0, 1], kq[0, 0]) and np.array_equal(e[0, 2], kq[0, 1])
+
+
+def test_beta_zero_is_pure_decay():
+    rng = np.random.default_rng(20)
+    Bt, HV, HK, dk, dv = 2, 4, 2, 5, 3
+    S0 = 0.1 * rng.standard_normal((Bt, HV, dv, dk))
+    rep = og.GDNReplay(S0, 4, HK)
+    S = S0.copy()
+    prod = np.ones((Bt, HV))
+    for t in range(7):
+        s = _rand_step(rng, Bt, HV, HK, dk, dv)
+        s["beta"][:] = 0.0
+        prod *= s["alpha"]
+        S, o = og.conventional_step(S, **s)
+        ro, _ = rep.step(**s)
+        qh = np.repeat(s["q"], HV // HK, axis=1)
+        ref = og.default_scale(dk) * prod[:, :, None] * np.einsum("bhij,bhj->bhi", S0, qh)
+        assert np.allclose(o, ref, atol=1e-14)
+        assert np.allclose(ro, ref, atol=1e-14)
+
+
+def test_delta_rule_writes_value_exactly():
+    # alpha = beta = 1 and a unit axis key: S_t k_t = v_t, so q = k reads back scale * v.
+    rng = np.random.default_rng(21)
+    Bt, HV, HK, dk, dv = 1, 2, 1, 4, 3
+    S0 = rng.standard_normal((Bt, HV, dv, dk))
+    rep = og.GDNReplay(S0, 3, HK)
+    S = S0.copy()
+    for t in range(5):
+        j = t % dk
+        k = np.zeros((Bt, HK, dk)); k[..., j] = 1.0
+        v = rng.standard_normal((Bt, HV, dv))
+        one = np.ones((Bt, HV))
+        S, o = og.conventional_step(S, k, k, v, one, one)
+        ro, _ = rep.step(k, k, v, one, one)
+        assert np.array_equal(o, og.default_scale(dk) * v)
+        assert np.allclose(ro, og.default_scale(dk) * v, atol=1e-13)
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 5])
+def test_replay_matches_conventional(L):
+    rng = np.random.default_rng(22)
+    Bt, HV, HK, dk, dv = 2, 4, 2, 6, 5
+    S0 = 0.1 * rng.standard_normal((Bt, HV, dv, dk))
+    rep = og.GDNReplay(S0, L, HK)
+    S = S0.copy()
+    for t in range(1, 21):
+        s = _rand_step(rng, Bt, HV, HK, dk, dv)
+        S, o = og.conventional_step(S, **s)
+        ro, fl = rep.step(**s)
+        assert np.max(np.abs(ro - o)) <= 1e-12
+        assert bool(fl.all()) == (t % L == 0)
+        if t % L == 0:
+            assert np.max(np.abs(rep.ckpt - S)) <= 1e-12
+
+
+def test_matrix_fold_matches_rowwise_updates_and_partial_flush():
+    rng = np.random.default_rng(23)
+    Bt, HV, HK, dk, dv = 1, 2, 1, 4, 3
+    S0 = rng.standard_normal((Bt, HV, dv, dk))
+    rep = og.GDNReplay(S0, 8, HK)
+    S = S0.copy()
+    for t in range(5):
+        s = _rand_step(rng, Bt, HV, HK, dk, dv)
+        # row-wise form of one step: S[i,:] <- alpha (S[i,:] - beta (S[i,:].k) k) + beta v[i] k
+        kh = np.repeat(s["k"], HV // HK, axis=1)
+        for h in range(HV):
+            for i in range(dv):
+                row = S[0, h, i]
+                S[0, h, i] = s["alpha"][0, h] * (row - s["beta"][0, h] * (row @ kh[0, h]) * kh[0, h]) \
+                    + s["beta"][0, h] * s["v"][0, h, i] * kh[0, h]
+        rep.step(**s)
+    assert list(rep.cursor) == [5]
+    rep.flush()
+    assert np.max(np.abs(rep.ckpt - S)) <= 1e-12
+    before = rep.ckpt.copy()
+    rep.flush()
+    assert np.array_equal(rep.ckpt, before)
+
+
+def test_synth_gdn_inputs_shapes_and_ranges():
+    gen = synth.GDNInputs(4, 4, 2, 8, 8, io="bf16", seed=5)
+    s = gen.step()
+    assert s["q"].shape == (4, 2, 8) and s["v"].shape == (4, 4, 8)
+    assert np.all((s["beta"] > 0) & (s["beta"] < 1))
+    assert np.all((s["alpha"] > 0) & (s["alpha"] < 1))
+    assert np.allclose(np.linalg.norm(s["k"].astype(np.float64), axis=-1), 1.0, atol=1e-2)
+    assert np.array_equal(synth.round_bf16(s["q"]), s["q"])
