@@ -1,0 +1,315 @@
+// C ABI of libreplayssm: host-side validation and kernel dispatch.
+// Every check runs before the first HIP call; a failed check launches nothing.
+
+#include <stdint.h>
+
+#include <climits>
+
+#include "../../include/replayssm.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQ(cond)                                          \
+    do {                                                   \
+        if (!(cond)) return REPLAYSSM_ERR_INVALID_ARGUMENT; \
+    } while (0)
+
+replayssm_status hip_status(hipError_t e) { return e == hipSuccess ? REPLAYSSM_OK : REPLAYSSM_ERR_HIP; }
+
+size_t io_size(replayssm_dtype t) { return t == REPLAYSSM_BF16 ? 2 : 4; }
+
+replayssm_status check_mamba2_desc(const replayssm_mamba2_desc* d, bool need_L) {
+    REQ(d != nullptr);
+    REQ(d->batch >= 1 && d->nheads >= 1 && d->ngroups >= 1 && d->headdim >= 1 && d->dstate >= 1);
+    REQ(d->nheads % d->ngroups == 0);
+    REQ(d->io_dtype == REPLAYSSM_F32 || d->io_dtype == REPLAYSSM_BF16);
+    if (need_L) REQ(d->buffer_len >= 1 && d->buffer_len <= REPLAYSSM_MAX_BUFFER_LEN);
+    REQ((int64_t)d->batch * d->nheads <= INT_MAX / REPLAYSSM_MAX_BUFFER_LEN);
+    if (!rssm::mamba2_shape_supported(d->headdim, d->dstate)) return REPLAYSSM_ERR_UNSUPPORTED;
+    return REPLAYSSM_OK;
+}
+
+replayssm_status check_mamba2_state(const replayssm_mamba2_desc* d, const replayssm_mamba2_state* s) {
+    REQ(s != nullptr);
+    REQ(s->ckpt && s->rec_x && s->rec_B && s->rec_dt);
+    REQ(aligned(s->ckpt, 16) && aligned(s->rec_x, 16) && aligned(s->rec_B, 16) && aligned(s->rec_dt, 4));
+    REQ(s->ckpt_lp == nullptr || aligned(s->ckpt_lp, 16));
+    REQ(s->ckpt_lp != (void*)s->ckpt);
+    (void)d;
+    return REPLAYSSM_OK;
+}
+
+replayssm_status check_mamba2_inputs(const replayssm_mamba2_desc* d, const void* x, const void* z,
+                                     const void* B, const void* C, const void* dt_raw,
+                                     const float* dt_bias, const float* A, const float* D,
+                                     const float* out) {
+    REQ(x && z && B && C && dt_raw && dt_bias && A && D && out);
+    REQ(aligned(x, 16) && aligned(z, 16) && aligned(B, 16) && aligned(C, 16));
+    REQ(aligned(dt_raw, io_size(d->io_dtype)) && aligned(dt_bias, 4) && aligned(A, 4) &&
+        aligned(D, 4) && aligned(out, 4));
+    return REPLAYSSM_OK;
+}
+
+rssm::Mamba2Args mamba2_args(const replayssm_mamba2_desc* d, const replayssm_mamba2_state* s) {
+    rssm::Mamba2Args a{};
+    a.ckpt = s->ckpt;
+    a.ckpt_lp = static_cast<uint16_t*>(s->ckpt_lp);
+    a.rec_x = s->rec_x;
+    a.rec_B = s->rec_B;
+    a.rec_dt = s->rec_dt;
+    a.batch = d->batch;
+    a.nheads = d->nheads;
+    a.headdim = d->headdim;
+    a.dstate = d->dstate;
+    a.ngroups = d->ngroups;
+    a.L = d->buffer_len;
+    a.dt_softplus = d->dt_softplus ? 1 : 0;
+    return a;
+}
+
+replayssm_status check_gdn_desc(const replayssm_gdn_desc* d, bool need_L) {
+    REQ(d != nullptr);
+    REQ(d->batch >= 1 && d->num_v_heads >= 1 && d->num_k_heads >= 1 && d->dk >= 1 && d->dv >= 1);
+    REQ(d->num_v_heads % d->num_k_heads == 0);
+    REQ(d->io_dtype == REPLAYSSM_F32 || d->io_dtype == REPLAYSSM_BF16);
+    REQ(d->scale >= 0.0f && d->scale < 1e30f);
+    if (need_L) REQ(d->buffer_len >= 1 && d->buffer_len <= REPLAYSSM_MAX_BUFFER_LEN);
+    REQ((int64_t)d->batch * d->num_v_heads * 2 <= INT_MAX / REPLAYSSM_MAX_BUFFER_LEN);
+    if (!rssm::gdn_shape_supported(d->dk, d->dv)) return REPLAYSSM_ERR_UNSUPPORTED;
+    return REPLAYSSM_OK;
+}
+
+rssm::GdnArgs gdn_args(const replayssm_gdn_desc* d) {
+    rssm::GdnArgs a{};
+    a.batch = d->batch;
+    a.hv = d->num_v_heads;
+    a.hk = d->num_k_heads;
+    a.dk = d->dk;
+    a.dv = d->dv;
+    a.L = d->buffer_len;
+    a.scale = d->scale > 0.0f ? d->scale : 1.0f / __builtin_sqrtf((float)d->dk);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* replayssm_status_string(replayssm_status status) {
+    switch (status) {
+        case REPLAYSSM_OK: return "ok";
+        case REPLAYSSM_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case REPLAYSSM_ERR_UNSUPPORTED: return "unsupported shape";
+        case REPLAYSSM_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+int32_t replayssm_version(void) { return 100; }
+
+replayssm_status replayssm_mamba2_decode(const replayssm_mamba2_desc* desc,
+                                         const replayssm_mamba2_state* state,
+                                         const int32_t* cursor_in, int32_t* cursor_out,
+                                         const void* x, const void* z, const void* B,
+                                         const void* C, const void* dt_raw, const float* dt_bias,
+                                         const float* A, const float* D, float* out,
+                                         int32_t* err_flags, hipStream_t stream) {
+    replayssm_status st = check_mamba2_desc(desc, true);
+    if (st != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_state(desc, state)) != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_inputs(desc, x, z, B, C, dt_raw, dt_bias, A, D, out)) != REPLAYSSM_OK) return st;
+    REQ(cursor_in && cursor_out && cursor_in != cursor_out);
+    REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
+    if (rssm::mamba2_replay_smem_bytes(desc->headdim, desc->dstate, desc->buffer_len, 0) >
+        rssm::mamba2_max_smem_bytes())
+        return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::Mamba2Args a = mamba2_args(desc, state);
+    a.cursor_in = cursor_in;
+    a.cursor_out = cursor_out;
+    a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
+    a.n_pos = 1;
+    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, 0, stream));
+}
+
+replayssm_status replayssm_mamba2_flush(const replayssm_mamba2_desc* desc,
+                                        const replayssm_mamba2_state* state,
+                                        const int32_t* cursor_in, int32_t* cursor_out,
+                                        const float* A, int32_t* err_flags, hipStream_t stream) {
+    replayssm_status st = check_mamba2_desc(desc, true);
+    if (st != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_state(desc, state)) != REPLAYSSM_OK) return st;
+    REQ(A && aligned(A, 4));
+    REQ(cursor_in && cursor_out && cursor_in != cursor_out);
+    REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
+    if (rssm::mamba2_replay_smem_bytes(desc->headdim, desc->dstate, desc->buffer_len, 0) >
+        rssm::mamba2_max_smem_bytes())
+        return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::Mamba2Args a = mamba2_args(desc, state);
+    a.cursor_in = cursor_in;
+    a.cursor_out = cursor_out;
+    a.A = A;
+    a.err_flags = err_flags;
+    a.n_pos = 0;
+    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, 1, stream));
+}
+
+replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
+                                              const replayssm_mamba2_state* state,
+                                              const int32_t* head, const int32_t* committed,
+                                              int32_t n_pos, const void* x, const void* z,
+                                              const void* B, const void* C, const void* dt_raw,
+                                              const float* dt_bias, const float* A, const float* D,
+                                              float* out, int32_t* flushed, int32_t* err_flags,
+                                              hipStream_t stream) {
+    replayssm_status st = check_mamba2_desc(desc, true);
+    if (st != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_state(desc, state)) != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_inputs(desc, x, z, B, C, dt_raw, dt_bias, A, D, out)) != REPLAYSSM_OK) return st;
+    REQ(n_pos >= 1 && n_pos <= desc->buffer_len);
+    REQ((int64_t)desc->batch * n_pos * desc->nheads <= INT_MAX / 2);
+    REQ(head && committed && flushed && head != committed);
+    REQ((const int32_t*)flushed != head && (const int32_t*)flushed != committed);
+    REQ(aligned(head, 4) && aligned(committed, 4) && aligned(flushed, 4) && aligned(err_flags, 4));
+    if (rssm::mamba2_replay_smem_bytes(desc->headdim, desc->dstate, desc->buffer_len, n_pos) >
+        rssm::mamba2_max_smem_bytes())
+        return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::Mamba2Args a = mamba2_args(desc, state);
+    a.cursor_in = head;
+    a.committed = committed;
+    a.flushed = flushed;
+    a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
+    a.n_pos = n_pos;
+    hipError_t e = rssm::launch_mamba2_replay(a, desc->io_dtype, 2, stream);
+    if (e != hipSuccess) return REPLAYSSM_ERR_HIP;
+    return hip_status(rssm::launch_mamba2_spec_append_B(a, desc->io_dtype, stream));
+}
+
+replayssm_status replayssm_commit(int32_t batch, int32_t buffer_len, int32_t n_pos, int32_t* head,
+                                  int32_t* committed, const int32_t* flushed, const int32_t* n_keep,
+                                  int32_t* err_flags, hipStream_t stream) {
+    REQ(batch >= 1 && buffer_len >= 1 && buffer_len <= REPLAYSSM_MAX_BUFFER_LEN);
+    REQ(n_pos >= 1 && n_pos <= buffer_len);
+    REQ(head && committed && flushed && n_keep && head != committed);
+    REQ(aligned(head, 4) && aligned(committed, 4) && aligned(flushed, 4) && aligned(n_keep, 4) &&
+        aligned(err_flags, 4));
+    return hip_status(rssm::launch_commit(batch, buffer_len, n_pos, head, committed, flushed, n_keep,
+                                          err_flags, stream));
+}
+
+replayssm_status replayssm_reset_cursors(int32_t batch, int32_t* head, int32_t* cursor,
+                                         const int32_t* seq_idx, int32_t n_seq, hipStream_t stream) {
+    REQ(batch >= 1 && cursor && head != cursor);
+    REQ(aligned(head, 4) && aligned(cursor, 4) && aligned(seq_idx, 4));
+    if (seq_idx == nullptr) n_seq = batch;
+    REQ(n_seq >= 0);
+    return hip_status(rssm::launch_reset(batch, head, cursor, seq_idx, n_seq, stream));
+}
+
+replayssm_status replayssm_selective_state_update(const replayssm_mamba2_desc* desc, float* state,
+                                                  const void* x, const void* z, const void* B,
+                                                  const void* C, const void* dt_raw,
+                                                  const float* dt_bias, const float* A,
+                                                  const float* D, float* out, hipStream_t stream) {
+    replayssm_status st = check_mamba2_desc(desc, false);
+    if (st != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_inputs(desc, x, z, B, C, dt_raw, dt_bias, A, D, out)) != REPLAYSSM_OK) return st;
+    REQ(state && aligned(state, 16));
+    rssm::Mamba2ConvArgs a{};
+    a.state = state;
+    a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out;
+    a.batch = desc->batch; a.nheads = desc->nheads; a.headdim = desc->headdim;
+    a.dstate = desc->dstate; a.ngroups = desc->ngroups; a.dt_softplus = desc->dt_softplus ? 1 : 0;
+    a.n_pos = 1;
+    return hip_status(rssm::launch_mamba2_conventional(a, desc->io_dtype, false, stream));
+}
+
+replayssm_status replayssm_mamba2_spec_baseline(const replayssm_mamba2_desc* desc, float* snapshots,
+                                                const int32_t* slot_in, int32_t n_pos,
+                                                const void* x, const void* z, const void* B,
+                                                const void* C, const void* dt_raw,
+                                                const float* dt_bias, const float* A,
+                                                const float* D, float* out, hipStream_t stream) {
+    replayssm_status st = check_mamba2_desc(desc, false);
+    if (st != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_inputs(desc, x, z, B, C, dt_raw, dt_bias, A, D, out)) != REPLAYSSM_OK) return st;
+    REQ(snapshots && aligned(snapshots, 16) && slot_in && aligned(slot_in, 4));
+    REQ(n_pos >= 1 && n_pos <= REPLAYSSM_MAX_BUFFER_LEN);
+    REQ((int64_t)desc->batch * n_pos * desc->nheads <= INT_MAX / 2);
+    rssm::Mamba2ConvArgs a{};
+    a.state = snapshots;
+    a.slot_in = slot_in;
+    a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out;
+    a.batch = desc->batch; a.nheads = desc->nheads; a.headdim = desc->headdim;
+    a.dstate = desc->dstate; a.ngroups = desc->ngroups; a.dt_softplus = desc->dt_softplus ? 1 : 0;
+    a.n_pos = n_pos;
+    return hip_status(rssm::launch_mamba2_conventional(a, desc->io_dtype, true, stream));
+}
+
+replayssm_status replayssm_gdn_decode(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
+                                      const int32_t* cursor_in, int32_t* cursor_out, const void* q,
+                                      const void* k, const void* v, const float* alpha,
+                                      const float* beta, float* out, int32_t* err_flags,
+                                      hipStream_t stream) {
+    replayssm_status st = check_gdn_desc(desc, true);
+    if (st != REPLAYSSM_OK) return st;
+    REQ(state && state->ckpt && state->rec_k && state->rec_v && state->rec_alpha && state->rec_beta);
+    REQ(aligned(state->ckpt, 16) && aligned(state->rec_k, 16) && aligned(state->rec_v, 16) &&
+        aligned(state->rec_alpha, 4) && aligned(state->rec_beta, 4));
+    REQ(q && k && v && alpha && beta && out);
+    REQ(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(alpha, 4) && aligned(beta, 4) &&
+        aligned(out, 4));
+    REQ(cursor_in && cursor_out && cursor_in != cursor_out);
+    REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
+    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len) > rssm::mamba2_max_smem_bytes())
+        return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::GdnArgs a = gdn_args(desc);
+    a.ckpt = state->ckpt; a.rec_k = state->rec_k; a.rec_v = state->rec_v;
+    a.rec_alpha = state->rec_alpha; a.rec_beta = state->rec_beta;
+    a.cursor_in = cursor_in; a.cursor_out = cursor_out;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out; a.err_flags = err_flags;
+    return hip_status(rssm::launch_gdn_replay(a, desc->io_dtype, 0, stream));
+}
+
+replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
+                                     const int32_t* cursor_in, int32_t* cursor_out, int32_t* err_flags,
+                                     hipStream_t stream) {
+    replayssm_status st = check_gdn_desc(desc, true);
+    if (st != REPLAYSSM_OK) return st;
+    REQ(state && state->ckpt && state->rec_k && state->rec_v && state->rec_alpha && state->rec_beta);
+    REQ(aligned(state->ckpt, 16) && aligned(state->rec_k, 16) && aligned(state->rec_v, 16) &&
+        aligned(state->rec_alpha, 4) && aligned(state->rec_beta, 4));
+    REQ(cursor_in && cursor_out && cursor_in != cursor_out);
+    REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
+    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len) > rssm::mamba2_max_smem_bytes())
+        return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::GdnArgs a = gdn_args(desc);
+    a.ckpt = state->ckpt; a.rec_k = state->rec_k; a.rec_v = state->rec_v;
+    a.rec_alpha = state->rec_alpha; a.rec_beta = state->rec_beta;
+    a.cursor_in = cursor_in; a.cursor_out = cursor_out; a.err_flags = err_flags;
+    return hip_status(rssm::launch_gdn_replay(a, desc->io_dtype, 1, stream));
+}
+
+replayssm_status replayssm_gdn_conventional_decode(const replayssm_gdn_desc* desc, float* state,
+                                                   const void* q, const void* k, const void* v,
+                                                   const float* alpha, const float* beta,
+                                                   float* out, hipStream_t stream) {
+    replayssm_status st = check_gdn_desc(desc, false);
+    if (st != REPLAYSSM_OK) return st;
+    REQ(state && aligned(state, 16));
+    REQ(q && k && v && alpha && beta && out);
+    REQ(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(alpha, 4) && aligned(beta, 4) &&
+        aligned(out, 4));
+    rssm::GdnArgs a = gdn_args(desc);
+    a.ckpt = state;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out;
+    return hip_status(rssm::launch_gdn_conventional(a, desc->io_dtype, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace rssm {
+
+enum IoType { kIoF32 = 0, kIoBF16 = 1 };
+
+struct Mamba2Args {
+    float* ckpt;          // [B,H,P,N] f32
+    uint16_t* ckpt_lp;    // [B,H,P,N] bf16 or null
+    void* rec_x;          // [B,H,L,P] io
+    void* rec_B;          // [B,G,L,N] io
+    float* rec_dt;        // [B,H,L]
+    const int32_t* cursor_in;   // AR cursor, or the speculative head
+    int32_t* cursor_out;        // AR only
+    const int32_t* committed;   // speculative only
+    int32_t* flushed;           // speculative only
+    const void* x;        // [B,(T,)H,P]
+    const void* z;        // [B,(T,)H,P]
+    const void* B;        // [B,(T,)G,N]
+    const void* C;        // [B,(T,)G,N]
+    const void* dt_raw;   // [B,(T,)H]
+    const float* dt_bias; // [H]
+    const float* A;       // [H]
+    const float* D;       // [H]
+    float* out;           // [B,(T,)H,P]
+    int32_t* err_flags;
+    int32_t batch, nheads, headdim, dstate, ngroups, L, dt_softplus, n_pos;
+};
+
+// Conventional read-update-write step (and the per-position snapshot baseline).
+struct Mamba2ConvArgs {
+    float* state;           // [B,H,P,N], or snapshots [B,T,H,P,N]
+    const int32_t* slot_in; // snapshot baseline only
+    const void* x;
+    const void* z;
+    const void* B;
+    const void* C;
+    const void* dt_raw;
+    const float* dt_bias;
+    const float* A;
+    const float* D;
+    float* out;
+    int32_t batch, nheads, headdim, dstate, ngroups, dt_softplus, n_pos;
+};
+
+struct GdnArgs {
+    float* ckpt;          // [B,HV,dv,dk]
+    void* rec_k;          // [B,HK,L,dk]
+    void* rec_v;          // [B,HV,L,dv]
+    float* rec_alpha;     // [B,HV,L]
+    float* rec_beta;      // [B,HV,L]
+    const int32_t* cursor_in;
+    int32_t* cursor_out;
+    const void* q;        // [B,HK,dk]
+    const void* k;        // [B,HK,dk]
+    const void* v;        // [B,HV,dv]
+    const float* alpha;   // [B,HV]
+    const float* beta;    // [B,HV]
+    float* out;           // [B,HV,dv]
+    int32_t* err_flags;
+    int32_t batch, hv, hk, dk, dv, L;
+    float scale;
+};
+
+bool mamba2_shape_supported(int headdim, int dstate);
+size_t mamba2_replay_smem_bytes(int headdim, int dstate, int L, int n_pos);
+size_t mamba2_max_smem_bytes();
+
+// mode: 0 = AR decode step, 1 = fold stored records only (flush), 2 = speculative verify
+hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int mode, hipStream_t stream);
+hipError_t launch_mamba2_spec_append_B(const Mamba2Args& a, int io, hipStream_t stream);
+hipError_t launch_mamba2_conventional(const Mamba2ConvArgs& a, int io, bool snapshots,
+                                      hipStream_t stream);
+
+hipError_t launch_commit(int32_t batch, int32_t L, int32_t n_pos, int32_t* head,
+                         int32_t* committed, const int32_t* flushed, const int32_t* n_keep,
+                         int32_t* err_flags, hipStream_t stream);
+hipError_t launch_reset(int32_t batch, int32_t* head, int32_t* cursor, const int32_t* seq_idx,
+                        int32_t n_seq, hipStream_t stream);
+
+bool gdn_shape_supported(int dk, int dv);
+size_t gdn_smem_bytes(int dk, int dv, int L);
+// mode: 0 = AR decode, 1 = fold stored records only
+hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t stream);
+hipError_t launch_gdn_conventional(const GdnArgs& a, int io, hipStream_t stream);
+
+}  // namespace rssm

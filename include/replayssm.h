@@ -1,0 +1,314 @@
+/*
+ * replayssm.h -- C ABI of the ReplaySSM decode library for AMD Instinct MI355X (gfx950).
+ *
+ * ReplaySSM keeps the recurrent state of a state-space (SSM) layer as a checkpoint
+ * plus a bounded buffer of recent input records ("ReplaySSM Caches Inputs Instead of
+ * State to Speed Up Hybrid-Model Decoding", section "How ReplaySSM works").  On a
+ * non-flush step the kernel appends the step's record and computes the output from
+ * the checkpoint and the buffer without storing a state; when the buffer of L
+ * records fills, the flush step folds the records into the checkpoint and stores it
+ * once.  Speculative verification appends draft records and is output-only; rollback
+ * moves a cursor ("ReplaySSM" README, benefit "Cheap rollback").  An optional bf16
+ * read copy of the checkpoint serves non-flush reads while the fp32 checkpoint
+ * carries the recurrence (same README, benefit "Separate state precisions").  The
+ * entry points follow the kernels listed in "ReplaySSM (a vLLM research fork)",
+ * section "Core implementation files".
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * - Every pointer argument is a DEVICE pointer owned by the caller, except the
+ *   descriptor and state structs themselves, which are host memory read during the
+ *   call only.  The library never allocates or frees memory, keeps no mutable
+ *   global state and never synchronises: each call enqueues its kernels on `stream`
+ *   and returns.  Buffers must stay alive until that stream work has finished.
+ * - Arrays are dense and row-major with the last dimension contiguous, in the
+ *   shapes written next to each argument ([batch, nheads, headdim] and so on).
+ * - Alignment: the checkpoint and its bf16 copy must be 16-byte aligned; every
+ *   other array must be aligned to its element size.
+ * - Errors: every entry point validates its arguments on the host before it touches
+ *   the GPU.  On REPLAYSSM_ERR_INVALID_ARGUMENT or REPLAYSSM_ERR_UNSUPPORTED nothing
+ *   is launched and nothing is written.  REPLAYSSM_ERR_HIP reports a launch failure
+ *   (hipGetLastError) after the enqueue.
+ * - Device-side errors: `err_flags` (may be NULL) points to one int32 word.  A
+ *   kernel that meets a cursor outside its documented range ORs
+ *   REPLAYSSM_DEVERR_CURSOR into it, skips that sequence (its outputs, records and
+ *   checkpoint are left untouched) and copies the bad cursor to the output cursor
+ *   unchanged.  The caller clears the word.
+ * - Reentrancy: functions are reentrant and thread-safe; calls on one stream are
+ *   ordered by the stream.
+ * - Determinism: reductions use no atomics; the same inputs give bit-identical
+ *   outputs.
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    REPLAYSSM_OK = 0,
+    REPLAYSSM_ERR_INVALID_ARGUMENT = 1, /* null required pointer, bad size, misalignment, aliasing */
+    REPLAYSSM_ERR_UNSUPPORTED = 2,      /* a shape outside the compiled set (see each call) */
+    REPLAYSSM_ERR_HIP = 3               /* the HIP runtime rejected the launch */
+} replayssm_status;
+
+typedef enum {
+    REPLAYSSM_F32 = 0,
+    REPLAYSSM_BF16 = 1
+} replayssm_dtype;
+
+enum { REPLAYSSM_DEVERR_CURSOR = 1 };
+
+/* Largest buffer length (window L) the kernels accept. */
+#define REPLAYSSM_MAX_BUFFER_LEN 64
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* replayssm_status_string(replayssm_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t replayssm_version(void);
+
+/* ======================================================================================
+ * Mamba2
+ * ====================================================================================== */
+
+/*
+ * Shapes of one Mamba2 SSM layer.  Head h reads the B/C vectors of group
+ * g = h / (nheads / ngroups) (consecutive heads share a group).
+ *
+ *   batch        >= 1
+ *   nheads       >= 1, a multiple of ngroups
+ *   headdim (P)  in {16, 32, 64, 128};  dstate (N) in {16, 32, 64, 128, 256};
+ *                headdim*dstate <= 16384                       (else UNSUPPORTED)
+ *   buffer_len   window L, 1 <= L <= REPLAYSSM_MAX_BUFFER_LEN
+ *   io_dtype     dtype of x, z, B, C, dt_raw and of the x/B records
+ *   dt_softplus  nonzero: dt = softplus(dt_raw + dt_bias); zero: dt = dt_raw + dt_bias
+ */
+typedef struct {
+    int32_t batch, nheads, headdim, dstate, ngroups, buffer_len;
+    replayssm_dtype io_dtype;
+    int32_t dt_softplus;
+} replayssm_mamba2_desc;
+
+/*
+ * Per-layer decode state.  The record buffer ("ring") has buffer_len slots per
+ * sequence.  Autoregressive decode keeps records in slots 0..cursor-1; speculative
+ * decode uses the slots circularly from `head`.
+ *
+ *   ckpt     f32  [batch, nheads, headdim, dstate]   fp32 checkpoint (required)
+ *   ckpt_lp  bf16 [batch, nheads, headdim, dstate]   optional read copy, or NULL.
+ *            When set, non-flush steps read it instead of ckpt; every flush reads
+ *            ckpt, writes ckpt and refreshes ckpt_lp (round to nearest even).
+ *   rec_x    io   [batch, nheads, buffer_len, headdim]   x records (exact copies)
+ *   rec_B    io   [batch, ngroups, buffer_len, dstate]   B records (exact copies)
+ *   rec_dt   f32  [batch, nheads, buffer_len]            dt after softplus
+ */
+typedef struct {
+    float* ckpt;
+    void* ckpt_lp;
+    void* rec_x;
+    void* rec_B;
+    float* rec_dt;
+} replayssm_mamba2_state;
+
+/*
+ * One autoregressive decode step, output-only route ("How ReplaySSM works":
+ * non-flush steps append the inputs and compute the output from the checkpoint
+ * and the buffer without storing a state; the step that fills the buffer folds
+ * it into the checkpoint and stores the checkpoint once).
+ *
+ * For every sequence b with c = cursor_in[b] (0 <= c < L):
+ *   window = the c stored records followed by this step's record (x_t, B_t, dt_t);
+ *   lam_s  = sum of dt over the window records after s;  decay = exp(A[h] * sum dt);
+ *   w_s    = dt_s * exp(A[h] * lam_s);
+ *   y      = decay * (ckpt . C_t) + sum_s w_s (B_s . C_t) x_s + D[h] x_t;
+ *   out    = y * z * sigmoid(z).
+ *   If c + 1 < L: the record is stored in slot c; cursor_out[b] = c + 1; the
+ *   checkpoint is not written.
+ *   If c + 1 == L (flush): ckpt <- decay * ckpt + sum_s w_s outer(x_s, B_s) is
+ *   stored (and ckpt_lp refreshed); y is read from the new checkpoint
+ *   (y = ckpt_new . C_t + D[h] x_t); cursor_out[b] = 0.
+ * Sequences flush independently, so one call may mix flush and non-flush
+ * sequences.
+ *
+ *   cursor_in  int32 [batch]  read only;  cursor_out int32 [batch]  written.
+ *              They must be distinct arrays (ping-pong between steps).
+ *   x, z       io [batch, nheads, headdim];  B, C io [batch, ngroups, dstate];
+ *   dt_raw     io [batch, nheads];  dt_bias, A, D f32 [nheads];
+ *   out        f32 [batch, nheads, headdim];  err_flags int32 [1] or NULL.
+ */
+replayssm_status replayssm_mamba2_decode(const replayssm_mamba2_desc* desc,
+                                         const replayssm_mamba2_state* state,
+                                         const int32_t* cursor_in, int32_t* cursor_out,
+                                         const void* x, const void* z, const void* B,
+                                         const void* C, const void* dt_raw,
+                                         const float* dt_bias, const float* A, const float* D,
+                                         float* out, int32_t* err_flags, hipStream_t stream);
+
+/*
+ * Fold the 0..L-1 records each sequence holds into its checkpoint (same fold as
+ * the flush step, over the stored records only), refresh ckpt_lp when it is set,
+ * and set cursor_out[b] = 0.  With c = 0 the checkpoint is left bit-unchanged and
+ * only ckpt_lp is (re)created, which is how the bf16 copy is initialised.  Used to
+ * hand a sequence's whole state over (checkpoint save, migration).
+ *   cursor_in, cursor_out  int32 [batch], distinct;  A f32 [nheads].
+ */
+replayssm_status replayssm_mamba2_flush(const replayssm_mamba2_desc* desc,
+                                        const replayssm_mamba2_state* state,
+                                        const int32_t* cursor_in, int32_t* cursor_out,
+                                        const float* A, int32_t* err_flags, hipStream_t stream);
+
+/*
+ * Speculative verification over n_pos positions (the last accepted token and the
+ * drafts) on the circular buffer ("ReplaySSM" README, benefit "Cheap rollback";
+ * "How ReplaySSM works": draft inputs are appended to the buffer instead of
+ * snapshotting the state).
+ *
+ * Per sequence b, with hd = head[b] (0 <= hd < L), cm = committed[b]
+ * (0 <= cm <= L) and 1 <= n_pos <= L:
+ *   if cm + n_pos > L the cm committed records (slots (hd + i) % L) are folded into
+ *   the checkpoint, which is stored (and ckpt_lp refreshed), flushed[b] = 1 and the
+ *   window starts empty; otherwise flushed[b] = 0 and the checkpoint is not written.
+ *   Position j's record is written to slot (hd + cm + j) % L and its output is the
+ *   replay output over the committed records (none after a flush) followed by
+ *   positions 0..j.  One checkpoint read serves all n_pos outputs.
+ * head and committed are NOT changed here; replayssm_commit applies the round.
+ *
+ *   x, z   io [batch, n_pos, nheads, headdim];  B, C io [batch, n_pos, ngroups, dstate];
+ *   dt_raw io [batch, n_pos, nheads];  out f32 [batch, n_pos, nheads, headdim];
+ *   flushed int32 [batch] written;  head, committed int32 [batch] read only.
+ */
+replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
+                                              const replayssm_mamba2_state* state,
+                                              const int32_t* head, const int32_t* committed,
+                                              int32_t n_pos,
+                                              const void* x, const void* z, const void* B,
+                                              const void* C, const void* dt_raw,
+                                              const float* dt_bias, const float* A,
+                                              const float* D, float* out, int32_t* flushed,
+                                              int32_t* err_flags, hipStream_t stream);
+
+/*
+ * Apply a verified round: for each b, if flushed[b] then head[b] = (head[b] +
+ * committed[b]) % buffer_len and committed[b] = 0; then committed[b] += n_keep[b].
+ * n_keep[b] (1 <= n_keep <= n_pos) is the kept prefix (last accepted token plus the
+ * accepted drafts).  Rejected records are dropped by not counting them; no state
+ * is touched.  A sequence whose n_keep is out of range or whose result would exceed
+ * buffer_len is left unchanged and REPLAYSSM_DEVERR_CURSOR is ORed into err_flags.
+ *   head, committed int32 [batch] read-write;  flushed, n_keep int32 [batch].
+ */
+replayssm_status replayssm_commit(int32_t batch, int32_t buffer_len, int32_t n_pos,
+                                  int32_t* head, int32_t* committed, const int32_t* flushed,
+                                  const int32_t* n_keep, int32_t* err_flags, hipStream_t stream);
+
+/*
+ * Reset cursors for new sequences: head[b] = 0 (when head is not NULL) and
+ * cursor[b] = 0, for b in seq_idx[0..n_seq-1] (seq_idx NULL: every b < batch).
+ * `cursor` is the committed count (speculative) or the AR cursor.  Indices outside
+ * [0, batch) are ignored.  The caller supplies the new sequence's checkpoint.
+ */
+replayssm_status replayssm_reset_cursors(int32_t batch, int32_t* head, int32_t* cursor,
+                                         const int32_t* seq_idx, int32_t n_seq,
+                                         hipStream_t stream);
+
+/*
+ * Conventional read-update-write decode step, the baseline the method is measured
+ * against ("Why SSM layers slow down hybrid models": each step loads and stores the
+ * full state).  state f32 [batch, nheads, headdim, dstate] is updated in place:
+ *   h = exp(dt*A) h + dt outer(x, B);  y = h . C + D x;  out = y * z * sigmoid(z).
+ * desc->buffer_len is ignored.  Other arguments as in replayssm_mamba2_decode.
+ */
+replayssm_status replayssm_selective_state_update(const replayssm_mamba2_desc* desc, float* state,
+                                                  const void* x, const void* z, const void* B,
+                                                  const void* C, const void* dt_raw,
+                                                  const float* dt_bias, const float* A,
+                                                  const float* D, float* out, hipStream_t stream);
+
+/*
+ * Conventional speculative baseline: one state snapshot per position ("Why SSM
+ * layers slow down hybrid models": engines store a snapshot after every draft
+ * token, one read and T writes per step).  Reads snapshot slot_in[b] of
+ * snapshots f32 [batch, n_pos, nheads, headdim, dstate], runs the n_pos updates in
+ * order and writes the state after position j into slot j; outputs as
+ * replayssm_mamba2_spec_verify.  The next round passes slot_in[b] = n_keep[b] - 1.
+ */
+replayssm_status replayssm_mamba2_spec_baseline(const replayssm_mamba2_desc* desc, float* snapshots,
+                                                const int32_t* slot_in, int32_t n_pos,
+                                                const void* x, const void* z, const void* B,
+                                                const void* C, const void* dt_raw,
+                                                const float* dt_bias, const float* A,
+                                                const float* D, float* out, hipStream_t stream);
+
+/* ======================================================================================
+ * Gated DeltaNet
+ * ====================================================================================== */
+
+/*
+ * Shapes of one Gated DeltaNet layer.  Value head hv reads q/k head
+ * hv / (num_v_heads / num_k_heads).
+ *   dk, dv in {64, 128} (else UNSUPPORTED);  1 <= buffer_len <= REPLAYSSM_MAX_BUFFER_LEN;
+ *   io_dtype: dtype of q, k, v and of the k/v records;
+ *   scale: output scale; 0 means 1/sqrt(dk).
+ */
+typedef struct {
+    int32_t batch, num_v_heads, num_k_heads, dk, dv, buffer_len;
+    replayssm_dtype io_dtype;
+    float scale;
+} replayssm_gdn_desc;
+
+/*
+ *   ckpt       f32 [batch, num_v_heads, dv, dk]
+ *   rec_k      io  [batch, num_k_heads, buffer_len, dk]
+ *   rec_v      io  [batch, num_v_heads, buffer_len, dv]
+ *   rec_alpha  f32 [batch, num_v_heads, buffer_len]
+ *   rec_beta   f32 [batch, num_v_heads, buffer_len]
+ */
+typedef struct {
+    float* ckpt;
+    void* rec_k;
+    void* rec_v;
+    float* rec_alpha;
+    float* rec_beta;
+} replayssm_gdn_state;
+
+/*
+ * One autoregressive Gated DeltaNet decode step in replay form (the GDN
+ * autoregressive kernel of "Core implementation files"; mechanism of "How
+ * ReplaySSM works").  The gated delta rule is
+ *   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = scale S_t q_t.
+ * Without storing S_t the output is o = scale (ckpt u + acc), where q is carried
+ * back through the window (newest record first):
+ *   kappa = k_s . u;  acc += beta_s kappa v_s;  u = alpha_s (u - beta_s kappa k_s).
+ * Flush (c + 1 == L): the window's updates are applied to the checkpoint row by row
+ * in order and the checkpoint is stored once; o is read from the new checkpoint.
+ *
+ *   cursor_in/out int32 [batch] (distinct);  q, k io [batch, num_k_heads, dk];
+ *   v io [batch, num_v_heads, dv];  alpha, beta f32 [batch, num_v_heads];
+ *   out f32 [batch, num_v_heads, dv].
+ */
+replayssm_status replayssm_gdn_decode(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
+                                      const int32_t* cursor_in, int32_t* cursor_out,
+                                      const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta, float* out,
+                                      int32_t* err_flags, hipStream_t stream);
+
+/* Fold the 0..L-1 stored GDN records into the checkpoint; cursor_out[b] = 0. */
+replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
+                                     const int32_t* cursor_in, int32_t* cursor_out,
+                                     int32_t* err_flags, hipStream_t stream);
+
+/* Conventional GDN step: state f32 [batch, num_v_heads, dv, dk] updated in place. */
+replayssm_status replayssm_gdn_conventional_decode(const replayssm_gdn_desc* desc, float* state,
+                                                   const void* q, const void* k, const void* v,
+                                                   const float* alpha, const float* beta,
+                                                   float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPLAYSSM_H */

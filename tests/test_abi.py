@@ -1,0 +1,198 @@
+"""Host-side tests of the C ABI: the library loads, exports every function that
+include/replayssm.h declares, and rejects invalid arguments before touching the GPU.
+
+No call here reaches a kernel launch: every call carries at least one invalid
+argument, and the pointers are fake addresses that are never dereferenced.  The
+module is skipped where a GPU is visible so that a regression in the validation
+could never launch a kernel on fake pointers.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from hybrid_model_ssm_amd import replayssm as rs  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "replayssm.h")
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(), reason="host-only ABI checks")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rs.LIB_PATH):
+        from hybrid_model_ssm_amd import build
+        build.build()
+    return rs.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int32_t|replayssm_status)\s+(replayssm_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("replayssm_mamba2_decode", "replayssm_mamba2_flush", "replayssm_mamba2_spec_verify",
+              "replayssm_commit", "replayssm_reset_cursors", "replayssm_gdn_decode", "replayssm_gdn_flush",
+              "replayssm_selective_state_update"):
+        assert n in names
+    assert set(names) == set(rs.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert rs.status_string(0) == "ok"
+    assert rs.status_string(1) == "invalid argument"
+    assert rs.status_string(2) == "unsupported shape"
+    assert rs.status_string(3) == "HIP launch failure"
+    assert rs.status_string(99) == "unknown status"
+    assert rs.version() == 100
+
+
+# fake, 256-byte aligned device addresses (never dereferenced)
+def fake(i):
+    return 0x7f0000000000 + 0x100000 * i
+
+
+def m2desc(**kw):
+    d = dict(batch=4, nheads=8, headdim=64, dstate=128, ngroups=2, buffer_len=16, io_dtype=rs.BF16,
+             dt_softplus=1)
+    d.update(kw)
+    return rs.Mamba2DescC(**d)
+
+
+def m2state(**kw):
+    d = dict(ckpt=fake(1), ckpt_lp=None, rec_x=fake(2), rec_B=fake(3), rec_dt=fake(4))
+    d.update(kw)
+    return rs.Mamba2StateC(**d)
+
+
+def decode(L, desc=None, state=None, **kw):
+    a = dict(cin=fake(5), cout=fake(6), x=fake(7), z=fake(8), B=fake(9), C=fake(10), dt=fake(11),
+             bias=fake(12), A=fake(13), D=fake(14), out=fake(15), err=None)
+    a.update(kw)
+    desc = desc if desc is not None else m2desc()
+    state = state if state is not None else m2state()
+    return L.replayssm_mamba2_decode(ctypes.byref(desc), ctypes.byref(state), a["cin"], a["cout"], a["x"],
+                                     a["z"], a["B"], a["C"], a["dt"], a["bias"], a["A"], a["D"], a["out"],
+                                     a["err"], None)
+
+
+INV, UNS = rs.ERR_INVALID_ARGUMENT, rs.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("desc_kw,expect", [
+    (dict(batch=0), INV), (dict(nheads=0), INV), (dict(ngroups=3), INV), (dict(buffer_len=0), INV),
+    (dict(buffer_len=65), INV), (dict(io_dtype=7), INV), (dict(headdim=48), UNS), (dict(dstate=24), UNS),
+    (dict(headdim=128, dstate=256), UNS), (dict(headdim=0), INV),
+])
+def test_mamba2_decode_rejects_bad_desc(L, desc_kw, expect):
+    # a bad x pointer as well, so that no variant could ever launch
+    assert decode(L, desc=m2desc(**desc_kw), x=None) in (expect, INV)
+    assert decode(L, desc=m2desc(**desc_kw), cout=fake(5)) == expect
+
+
+def test_mamba2_decode_rejects_bad_pointers(L):
+    assert L.replayssm_mamba2_decode(None, ctypes.byref(m2state()), *([fake(1)] * 11), None, None) == INV
+    assert decode(L, state=m2state(ckpt=None), cout=fake(5)) == INV
+    assert decode(L, state=m2state(ckpt=fake(1) + 4), cout=fake(5)) == INV      # 16-byte alignment
+    assert decode(L, state=m2state(ckpt_lp=fake(20) + 8), cout=fake(5)) == INV
+    assert decode(L, state=m2state(ckpt_lp=fake(1)), cout=fake(5)) == INV        # copy aliases ckpt
+    assert decode(L, state=m2state(rec_B=None), cout=fake(5)) == INV
+    assert decode(L, cout=fake(5)) == INV                                         # cursor_in == cursor_out
+    assert decode(L, cin=None) == INV
+    assert decode(L, x=fake(7) + 2, cout=fake(5)) == INV
+    assert decode(L, out=fake(15) + 1, cout=fake(5)) == INV
+    assert decode(L, D=None, cout=fake(5)) == INV
+    assert decode(L, err=fake(16) + 2, cout=fake(5)) == INV
+
+
+def test_mamba2_smem_limit_is_unsupported(L):
+    # dstate 256, headdim 64, L=64: the staged window exceeds 64 KiB of LDS
+    assert decode(L, desc=m2desc(dstate=256, buffer_len=64)) == UNS
+
+
+def test_mamba2_flush_and_spec_validation(L):
+    d, s = m2desc(), m2state()
+    assert L.replayssm_mamba2_flush(ctypes.byref(d), ctypes.byref(s), fake(5), fake(5), fake(13), None, None) == INV
+    assert L.replayssm_mamba2_flush(ctypes.byref(d), ctypes.byref(s), fake(5), fake(6), None, None, None) == INV
+
+    def spec(n_pos, head=fake(5), com=fake(6), flushed=fake(17), x=fake(7)):
+        return L.replayssm_mamba2_spec_verify(ctypes.byref(d), ctypes.byref(s), head, com, n_pos, x, fake(8),
+                                              fake(9), fake(10), fake(11), fake(12), fake(13), fake(14),
+                                              fake(15), flushed, None, None)
+    assert spec(0, x=None) == INV
+    assert spec(17, x=None) == INV
+    assert spec(4, head=fake(6), x=None) == INV
+    assert spec(4, flushed=fake(5), x=None) == INV
+    assert spec(0) == INV and spec(17) == INV and spec(4, head=fake(6)) == INV and spec(4, flushed=fake(6)) == INV
+
+
+def test_cursor_call_validation(L):
+    C = L.replayssm_commit
+    assert C(0, 16, 4, fake(1), fake(2), fake(3), fake(4), None, None) == INV
+    assert C(4, 0, 1, fake(1), fake(2), fake(3), fake(4), None, None) == INV
+    assert C(4, 16, 17, fake(1), fake(2), fake(3), fake(4), None, None) == INV
+    assert C(4, 16, 0, fake(1), fake(2), fake(3), fake(4), None, None) == INV
+    assert C(4, 16, 4, fake(1), fake(1), fake(3), fake(4), None, None) == INV
+    assert C(4, 16, 4, fake(1), fake(2), None, fake(4), None, None) == INV
+    R = L.replayssm_reset_cursors
+    assert R(0, fake(1), fake(2), None, 0, None) == INV
+    assert R(4, fake(1), None, None, 0, None) == INV
+    assert R(4, fake(1), fake(1), None, 0, None) == INV
+    assert R(4, fake(1), fake(2), fake(3), -1, None) == INV
+
+
+def test_conventional_validation(L):
+    d = m2desc(buffer_len=0)   # ignored by the conventional call
+    args = [fake(i) for i in range(7, 16)]
+    assert L.replayssm_selective_state_update(ctypes.byref(d), None, *args, None) == INV
+    assert L.replayssm_selective_state_update(ctypes.byref(m2desc(ngroups=3)), fake(1), *args, None) == INV
+    assert L.replayssm_mamba2_spec_baseline(ctypes.byref(d), fake(1), fake(2), 0, *args, None) == INV
+    assert L.replayssm_mamba2_spec_baseline(ctypes.byref(d), fake(1), None, 4, *args, None) == INV
+
+
+def gdesc(**kw):
+    d = dict(batch=4, num_v_heads=8, num_k_heads=4, dk=128, dv=128, buffer_len=16, io_dtype=rs.BF16, scale=0.0)
+    d.update(kw)
+    return rs.GdnDescC(**d)
+
+
+def test_gdn_validation(L):
+    s = rs.GdnStateC(fake(1), fake(2), fake(3), fake(4), fake(5))
+
+    def dec(desc, cin=fake(6), cout=fake(7), q=fake(8)):
+        return L.replayssm_gdn_decode(ctypes.byref(desc), ctypes.byref(s), cin, cout, q, fake(9), fake(10),
+                                      fake(11), fake(12), fake(13), None, None)
+    assert dec(gdesc(num_k_heads=3), cout=fake(6)) == INV
+    assert dec(gdesc(dk=96), cout=fake(6)) == UNS
+    assert dec(gdesc(dv=32), cout=fake(6)) == UNS
+    assert dec(gdesc(buffer_len=0), cout=fake(6)) == INV
+    assert dec(gdesc(scale=-1.0), cout=fake(6)) == INV
+    assert dec(gdesc(), cout=fake(6)) == INV
+    assert dec(gdesc(), q=None) == INV
+    assert dec(gdesc(), q=fake(8) + 4, cout=fake(6)) == INV
+    assert L.replayssm_gdn_flush(ctypes.byref(gdesc()), ctypes.byref(s), fake(6), fake(6), None, None) == INV
+    assert L.replayssm_gdn_conventional_decode(ctypes.byref(gdesc()), None, fake(8), fake(9), fake(10),
+                                               fake(11), fake(12), fake(13), None) == INV
+
+
+def test_binding_refuses_host_tensors(L):
+    desc = rs.Mamba2Desc(1, 1, 16, 16, 1, 4, rs.F32)
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        rs._ptr(t, torch.float32, "t")
+    with pytest.raises(TypeError):
+        rs._ptr([1, 2], None, "t")
+    assert desc.c().headdim == 16

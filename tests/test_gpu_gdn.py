@@ -1,0 +1,152 @@
+"""GPU parity: Gated DeltaNet replay decode and the conventional GDN kernel against the
+fp64 oracle (max |d| <= 1e-4 (1 + |ref|); cursors bit for bit)."""
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_model_ssm_amd import replayssm as rs
+from hybrid_model_ssm_amd import synth
+from oracle import gdn as og
+from tests.gpu_helpers import DEV, assert_fp32_close, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class GpuGdn:
+    def __init__(self, desc, static):
+        self.desc = desc
+        B = desc.batch
+        self.state = rs.GdnState.allocate(desc, ckpt=to_dev(static.ckpt, torch.float32))
+        self.cur = [torch.zeros(B, dtype=torch.int32, device=DEV), torch.zeros(B, dtype=torch.int32, device=DEV)]
+        self.flip = 0
+        self.out = torch.empty(B, desc.num_v_heads, desc.dv, dtype=torch.float32, device=DEV)
+        self.err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.conv_state = to_dev(static.ckpt, torch.float32)
+        self.conv_out = torch.empty_like(self.out)
+
+    @property
+    def cursor(self):
+        return self.cur[self.flip]
+
+    def _in(self, s):
+        io = self.desc.torch_io
+        return ([to_dev(s[k], io) for k in ("q", "k", "v")] +
+                [to_dev(s[k], torch.float32) for k in ("alpha", "beta")])
+
+    def step(self, s):
+        q, k, v, al, be = self._in(s)
+        rs.gdn_decode(self.desc, self.state, self.cur[self.flip], self.cur[1 - self.flip], q, k, v, al, be,
+                      self.out, self.err)
+        self.flip ^= 1
+        return self.out
+
+    def conventional(self, s):
+        q, k, v, al, be = self._in(s)
+        rs.gdn_conventional_decode(self.desc, self.conv_state, q, k, v, al, be, self.conv_out)
+        return self.conv_out
+
+    def flush(self):
+        rs.gdn_flush(self.desc, self.state, self.cur[self.flip], self.cur[1 - self.flip], self.err)
+        self.flip ^= 1
+
+
+SHAPES = [  # B, HV, HK, dk, dv, L, io
+    (2, 4, 2, 64, 64, 4, "f32"),
+    (3, 4, 4, 128, 128, 5, "bf16"),
+    (2, 6, 2, 128, 64, 4, "bf16"),
+    (2, 2, 1, 64, 128, 3, "f32"),
+    (4, 8, 4, 128, 128, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}HV{}HK{}dk{}dv{}L{}{}".format(*s))
+def test_gdn_replay_and_conventional(shape):
+    B, HV, HK, dk, dv, L, io = shape
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io=io, seed=31)
+    st = gen.static
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16 if io == "bf16" else rs.F32)
+    gpu = GpuGdn(desc, st)
+    rep = og.GDNReplay(st.ckpt, L, HK)
+    S = st.ckpt.astype(np.float64)
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        S, ref = og.conventional_step(S, **s)
+        rref, _ = rep.step(**s)
+        out = gpu.step(s).cpu().numpy()
+        assert_fp32_close(out, ref, f"{shape} replay step {t}")
+        assert_fp32_close(out, rref, f"{shape} replay vs replay-oracle step {t}")
+        assert_fp32_close(gpu.conventional(s).cpu().numpy(), ref, f"{shape} conventional step {t}")
+        assert_fp32_close(gpu.conv_state.cpu().numpy(), S, f"{shape} conventional state step {t}")
+        assert np.array_equal(gpu.cursor.cpu().numpy(), np.full(B, t % L, np.int32))
+        if t % L == 0:
+            assert_fp32_close(gpu.state.ckpt.cpu().numpy(), S, f"{shape} checkpoint step {t}")
+    assert gpu.err.item() == 0
+
+
+def test_gdn_full_size_sampled():
+    """B=256, 32 value heads over 16 q/k heads, dk=dv=128, L=16: 2L+2 steps, 8 sampled
+    sequences against the oracle."""
+    w = synth.WORKLOADS["gdn_hv32"]
+    gen = synth.gdn_inputs("gdn_hv32")
+    st = gen.static
+    B, L = w["batch"], w["buffer_len"]
+    desc = rs.GdnDesc(B, w["num_v_heads"], w["num_k_heads"], w["dk"], w["dv"], L, rs.BF16)
+    gpu = GpuGdn(desc, st)
+    sample = np.array([0, 2, 50, 127, 128, 199, 254, 255])
+    rep = og.GDNReplay(st.ckpt[sample], L, w["num_k_heads"])
+    S = st.ckpt[sample].astype(np.float64)
+    idx = torch.from_numpy(sample).to(DEV)
+    for t in range(1, 2 * L + 3):
+        s = gen.step()
+        ss = {k: v[sample] for k, v in s.items()}
+        ref, _ = rep.step(**ss)
+        S, _ = og.conventional_step(S, **ss)
+        out = gpu.step(s)
+        assert_fp32_close(out[idx].cpu().numpy(), ref, f"step {t}")
+        assert torch.equal(gpu.cursor, torch.full((B,), t % L, dtype=torch.int32, device=DEV))
+        if t % L == 0:
+            assert_fp32_close(gpu.state.ckpt[idx].cpu().numpy(), S, f"checkpoint step {t}")
+
+
+def test_gdn_explicit_flush_and_bad_cursor():
+    B, HV, HK, dk, dv, L = 3, 4, 2, 128, 128, 16
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=32)
+    st = gen.static
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    gpu = GpuGdn(desc, st)
+    S = st.ckpt.astype(np.float64)
+    for t in range(6):
+        s = gen.step()
+        S, _ = og.conventional_step(S, **s)
+        gpu.step(s)
+    gpu.flush()
+    assert gpu.cursor.cpu().tolist() == [0] * B
+    assert_fp32_close(gpu.state.ckpt.cpu().numpy(), S, "explicit flush")
+    ck = gpu.state.ckpt.clone()
+    gpu.flush()
+    assert torch.equal(gpu.state.ckpt, ck)
+    gpu.cur[gpu.flip].copy_(torch.tensor([0, -1, 2], dtype=torch.int32))
+    gpu.out.fill_(7.0)
+    gpu.step(gen.step())
+    assert gpu.err.item() & rs.DEVERR_CURSOR
+    assert torch.all(gpu.out[1] == 7.0)
+    assert gpu.cursor.cpu().tolist() == [1, -1, 3]
+
+
+def test_gdn_L1_equals_conventional_kernel():
+    B, HV, HK, dk, dv = 2, 4, 2, 128, 128
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=33)
+    st = gen.static
+    gpu = GpuGdn(rs.GdnDesc(B, HV, HK, dk, dv, 1, rs.BF16), st)
+    for t in range(5):
+        s = gen.step()
+        o = gpu.step(s).clone()
+        c = gpu.conventional(s)
+        assert_fp32_close(o.cpu().numpy(), c.cpu().numpy(), f"step {t}", rel=1e-5)
+        assert_fp32_close(gpu.state.ckpt.cpu().numpy(), gpu.conv_state.cpu().numpy(), f"state {t}", rel=1e-5)

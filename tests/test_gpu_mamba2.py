@@ -1,0 +1,278 @@
+"""GPU parity: Mamba2 autoregressive replay decode (HIP, through the C ABI) against
+the fp64 oracle.  Outputs and flushed checkpoints: max |d| <= 1e-4 (1 + |ref|)
+elementwise (fp32 reads); max |d| <= 2e-2 RMS(ref) per step (bf16 reads).
+Cursors are compared bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_model_ssm_amd import replayssm as rs
+from hybrid_model_ssm_amd import synth
+from oracle import mamba2 as om
+from tests.gpu_helpers import (DEV, GpuConventional, GpuMamba2, assert_fp32_close, require_gpu,
+                               rms_violation, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _gen(B, H, P, N, G, io, seed):
+    return synth.Mamba2Inputs(B, H, P, N, G, io=io, seed=seed)
+
+
+def _desc(B, H, P, N, G, L, io):
+    return rs.Mamba2Desc(B, H, P, N, G, L, rs.BF16 if io == "bf16" else rs.F32, True)
+
+
+def test_tiny_workload_every_step():
+    """B=2, H=4, P=16, N=16, G=1, L=4, 64 steps, f32 inputs: outputs every step,
+    cursors, and every flushed checkpoint against the conventional state."""
+    w = synth.WORKLOADS["mamba2_tiny"]
+    gen = synth.mamba2_inputs("mamba2_tiny")
+    st = gen.static
+    desc = _desc(w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"], w["buffer_len"], w["io"])
+    gpu = GpuMamba2(desc, st)
+    conv = GpuConventional(desc, st)
+    h = st.ckpt.astype(np.float64)
+    rep = om.Mamba2Replay(st.ckpt, w["buffer_len"], st.A, st.D, st.dt_bias, w["ngroups"])
+    L = w["buffer_len"]
+    for t in range(1, w["steps"] + 1):
+        s = gen.step()
+        h, ref = om.conventional_step(h, **s, dt_bias=st.dt_bias, A=st.A, D=st.D)
+        rref, _ = rep.step(**s)
+        out = gpu.step(s).cpu().numpy()
+        cout = conv.step(s).cpu().numpy()
+        assert_fp32_close(out, ref, f"replay step {t}")
+        assert_fp32_close(out, rref, f"replay vs replay-oracle step {t}")
+        assert_fp32_close(cout, ref, f"conventional step {t}")
+        assert_fp32_close(conv.state.cpu().numpy(), h, f"conventional state step {t}")
+        assert np.array_equal(gpu.cursor.cpu().numpy(), np.full(w["batch"], t % L, np.int32))
+        if t % L == 0:
+            assert_fp32_close(gpu.state.ckpt.cpu().numpy(), h, f"checkpoint after flush at step {t}")
+    assert gpu.err.item() == 0
+
+
+SHAPES = [  # (B, H, P, N, G, L, io)
+    (3, 4, 16, 16, 2, 4, "f32"),
+    (2, 4, 32, 32, 1, 5, "bf16"),
+    (2, 4, 64, 64, 2, 3, "bf16"),
+    (3, 5, 64, 128, 1, 4, "bf16"),     # grid of 15 workgroups: not a multiple of 8
+    (2, 4, 128, 128, 2, 4, "f32"),
+    (2, 4, 64, 256, 2, 4, "bf16"),
+    (2, 4, 16, 128, 2, 4, "f32"),
+    (2, 4, 128, 16, 2, 4, "bf16"),
+    (2, 4, 128, 32, 4, 4, "bf16"),
+    (4, 8, 64, 128, 2, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}P{}N{}G{}L{}{}".format(*s))
+def test_shapes_and_tiles(shape):
+    B, H, P, N, G, L, io = shape
+    gen = _gen(B, H, P, N, G, io, seed=11)
+    st = gen.static
+    desc = _desc(B, H, P, N, G, L, io)
+    gpu = GpuMamba2(desc, st)
+    conv = GpuConventional(desc, st)
+    h = st.ckpt.astype(np.float64)
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        h, ref = om.conventional_step(h, **s, dt_bias=st.dt_bias, A=st.A, D=st.D)
+        assert_fp32_close(gpu.step(s).cpu().numpy(), ref, f"{shape} step {t}")
+        assert_fp32_close(conv.step(s).cpu().numpy(), ref, f"{shape} conventional step {t}")
+        if t % L == 0:
+            assert_fp32_close(gpu.state.ckpt.cpu().numpy(), h, f"{shape} checkpoint step {t}")
+    assert np.array_equal(gpu.cursor.cpu().numpy(), np.full(B, (2 * L + 1) % L, np.int32))
+
+
+def test_mixed_cursor_phases_with_preloaded_records():
+    """Sequences start at different cursors with records already in their buffers, so
+    one launch mixes flushing and non-flushing sequences."""
+    B, H, P, N, G, L = 6, 4, 64, 128, 2, 8
+    rng = np.random.default_rng(5)
+    gen = _gen(B, H, P, N, G, "bf16", seed=12)
+    st = gen.static
+    desc = _desc(B, H, P, N, G, L, "bf16")
+    gpu = GpuMamba2(desc, st)
+    rep = om.Mamba2Replay(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    cursors = np.array([0, 7, 3, 6, 1, 7], np.int32)
+    rec_x = synth.round_bf16(rng.standard_normal((B, H, L, P)).astype(np.float32))
+    rec_B = synth.round_bf16((rng.standard_normal((B, G, L, N)) / np.sqrt(N)).astype(np.float32))
+    rec_dt = rng.uniform(1e-3, 1e-1, (B, H, L)).astype(np.float32)
+    gpu.state.rec_x.copy_(to_dev(rec_x, torch.bfloat16))
+    gpu.state.rec_B.copy_(to_dev(rec_B, torch.bfloat16))
+    gpu.state.rec_dt.copy_(to_dev(rec_dt, torch.float32))
+    gpu.cur[0].copy_(torch.from_numpy(cursors))
+    for b in range(B):
+        rep.records[b] = [(rec_x[b, :, s], rec_B[b, :, s], rec_dt[b, :, s]) for s in range(cursors[b])]
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        ref, flushed = rep.step(**s)
+        assert_fp32_close(gpu.step(s).cpu().numpy(), ref, f"step {t}")
+        assert np.array_equal(gpu.cursor.cpu().numpy(), rep.cursor)
+        for b in np.nonzero(flushed)[0]:
+            assert_fp32_close(gpu.state.ckpt[b].cpu().numpy(), rep.ckpt[b], f"seq {b} checkpoint step {t}")
+
+
+@pytest.mark.parametrize("name", ["mamba2_h64", "mamba2_h128"])
+def test_full_size_sampled_sequences(name):
+    """Full workload shape (B=256, fp32 checkpoint of 2 or 4 MiB per sequence, L=16)
+    for 2L+2 steps; every output of 8 sampled sequences (first and last included)
+    against the oracle, all cursors bit for bit."""
+    w = synth.WORKLOADS[name]
+    gen = synth.mamba2_inputs(name)
+    st = gen.static
+    B, L = w["batch"], w["buffer_len"]
+    desc = _desc(B, w["nheads"], w["headdim"], w["dstate"], w["ngroups"], L, w["io"])
+    gpu = GpuMamba2(desc, st)
+    sample = np.array([0, 1, 37, 100, 128, 201, 254, 255])
+    rep = om.Mamba2Replay(st.ckpt[sample], L, st.A, st.D, st.dt_bias, w["ngroups"])
+    h = st.ckpt[sample].astype(np.float64)
+    for t in range(1, 2 * L + 3):
+        s = gen.step()
+        ss = {k: v[sample] for k, v in s.items()}
+        ref, _ = rep.step(**ss)
+        h, _ = om.conventional_step(h, **ss, dt_bias=st.dt_bias, A=st.A, D=st.D)
+        out = gpu.step(s)
+        assert_fp32_close(out[torch.from_numpy(sample).to(DEV)].cpu().numpy(), ref, f"{name} step {t}")
+        assert torch.equal(gpu.cursor, torch.full((B,), t % L, dtype=torch.int32, device=DEV))
+        if t % L == 0:
+            assert_fp32_close(gpu.state.ckpt[torch.from_numpy(sample).to(DEV)].cpu().numpy(), h,
+                              f"{name} checkpoint step {t}")
+    assert gpu.err.item() == 0
+
+
+def test_full_batch_small_heads():
+    """Every sequence of a B=256 batch (H=16, G=2, P=64, N=128, L=16) for 2L+1 steps."""
+    B, H, P, N, G, L = 256, 16, 64, 128, 2, 16
+    gen = _gen(B, H, P, N, G, "bf16", seed=13)
+    st = gen.static
+    gpu = GpuMamba2(_desc(B, H, P, N, G, L, "bf16"), st)
+    h = st.ckpt.astype(np.float64)
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        h, ref = om.conventional_step(h, **s, dt_bias=st.dt_bias, A=st.A, D=st.D)
+        assert_fp32_close(gpu.step(s).cpu().numpy(), ref, f"step {t}")
+        if t % L == 0:
+            assert_fp32_close(gpu.state.ckpt.cpu().numpy(), h, f"checkpoint step {t}")
+
+
+def test_bf16_read_copy():
+    """bf16 read copy: outputs within 2e-2 RMS of the oracle, and the fp32 checkpoint
+    trajectory bit-identical to the fp32-read run (rounding of the read copy never
+    enters the recurrence)."""
+    B, H, P, N, G, L = 16, 16, 64, 128, 2, 16
+    gen = _gen(B, H, P, N, G, "bf16", seed=14)
+    st = gen.static
+    desc = _desc(B, H, P, N, G, L, "bf16")
+    lp = GpuMamba2(desc, st, lowp=True)
+    fp = GpuMamba2(desc, st)
+    # the copy is created by a flush of an empty buffer: RNE of the fp32 checkpoint
+    assert torch.equal(lp.state.ckpt_lp, lp.state.ckpt.to(torch.bfloat16))
+    assert torch.equal(lp.state.ckpt, fp.state.ckpt)
+    rep = om.Mamba2Replay(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    worst = 0.0
+    for t in range(1, 3 * L + 2):
+        s = gen.step()
+        ref, _ = rep.step(**s)
+        o_lp = lp.step(s).cpu().numpy()
+        o_fp = fp.step(s).cpu().numpy()
+        v = rms_violation(o_lp, ref)
+        worst = max(worst, v)
+        assert v <= 1.0, f"step {t}: max|d| / (2e-2 RMS) = {v:.3g}"
+        assert_fp32_close(o_fp, ref, f"fp32 step {t}")
+        if t % L == 0:
+            assert torch.equal(lp.state.ckpt, fp.state.ckpt), f"fp32 trajectories differ at step {t}"
+            assert torch.equal(lp.state.ckpt_lp, lp.state.ckpt.to(torch.bfloat16))
+    print(f"bf16-read worst max|d|/(2e-2 RMS) = {worst:.3g}")
+
+
+def test_L1_equals_conventional_kernel():
+    B, H, P, N, G = 4, 8, 64, 128, 2
+    gen = _gen(B, H, P, N, G, "bf16", seed=15)
+    st = gen.static
+    desc = _desc(B, H, P, N, G, 1, "bf16")
+    gpu = GpuMamba2(desc, st)
+    conv = GpuConventional(desc, st)
+    for t in range(6):
+        s = gen.step()
+        o = gpu.step(s).clone()
+        c = conv.step(s)
+        assert_fp32_close(o.cpu().numpy(), c.cpu().numpy(), f"L=1 output step {t}", rel=1e-6)
+        assert_fp32_close(gpu.state.ckpt.cpu().numpy(), conv.state.cpu().numpy(), f"L=1 state {t}", rel=1e-6)
+
+
+def test_dt_zero_keeps_checkpoint_and_B_zero_decays():
+    B, H, P, N, G, L = 2, 4, 64, 128, 2, 4
+    gen = _gen(B, H, P, N, G, "f32", seed=16)
+    st = gen.static
+    desc = rs.Mamba2Desc(B, H, P, N, G, L, rs.F32, False)
+    gpu = GpuMamba2(desc, st)
+    ck0 = gpu.state.ckpt.clone()
+    for t in range(2 * L):
+        s = gen.step()
+        s["dt_raw"] = np.broadcast_to(-st.dt_bias, (B, H)).astype(np.float32).copy()
+        gpu.step(s)
+    assert torch.equal(gpu.state.ckpt, ck0)
+    # B = 0: pure decay of the checkpoint
+    gpu2 = GpuMamba2(_desc(B, H, P, N, G, L, "f32"), st)
+    dtsum = np.zeros((B, H))
+    for t in range(L):
+        s = gen.step()
+        s["B"][:] = 0.0
+        dtsum += om.softplus(s["dt_raw"].astype(np.float64) + st.dt_bias)
+        gpu2.step(s)
+    ref = np.exp(st.A[None, :] * dtsum)[:, :, None, None] * st.ckpt
+    assert_fp32_close(gpu2.state.ckpt.cpu().numpy(), ref, "B=0 decay")
+
+
+def test_two_runs_bit_identical():
+    B, H, P, N, G, L = 8, 16, 64, 128, 2, 8
+    outs = []
+    for run in range(2):
+        gen = _gen(B, H, P, N, G, "bf16", seed=17)
+        gpu = GpuMamba2(_desc(B, H, P, N, G, L, "bf16"), gen.static)
+        o = [gpu.step(gen.step()).clone() for _ in range(L + 3)]
+        outs.append((torch.stack(o), gpu.state.ckpt.clone(), gpu.state.rec_x.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_bad_cursor_sets_flag_and_skips_sequence():
+    B, H, P, N, G, L = 3, 4, 64, 128, 2, 4
+    gen = _gen(B, H, P, N, G, "bf16", seed=18)
+    gpu = GpuMamba2(_desc(B, H, P, N, G, L, "bf16"), gen.static)
+    gpu.cur[0].copy_(torch.tensor([0, L, 1], dtype=torch.int32))
+    gpu.out.fill_(123.0)
+    ck = gpu.state.ckpt.clone()
+    gpu.step(gen.step())
+    assert gpu.err.item() & rs.DEVERR_CURSOR
+    assert torch.all(gpu.out[1] == 123.0)
+    assert not torch.any(gpu.out[0] == 123.0) and not torch.any(gpu.out[2] == 123.0)
+    assert gpu.cursor.cpu().tolist() == [1, L, 2]
+    assert torch.equal(gpu.state.ckpt, ck)
+
+
+def test_explicit_flush_equals_conventional_state():
+    B, H, P, N, G, L = 4, 8, 64, 128, 2, 16
+    gen = _gen(B, H, P, N, G, "bf16", seed=19)
+    st = gen.static
+    gpu = GpuMamba2(_desc(B, H, P, N, G, L, "bf16"), st, lowp=True)
+    h = st.ckpt.astype(np.float64)
+    for t in range(5):
+        s = gen.step()
+        h, _ = om.conventional_step(h, **s, dt_bias=st.dt_bias, A=st.A, D=st.D)
+        gpu.step(s)
+    assert gpu.cursor.cpu().tolist() == [5] * B
+    gpu.flush()
+    assert gpu.cursor.cpu().tolist() == [0] * B
+    assert_fp32_close(gpu.state.ckpt.cpu().numpy(), h, "explicit flush")
+    assert torch.equal(gpu.state.ckpt_lp, gpu.state.ckpt.to(torch.bfloat16))
+    ck = gpu.state.ckpt.clone()
+    gpu.flush()  # empty buffer: checkpoint bit-unchanged
+    assert torch.equal(gpu.state.ckpt, ck)
