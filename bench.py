@@ -1,0 +1,621 @@
+#!/usr/bin/env python3
+"""Decode throughput of the ReplaySSM hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--only headline]
+
+Headline (``value``): Mamba2 replay decode, one layer, B=256, H=128, P=64, N=128,
+G=8, L=16, bf16 inputs, fp32 checkpoint reads -- seq-tokens/s = batch * K / time
+for exactly K timed decode steps (one kernel launch each, flushes included at their
+true rate of one step in L).  Inputs sit in HBM before the timed region: a pool of
+2L pre-drawn steps is cycled.  ``roofline`` gives the replay kernel's algorithmic
+HBM bytes per launch divided by its average launch time (HIP events on the launch
+stream) against the 8 TB/s peak; ``traffic`` is the counter-measured HBM bytes per
+launch from the committed rocprofv3 summary when it matches the current kernel
+source, else null.  ``cpu_baseline`` times the fp64 CPU oracle (replay form) on a
+sample of the same workload and checks the GPU outputs for that sample.
+
+Measured beside the headline, each with its own timed region: the in-library
+conventional read-update-write kernel on the same inputs, the bf16 read copy, the
+B=256/H=64 layer, speculative verification (4 positions, commit) against the
+per-position snapshot baseline, and the Gated DeltaNet layer (replay and
+conventional).  ``ceiling`` reports plain device read and copy bandwidth.
+
+Auxiliary modes used to make the committed rocprofv3 summaries:
+    --calibrate-copy        also run a plain 1 GiB device copy (counter calibration)
+    --pmc-summarize FETCH_DIR WRITE_DIR  turn two rocprofv3 --pmc runs into a summary
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Mamba2 decode seq-tokens/s at B=256, L=16 + achieved HBM GB/s vs peak"
+PEAK_GBPS = 8000.0
+HEADLINE = "mamba2_h128"
+KERNEL_SOURCES = ["hybrid_model_ssm_amd/csrc/mamba2_kernels.h", "hybrid_model_ssm_amd/csrc/device_common.h"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_pmc.txt")
+REPLAY_KERNEL_TAG = "mamba2_replay_kernel<128, 8, unsigned short, false, 0>"
+COPY_BYTES = 1 << 30
+MiB = float(1 << 20)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------------------
+# algorithmic byte models (what the method must move per launch)
+# ------------------------------------------------------------------------------------
+
+def mamba2_replay_bytes(B, H, P, N, G, L, io, c, lowp=False):
+    """One decode step for B sequences all at cursor c (records stored before it)."""
+    fold = c + 1 == L
+    if fold:
+        state = P * N * 4 * 2 + (P * N * 2 if lowp else 0)
+    else:
+        state = P * N * (2 if lowp else 4)
+    per_h = state + 2 * P * io + io + P * 4 + c * (P * io + 4) + (0 if fold else P * io + 4)
+    per_g = 2 * N * io + c * N * io + (0 if fold else N * io)
+    return B * H * per_h + B * G * per_g
+
+
+def mamba2_conventional_bytes(B, H, P, N, G, io):
+    return B * H * (2 * P * N * 4 + 2 * P * io + io + P * 4) + B * G * 2 * N * io
+
+
+def spec_round_bytes(H, P, N, G, L, io, T, committed, lowp=False):
+    """One verify round; ``committed`` holds each sequence's committed count."""
+    tot = 0
+    for cm in committed:
+        fold = cm + T > L
+        if fold:
+            state = 2 * P * N * 4 + (P * N * 2 if lowp else 0)
+        else:
+            state = P * N * (2 if lowp else 4)
+        per_h = state + T * (2 * P * io + io + P * 4) + cm * (P * io + 4) + T * (P * io + 4)
+        per_g = T * 2 * N * io + cm * N * io + T * N * io
+        tot += H * per_h + G * per_g
+    return tot
+
+
+def spec_baseline_bytes(B, H, P, N, G, io, T):
+    return B * H * (P * N * 4 * (1 + T) + T * (2 * P * io + io + P * 4)) + B * G * T * 2 * N * io
+
+
+def gdn_replay_bytes(B, HV, HK, dk, dv, L, io, c):
+    fold = c + 1 == L
+    state = dv * dk * 4 * (2 if fold else 1)
+    per_hv = state + dv * io + 8 + dv * 4 + c * (dv * io + 8) + (0 if fold else dv * io + 8)
+    per_hk = 2 * dk * io + c * dk * io + (0 if fold else dk * io)
+    return B * HV * per_hv + B * HK * per_hk
+
+
+def gdn_conventional_bytes(B, HV, HK, dk, dv, io):
+    return B * HV * (2 * dv * dk * 4 + dv * io + 8 + dv * 4) + B * HK * 2 * dk * io
+
+
+# ------------------------------------------------------------------------------------
+# timing
+# ------------------------------------------------------------------------------------
+
+class Timer:
+    """HIP events on the current (launch) stream around exactly ``n`` launches."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, launch, first, n):
+        torch = self.torch
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for i in range(first, first + n):
+            launch(i)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        return e0.elapsed_time(e1) / 1e3, wall
+
+
+def _check(st, name):
+    if st != 0:
+        from hybrid_model_ssm_amd import replayssm as rs
+        raise rs.ReplaySSMError(st, name)
+
+
+class Mamba2Bench:
+    """Device buffers and pre-marshalled launch arguments for one Mamba2 workload."""
+
+    def __init__(self, torch, rs, synth, name, pool=32, lowp=False, conventional=False, seed_override=None):
+        import ctypes
+        self.torch, self.rs = torch, rs
+        w = dict(synth.WORKLOADS[name])
+        self.w = w
+        self.B, self.H, self.P, self.N, self.G, self.L = (w["batch"], w["nheads"], w["headdim"], w["dstate"],
+                                                          w["ngroups"], w["buffer_len"])
+        self.io = 2 if w["io"] == "bf16" else 4
+        gen = synth.mamba2_inputs(name) if seed_override is None else synth.mamba2_inputs(name, seed=seed_override)
+        st = gen.static
+        self.static = st
+        dev = "cuda"
+        f32 = torch.float32
+        self.desc = rs.Mamba2Desc(self.B, self.H, self.P, self.N, self.G, self.L,
+                                  rs.BF16 if w["io"] == "bf16" else rs.F32, True)
+        iot = self.desc.torch_io
+        t = lambda a, d: torch.from_numpy(a).to(dev).to(d)  # noqa: E731
+        self.ckpt0 = t(st.ckpt, f32)
+        self.A, self.D, self.bias = t(st.A, f32), t(st.D, f32), t(st.dt_bias, f32)
+        self.pool_np = [gen.step() for _ in range(pool)]
+        self.pool = [{k: t(v, iot) for k, v in s.items()} for s in self.pool_np]
+        self.out = torch.empty(self.B, self.H, self.P, dtype=f32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.conventional = conventional
+        self.lowp = lowp
+        L = rs.lib()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.stream = stream
+        if conventional:
+            self.state_conv = self.ckpt0.clone()
+            d = self.desc.c()
+            self._keep = [d]
+            self.args = [(ctypes.byref(d), self.state_conv.data_ptr(),
+                          *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
+                          self.bias.data_ptr(), self.A.data_ptr(), self.D.data_ptr(), self.out.data_ptr(), stream)
+                         for p in self.pool]
+            self.fn = L.replayssm_selective_state_update
+        else:
+            self.state = rs.Mamba2State.allocate(self.desc, lowp=lowp, ckpt=self.ckpt0.clone())
+            self.cur = [torch.zeros(self.B, dtype=torch.int32, device=dev) for _ in range(2)]
+            d, s = self.desc.c(), self.state.c()
+            self._keep = [d, s]
+            if lowp:  # create the bf16 read copy: a flush of the empty buffer (cursors stay 0)
+                rs.mamba2_flush(self.desc, self.state, self.cur[0], self.cur[1], self.A, self.err)
+            self.args = []
+            for i in range(2 * pool):
+                p = self.pool[i % pool]
+                self.args.append((ctypes.byref(d), ctypes.byref(s), self.cur[i % 2].data_ptr(),
+                                  self.cur[1 - i % 2].data_ptr(),
+                                  *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
+                                  self.bias.data_ptr(), self.A.data_ptr(), self.D.data_ptr(),
+                                  self.out.data_ptr(), self.err.data_ptr(), stream))
+            self.fn = L.replayssm_mamba2_decode
+
+    def launch(self, i):
+        a = self.args[i % len(self.args)]
+        st = self.fn(*a)
+        if st:
+            _check(st, self.fn.__name__)
+
+    def bytes_of_step(self, i):
+        """Algorithmic bytes of the i-th launch (0-based) from a fresh state."""
+        if self.conventional:
+            return mamba2_conventional_bytes(self.B, self.H, self.P, self.N, self.G, self.io)
+        return mamba2_replay_bytes(self.B, self.H, self.P, self.N, self.G, self.L, self.io, i % self.L, self.lowp)
+
+
+def time_mamba2(torch, rs, synth, name, steps, warmup, **kw):
+    b = Mamba2Bench(torch, rs, synth, name, **kw)
+    for i in range(warmup):
+        b.launch(i)
+    secs, wall = Timer(torch).run(b.launch, warmup, steps)
+    if not b.conventional:
+        exp = (warmup + steps) % b.L
+        if not torch.equal(b.cur[(warmup + steps) % 2], torch.full_like(b.cur[0], exp)):
+            raise RuntimeError("cursor check failed after the timed region")
+        if b.err.item() != 0:
+            raise RuntimeError("device error flag set")
+    nbytes = sum(b.bytes_of_step(i) for i in range(warmup, warmup + steps))
+    res = dict(seq_tokens_per_s=b.B * steps / secs, ms_per_step=secs * 1e3 / steps, seconds=secs, wall_s=wall,
+               bytes_per_step_MiB=nbytes / steps / MiB, hbm_gbps=nbytes / secs / 1e9,
+               frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS, steps=steps)
+    return res, b
+
+
+def time_spec(torch, rs, synth, rounds, warmup, baseline=False, lowp=False):
+    import ctypes
+    import numpy as np
+    w = synth.WORKLOADS["mamba2_spec_h128"]
+    B, H, P, N, G, L, T = w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"], w["buffer_len"], w["n_pos"]
+    io = 2
+    gen = synth.mamba2_inputs("mamba2_spec_h128")
+    st = gen.static
+    dev = "cuda"
+    f32 = torch.float32
+    t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
+    desc = rs.Mamba2Desc(B, H, P, N, G, L, rs.BF16, True)
+    pool_n = 32
+    pool, keeps = [], []
+    for _ in range(pool_n):
+        s = gen.step(n_pos=T)
+        pool.append({k: t(v, torch.bfloat16) for k, v in s.items()})
+        keeps.append(gen.accepted(T - 1) + 1)
+    keep_dev = [torch.from_numpy(k.astype(np.int32)).to(dev) for k in keeps]
+    A, D, bias = t(st.A, f32), t(st.D, f32), t(st.dt_bias, f32)
+    out = torch.empty(B, T, H, P, dtype=f32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    Lb = rs.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    d = desc.c()
+    if baseline:
+        snaps = torch.empty(B, T, H, P, N, dtype=f32, device=dev)
+        snaps[:, 0] = t(st.ckpt, f32)
+        slots = [torch.from_numpy((keeps[(r - 1) % pool_n] - 1).astype(np.int32)).to(dev) for r in range(pool_n)]
+        slots[0] = torch.zeros(B, dtype=torch.int32, device=dev)
+
+        def launch(r):
+            p = pool[r % pool_n]
+            _check(Lb.replayssm_mamba2_spec_baseline(ctypes.byref(d), snaps.data_ptr(), slots[r % pool_n].data_ptr(),
+                                                     T, *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
+                                                     bias.data_ptr(), A.data_ptr(), D.data_ptr(), out.data_ptr(),
+                                                     stream), "spec_baseline")
+        keep_state = [snaps]
+    else:
+        state = rs.Mamba2State.allocate(desc, lowp=lowp, ckpt=t(st.ckpt, f32))
+        s_c = state.c()
+        head = torch.zeros(B, dtype=torch.int32, device=dev)
+        com = torch.zeros(B, dtype=torch.int32, device=dev)
+        flushed = torch.zeros(B, dtype=torch.int32, device=dev)
+        if lowp:
+            z0, z1 = torch.zeros_like(head), torch.zeros_like(head)
+            rs.mamba2_flush(desc, state, z0, z1, A, err)
+
+        def launch(r):
+            p = pool[r % pool_n]
+            _check(Lb.replayssm_mamba2_spec_verify(ctypes.byref(d), ctypes.byref(s_c), head.data_ptr(), com.data_ptr(),
+                                                   T, *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
+                                                   bias.data_ptr(), A.data_ptr(), D.data_ptr(), out.data_ptr(),
+                                                   flushed.data_ptr(), err.data_ptr(), stream), "spec_verify")
+            _check(Lb.replayssm_commit(B, L, T, head.data_ptr(), com.data_ptr(), flushed.data_ptr(),
+                                       keep_dev[r % pool_n].data_ptr(), err.data_ptr(), stream), "commit")
+        keep_state = [state, s_c]
+    for r in range(warmup):
+        launch(r)
+    secs, wall = Timer(torch).run(launch, warmup, rounds)
+    accepted = sum(int(keeps[r % pool_n].sum()) for r in range(warmup, warmup + rounds))
+    # host model of the cursors (integer rules of the commit call) for the byte count
+    hd = np.zeros(B, np.int64)
+    cm = np.zeros(B, np.int64)
+    nbytes = 0
+    n_flush = 0
+    for r in range(warmup + rounds):
+        fl = cm + T > L
+        if r >= warmup:
+            nbytes += spec_baseline_bytes(B, H, P, N, G, io, T) if baseline else \
+                spec_round_bytes(H, P, N, G, L, io, T, cm, lowp)
+            n_flush += int(fl.sum())
+        hd = np.where(fl, (hd + cm) % L, hd)
+        cm = np.where(fl, 0, cm) + keeps[r % pool_n]
+    if not baseline:
+        if not (np.array_equal(head.cpu().numpy(), hd.astype(np.int32)) and
+                np.array_equal(com.cpu().numpy(), cm.astype(np.int32))):
+            raise RuntimeError("speculative cursors disagree with the host model")
+        if err.item() != 0:
+            raise RuntimeError("device error flag set")
+    del keep_state
+    return dict(accepted_tokens_per_s=accepted / secs, positions_per_s=B * T * rounds / secs,
+                ms_per_round=secs * 1e3 / rounds, rounds=rounds, bytes_per_round_MiB=nbytes / rounds / MiB,
+                hbm_gbps=nbytes / secs / 1e9, frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS,
+                accepted_per_round=accepted / rounds / B,
+                flush_fraction=(n_flush / (B * rounds)) if not baseline else None)
+
+
+def time_gdn(torch, rs, synth, steps, warmup, conventional=False):
+    import ctypes
+    import numpy as np
+    w = synth.WORKLOADS["gdn_hv32"]
+    B, HV, HK, dk, dv, L = w["batch"], w["num_v_heads"], w["num_k_heads"], w["dk"], w["dv"], w["buffer_len"]
+    gen = synth.gdn_inputs("gdn_hv32")
+    st = gen.static
+    dev = "cuda"
+    t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    pool = []
+    for _ in range(32):
+        s = gen.step()
+        pool.append({"q": t(s["q"], torch.bfloat16), "k": t(s["k"], torch.bfloat16), "v": t(s["v"], torch.bfloat16),
+                     "alpha": t(s["alpha"], torch.float32), "beta": t(s["beta"], torch.float32)})
+    out = torch.empty(B, HV, dv, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    Lb = rs.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    d = desc.c()
+    keys = ("q", "k", "v", "alpha", "beta")
+    if conventional:
+        S = t(st.ckpt, torch.float32)
+
+        def launch(i):
+            p = pool[i % 32]
+            _check(Lb.replayssm_gdn_conventional_decode(ctypes.byref(d), S.data_ptr(), *(p[k].data_ptr() for k in keys),
+                                                        out.data_ptr(), stream), "gdn_conventional")
+        keep = [S]
+    else:
+        state = rs.GdnState.allocate(desc, ckpt=t(st.ckpt, torch.float32))
+        s_c = state.c()
+        cur = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
+
+        def launch(i):
+            p = pool[i % 32]
+            _check(Lb.replayssm_gdn_decode(ctypes.byref(d), ctypes.byref(s_c), cur[i % 2].data_ptr(),
+                                           cur[1 - i % 2].data_ptr(), *(p[k].data_ptr() for k in keys),
+                                           out.data_ptr(), err.data_ptr(), stream), "gdn_decode")
+        keep = [state, s_c, cur]
+    for i in range(warmup):
+        launch(i)
+    secs, wall = Timer(torch).run(launch, warmup, steps)
+    if conventional:
+        nbytes = steps * gdn_conventional_bytes(B, HV, HK, dk, dv, 2)
+    else:
+        nbytes = sum(gdn_replay_bytes(B, HV, HK, dk, dv, L, 2, i % L) for i in range(warmup, warmup + steps))
+        if err.item() != 0:
+            raise RuntimeError("device error flag set")
+    del keep
+    return dict(seq_tokens_per_s=B * steps / secs, ms_per_step=secs * 1e3 / steps, steps=steps,
+                bytes_per_step_MiB=nbytes / steps / MiB, hbm_gbps=nbytes / secs / 1e9,
+                frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS)
+
+
+def ceiling(torch, calibrate_copy=False):
+    n = COPY_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+        a.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.mul(a, 1.0, out=b)   # plain streaming read + write of 1 GiB each (also the counter calibration)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / reps
+    e0.record()
+    for _ in range(reps):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_s = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    return dict(copy_gbps=2 * COPY_BYTES / copy_s / 1e9, read_gbps=COPY_BYTES / read_s / 1e9,
+                note="torch elementwise mul-by-one (1 GiB read + 1 GiB write) and sum (1 GiB read), fp32")
+
+
+# ------------------------------------------------------------------------------------
+# CPU oracle leg
+# ------------------------------------------------------------------------------------
+
+def cpu_baseline(torch, rs, synth, nseq, steps):
+    """Time the fp64 oracle (replay form) on ``nseq`` sequences of the headline workload
+    for ``steps`` steps, and check the GPU's outputs for the same sequences and inputs."""
+    import numpy as np
+    from oracle import mamba2 as om  # the oracle is test infrastructure; used only here
+    b = Mamba2Bench(torch, rs, synth, HEADLINE, pool=max(steps, 1))
+    st = b.static
+    sample = np.arange(nseq)
+    gpu_outs = []
+    for i in range(steps):
+        b.launch(i)
+        gpu_outs.append(b.out[:nseq].cpu().numpy())
+    rep = om.Mamba2Replay(st.ckpt[sample], b.L, st.A, st.D, st.dt_bias, b.G)
+    worst = 0.0
+    t0 = time.perf_counter()
+    outs = []
+    for i in range(steps):
+        s = {k: v[sample] for k, v in b.pool_np[i].items()}
+        o, _ = rep.step(**s)
+        outs.append(o)
+    secs = time.perf_counter() - t0
+    for o, g in zip(outs, gpu_outs):
+        worst = max(worst, float(np.max(np.abs(g - o) / (1e-4 * (1 + np.abs(o))))))
+    return dict(value=nseq * steps / secs, unit="seq-tokens/s", cores=1, kind="oracle",
+                sample=f"{nseq} of {b.B} sequences x {steps} decode steps (one L={b.L} window incl. its flush) "
+                       f"of the {HEADLINE} workload, NumPy float64 replay form, one process",
+                seconds=secs, gpu_parity_max_violation=worst, gpu_parity_ok=worst <= 1.0)
+
+
+# ------------------------------------------------------------------------------------
+# rocprofv3 counter summary
+# ------------------------------------------------------------------------------------
+
+def _read_counter_csv(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _avg_counter(rows, name_pred, counter):
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or not name_pred(r.get("Kernel_Name", "")):
+            continue
+        key = (r.get("Dispatch_Id"), r.get("Kernel_Name"))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        return None, 0
+    return sum(per.values()) / len(per), len(per)
+
+
+def pmc_summarize(fetch_dir, write_dir, out_path, command):
+    fr, wr = _read_counter_csv(fetch_dir), _read_counter_csv(write_dir)
+    is_replay = lambda n: REPLAY_KERNEL_TAG in n  # noqa: E731
+    is_copy = lambda n: "MulFunctor" in n  # the calibration kernel: 1 GiB read + 1 GiB write  # noqa: E731
+    f_rep, nf = _avg_counter(fr, is_replay, "FETCH_SIZE")
+    w_rep, nw = _avg_counter(wr, is_replay, "WRITE_SIZE")
+    f_cpy, _ = _avg_counter(fr, is_copy, "FETCH_SIZE")
+    w_cpy, _ = _avg_counter(wr, is_copy, "WRITE_SIZE")
+    if None in (f_rep, w_rep, f_cpy, w_cpy):
+        raise RuntimeError("missing counters for the replay kernel or the calibration copy")
+    f_scale = COPY_BYTES / (f_cpy * 1024.0)
+    w_scale = COPY_BYTES / (w_cpy * 1024.0)
+    traffic = f_rep * 1024.0 * f_scale + w_rep * 1024.0 * w_scale
+    lines = [
+        "# rocprofv3 HBM counters: Mamba2 replay decode kernel, workload mamba2_h128",
+        "# (B=256 H=128 P=64 N=128 G=8 L=16, bf16 io, fp32 checkpoint reads)",
+        f"command: {command}",
+        f"kernel: rssm::{REPLAY_KERNEL_TAG}",
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"dispatches: fetch {nf}, write {nw}",
+        f"FETCH_SIZE_KiB_per_dispatch: {f_rep:.1f}",
+        f"WRITE_SIZE_KiB_per_dispatch: {w_rep:.1f}",
+        f"copy_calibration: {COPY_BYTES} B device copy reads FETCH_SIZE {f_cpy:.1f} KiB, WRITE_SIZE {w_cpy:.1f} KiB",
+        f"scale_fetch: {f_scale:.4f}",
+        f"scale_write: {w_scale:.4f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+    ]
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def committed_traffic():
+    """Counter-measured bytes per launch from the committed summary, if it matches the source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None, "no counter summary committed"
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel source changed since the counters were taken"
+    return float(kv["traffic_bytes_per_launch"]), os.path.relpath(PMC_SUMMARY, ROOT)
+
+
+# ------------------------------------------------------------------------------------
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024, help="timed decode steps of the headline")
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--only", choices=["all", "headline"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=128)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-command", default="")
+    args = ap.parse_args(argv)
+
+    if args.pmc_summarize:
+        pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], PMC_SUMMARY, args.pmc_command)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the decode path has no cross-GPU exchange); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    from hybrid_model_ssm_amd import replayssm as rs
+    from hybrid_model_ssm_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    rs.lib()
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    head, hb = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup)
+    print(f"[bench] headline {head['seq_tokens_per_s']:.4g} seq-tok/s, {head['hbm_gbps']:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    del hb
+    torch.cuda.empty_cache()
+    launches = args.steps
+    nbytes_per_launch = head["bytes_per_step_MiB"] * MiB
+    avg_s = head["seconds"] / launches
+    traffic, traffic_src = committed_traffic()
+    roofline = dict(bound="hbm", achieved=nbytes_per_launch / avg_s / 1e9, peak=PEAK_GBPS, unit="GB/s",
+                    frac=nbytes_per_launch / avg_s / 1e9 / PEAK_GBPS, traffic=traffic,
+                    traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                    traffic_source=traffic_src,
+                    kernel=f"rssm::{REPLAY_KERNEL_TAG}", algorithmic_bytes_per_launch=nbytes_per_launch,
+                    avg_launch_us=avg_s * 1e6, launches=launches)
+
+    variants = {}
+    conv = None
+    if args.only == "all":
+        conv, _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup, conventional=True)
+        torch.cuda.empty_cache()
+        variants["mamba2_h128_conventional"] = conv
+        variants["mamba2_h128_bf16_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup,
+                                                           lowp=True)
+        torch.cuda.empty_cache()
+        variants["mamba2_h64_replay"], _ = time_mamba2(torch, rs, synth, "mamba2_h64", 256, 32)
+        torch.cuda.empty_cache()
+        variants["mamba2_h64_conventional"], _ = time_mamba2(torch, rs, synth, "mamba2_h64", 256, 32,
+                                                             conventional=True)
+        torch.cuda.empty_cache()
+        variants["spec_h128_verify"] = time_spec(torch, rs, synth, 256, 32)
+        torch.cuda.empty_cache()
+        variants["spec_h128_snapshot_baseline"] = time_spec(torch, rs, synth, 256, 32, baseline=True)
+        torch.cuda.empty_cache()
+        variants["gdn_hv32_replay"] = time_gdn(torch, rs, synth, 512, 32)
+        torch.cuda.empty_cache()
+        variants["gdn_hv32_conventional"] = time_gdn(torch, rs, synth, 512, 32, conventional=True)
+        torch.cuda.empty_cache()
+        print("[bench] variants done", file=sys.stderr, flush=True)
+    ceil = ceiling(torch, args.calibrate_copy) if (args.only == "all" or args.calibrate_copy) else None
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, rs, synth, args.cpu_seqs, 16)
+        print(f"[bench] cpu baseline {cpu['value']:.4g} seq-tok/s in {cpu['seconds']:.1f}s", file=sys.stderr,
+              flush=True)
+        if not cpu["gpu_parity_ok"]:
+            raise RuntimeError(f"GPU outputs disagree with the oracle: {cpu['gpu_parity_max_violation']}")
+
+    w = synth.WORKLOADS[HEADLINE]
+    line = {
+        "metric": METRIC,
+        "value": head["seq_tokens_per_s"],
+        "unit": "seq-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "batch": w["batch"], "nheads": w["nheads"], "headdim": w["headdim"],
+                   "dstate": w["dstate"], "ngroups": w["ngroups"], "buffer_len": w["buffer_len"],
+                   "io_dtype": w["io"], "checkpoint": "f32", "checkpoint_reads": "f32",
+                   "parallelism": "single GPU"},
+        "hbm_gbps": head["hbm_gbps"],
+        "hbm_frac_of_peak": head["frac_of_peak"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "speedup_vs_conventional": (head["seq_tokens_per_s"] / conv["seq_tokens_per_s"]) if conv else None,
+        "variants": variants,
+        "ceiling": ceil,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -23,7 +23,12 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libreplayssm.so")
 
-SOURCES = ["api.cpp", "mamba2_kernels.hip", "gdn_kernels.hip", "cursor_kernels.hip"]
+# (source, object name, extra defines); the Mamba2 kernel templates are instantiated in
+# slices (io dtype x replay mode, and the conventional kernels) that compile in parallel.
+SOURCES = [("api.cpp", "api", []), ("mamba2_launch.hip", "mamba2_launch", []),
+           ("gdn_kernels.hip", "gdn_kernels", []), ("cursor_kernels.hip", "cursor_kernels", [])]
+SOURCES += [("mamba2_inst.hip", f"mamba2_inst_io{io}_part{part}", [f"-DRSSM_IO={io}", f"-DRSSM_PART={part}"])
+            for io in (0, 1) for part in (0, 1, 2, 3)]
 ARCH = "gfx950"
 
 
@@ -41,9 +46,10 @@ def common_flags():
             "-Wno-unused-command-line-argument"]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(item, verbose):
+    src, name, defines = item
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [hipcc(), *common_flags(), *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -56,7 +62,7 @@ def _compile(src, verbose):
 
 def build(verbose=False, jobs=None):
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    jobs = jobs or min(len(SOURCES), int(os.environ.get("MAX_JOBS", 0)) or os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"

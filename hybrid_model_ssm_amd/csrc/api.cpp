@@ -53,6 +53,13 @@ replayssm_status check_mamba2_inputs(const replayssm_mamba2_desc* d, const void*
     return REPLAYSSM_OK;
 }
 
+// The replay kernel stages one head's window and the group's records in LDS.
+bool replay_fits(const replayssm_mamba2_desc* d, int n_pos) {
+    const size_t bytes = rssm::mamba2_replay_smem_bytes(d->headdim, d->dstate, d->nheads / d->ngroups,
+                                                        d->buffer_len, n_pos, d->io_dtype == REPLAYSSM_BF16 ? 2 : 4);
+    return bytes > 0 && bytes <= rssm::mamba2_max_smem_bytes();
+}
+
 rssm::Mamba2Args mamba2_args(const replayssm_mamba2_desc* d, const replayssm_mamba2_state* s) {
     rssm::Mamba2Args a{};
     a.ckpt = s->ckpt;
@@ -123,9 +130,7 @@ replayssm_status replayssm_mamba2_decode(const replayssm_mamba2_desc* desc,
     if ((st = check_mamba2_inputs(desc, x, z, B, C, dt_raw, dt_bias, A, D, out)) != REPLAYSSM_OK) return st;
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
-    if (rssm::mamba2_replay_smem_bytes(desc->headdim, desc->dstate, desc->buffer_len, 0) >
-        rssm::mamba2_max_smem_bytes())
-        return REPLAYSSM_ERR_UNSUPPORTED;
+    if (!replay_fits(desc, 0)) return REPLAYSSM_ERR_UNSUPPORTED;
     rssm::Mamba2Args a = mamba2_args(desc, state);
     a.cursor_in = cursor_in;
     a.cursor_out = cursor_out;
@@ -145,9 +150,7 @@ replayssm_status replayssm_mamba2_flush(const replayssm_mamba2_desc* desc,
     REQ(A && aligned(A, 4));
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
-    if (rssm::mamba2_replay_smem_bytes(desc->headdim, desc->dstate, desc->buffer_len, 0) >
-        rssm::mamba2_max_smem_bytes())
-        return REPLAYSSM_ERR_UNSUPPORTED;
+    if (!replay_fits(desc, 0)) return REPLAYSSM_ERR_UNSUPPORTED;
     rssm::Mamba2Args a = mamba2_args(desc, state);
     a.cursor_in = cursor_in;
     a.cursor_out = cursor_out;
@@ -174,9 +177,7 @@ replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
     REQ(head && committed && flushed && head != committed);
     REQ((const int32_t*)flushed != head && (const int32_t*)flushed != committed);
     REQ(aligned(head, 4) && aligned(committed, 4) && aligned(flushed, 4) && aligned(err_flags, 4));
-    if (rssm::mamba2_replay_smem_bytes(desc->headdim, desc->dstate, desc->buffer_len, n_pos) >
-        rssm::mamba2_max_smem_bytes())
-        return REPLAYSSM_ERR_UNSUPPORTED;
+    if (!replay_fits(desc, n_pos)) return REPLAYSSM_ERR_UNSUPPORTED;
     rssm::Mamba2Args a = mamba2_args(desc, state);
     a.cursor_in = head;
     a.committed = committed;
@@ -184,9 +185,7 @@ replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
     a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
     a.n_pos = n_pos;
-    hipError_t e = rssm::launch_mamba2_replay(a, desc->io_dtype, 2, stream);
-    if (e != hipSuccess) return REPLAYSSM_ERR_HIP;
-    return hip_status(rssm::launch_mamba2_spec_append_B(a, desc->io_dtype, stream));
+    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, 2, stream));
 }
 
 replayssm_status replayssm_commit(int32_t batch, int32_t buffer_len, int32_t n_pos, int32_t* head,

@@ -28,6 +28,14 @@ template <typename IO> struct Io;
 
 template <> struct Io<float> {
     using T = float;
+    using Raw4 = float4;  // four elements as loaded
+    __device__ static __forceinline__ Raw4 ldraw4(const T* p, size_t i) {
+        return *reinterpret_cast<const float4*>(p + i);
+    }
+    __device__ static __forceinline__ void straw4(T* p, size_t i, Raw4 r) {
+        *reinterpret_cast<float4*>(p + i) = r;
+    }
+    __device__ static __forceinline__ float4 cvt4(Raw4 r) { return r; }
     __device__ static __forceinline__ float ld(const T* p, size_t i) { return p[i]; }
     // four consecutive elements (i multiple of 4, 16-byte aligned)
     __device__ static __forceinline__ float4 ld4(const T* p, size_t i) {
@@ -37,6 +45,17 @@ template <> struct Io<float> {
 
 template <> struct Io<uint16_t> {
     using T = uint16_t;
+    using Raw4 = uint2;
+    __device__ static __forceinline__ Raw4 ldraw4(const T* p, size_t i) {
+        return *reinterpret_cast<const uint2*>(p + i);
+    }
+    __device__ static __forceinline__ void straw4(T* p, size_t i, Raw4 r) {
+        *reinterpret_cast<uint2*>(p + i) = r;
+    }
+    __device__ static __forceinline__ float4 cvt4(Raw4 r) {
+        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+    }
     __device__ static __forceinline__ float ld(const T* p, size_t i) { return bf16_bits_to_f32(p[i]); }
     // four consecutive elements (i multiple of 4, 8-byte aligned)
     __device__ static __forceinline__ float4 ld4(const T* p, size_t i) {

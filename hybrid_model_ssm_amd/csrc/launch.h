@@ -29,6 +29,8 @@ struct Mamba2Args {
     float* out;           // [B,(T,)H,P]
     int32_t* err_flags;
     int32_t batch, nheads, headdim, dstate, ngroups, L, dt_softplus, n_pos;
+    int32_t nchunk;       // workgroups per (sequence, group)
+    int32_t heads_per_chunk;
 };
 
 // Conventional read-update-write step (and the per-position snapshot baseline).
@@ -67,12 +69,13 @@ struct GdnArgs {
 };
 
 bool mamba2_shape_supported(int headdim, int dstate);
-size_t mamba2_replay_smem_bytes(int headdim, int dstate, int L, int n_pos);
+// 0 when the replay kernel cannot take this (headdim, dstate, nheads/ngroups, L, n_pos)
+size_t mamba2_replay_smem_bytes(int headdim, int dstate, int heads_per_group, int L, int n_pos,
+                                int io_bytes);
 size_t mamba2_max_smem_bytes();
 
 // mode: 0 = AR decode step, 1 = fold stored records only (flush), 2 = speculative verify
 hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int mode, hipStream_t stream);
-hipError_t launch_mamba2_spec_append_B(const Mamba2Args& a, int io, hipStream_t stream);
 hipError_t launch_mamba2_conventional(const Mamba2ConvArgs& a, int io, bool snapshots,
                                       hipStream_t stream);
 

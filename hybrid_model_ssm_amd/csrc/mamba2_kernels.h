@@ -1,0 +1,560 @@
+// Mamba2 ReplaySSM kernels for gfx950.
+//
+// The method ("ReplaySSM Caches Inputs Instead of State to Speed Up Hybrid-Model
+// Decoding", section "How ReplaySSM works"): the state is a checkpoint plus a buffer of
+// recent input records.  A non-flush step appends its record and computes the output
+// from the checkpoint and the buffer without storing a state; the step that fills the
+// buffer folds the records into the checkpoint and stores it once.  Unrolling the
+// Mamba2 recurrence h = exp(dt A) h + dt x B^T over a window of records s (oldest
+// first) gives, with lam_s = sum of dt over the window records after s:
+//
+//     decay = exp(A * sum_s dt_s),   w_s = dt_s * exp(A * lam_s)
+//     y     = decay * (Hc . C_t) + sum_s w_s (B_s . C_t) x_s + D x_t
+//     fold:   Hc <- decay * Hc + sum_s w_s x_s B_s^T
+//
+// Work decomposition: one 256-thread workgroup per (sequence, group of heads that share
+// B and C).  The group's B records, C vectors, the B_s . C_t dots and every head's
+// decay coefficients are staged once in LDS; the workgroup then streams its heads'
+// [headdim, dstate] fp32 checkpoint tiles, loading head i+1's tile into a second set
+// of registers while it reduces head i, so the HBM stream never waits on the per-head
+// work.  Within a tile, LPR = dstate/4 consecutive lanes cover one row with 16-byte
+// loads (a wave load instruction reads whole contiguous rows) and each thread holds
+// R rows.  Row dot products  Hc[p,:] . C  are finished with a transpose-reduce across
+// the LPR lanes, and the window's record terms  sum_s coef_s x_s[p]  ride in the same
+// reduction: lane q of a row adds the term of record s = q.  The flush fold is a
+// rank-|window| update applied to the tile in registers.
+//
+// Modes share one kernel body:
+//   kDecode  one autoregressive step (flushes in place when the buffer fills)
+//   kFold    fold the stored records only (explicit flush / bf16 copy refresh)
+//   kSpec    speculative verification over n_pos positions on the circular buffer
+//            ("ReplaySSM" README, benefit "Cheap rollback": output-only verification,
+//            rejected inputs dropped by moving a pointer)
+
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace rssm {
+
+constexpr int kDecode = 0;
+constexpr int kFold = 1;
+constexpr int kSpec = 2;
+constexpr int kThreads = 256;
+constexpr int kMaxHeadsPerWg = 16;
+constexpr int kFoldXPerThread = 4;  // 4-element loads per thread for one head's fold rows
+constexpr int kRecBatch = 8;        // record rows loaded together when forming the record terms
+
+template <int P, int N>
+struct Mamba2Tile {
+    static constexpr int LPR = N / 4;                  // lanes per checkpoint row
+    static constexpr int RPP = kThreads / LPR;         // rows per pass of the workgroup
+    static constexpr int R = (P + RPP - 1) / RPP;      // rows per thread
+    static constexpr bool MASK = (P % RPP) != 0;       // some threads hold no row
+    static_assert(R >= 1 && R <= LPR && (R & (R - 1)) == 0, "tile shape");
+};
+
+// LDS layout of the replay kernel (in 4-byte words).
+struct GroupSmem {
+    int NR, T1, US;
+    int oB, oC, oDt, oBeta, oCf, oDec, oW, oDecf, oY, oG, oU, oA, oD, total;
+    __host__ __device__ GroupSmem(int P, int N, int L, int T, int HC, int mode, int io_bytes) {
+        NR = (mode == kSpec) ? L + T : L;   // most window rows
+        T1 = T > 0 ? T : 1;
+        US = NR + 1;                        // row stride of the fold factors
+        oB = 0;                             // [NR][N] io    B rows of the window
+        oC = oB + (NR * N * io_bytes + 3) / 4;  // [T1][N]  C of each position
+        oDt = oC + T1 * N;                  // [HC][NR]      dt of each head and row
+        oBeta = oDt + HC * NR;              // [T1][NR]      B_s . C_j
+        oCf = oBeta + T1 * NR;              // [HC][T1][NR]  output coefficients w*beta
+        oDec = oCf + HC * T1 * NR;          // [HC][T1]      output decays
+        oW = oDec + HC * T1;                // [HC][NR]      fold weights
+        oDecf = oW + HC * NR;               // [HC]          fold decays
+        oY = oDecf + HC;                    // [HC][T1][P]   record terms + D x of each output
+        oG = oY + HC * T1 * P;              // [HC][T1][P]   silu(z) of each output
+        oU = oG + HC * T1 * P;              // [P][US]       fold factors w_s x_s[p] of one head
+        oA = oU + P * US;                   // [HC]
+        oD = oA + HC;                       // [HC]
+        total = oD + HC;
+    }
+};
+
+template <int P, int N, typename IO, bool LOWP, int MODE>
+__global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
+    using io = Io<IO>;
+    using Raw4 = typename io::Raw4;
+    using Tl = Mamba2Tile<P, N>;
+    constexpr int LPR = Tl::LPR, RPP = Tl::RPP, R = Tl::R;
+    constexpr bool MASK = Tl::MASK;
+    constexpr int P4 = P / 4, N4 = N / 4;
+    extern __shared__ float smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int H = a.nheads, G = a.ngroups, L = a.L;
+    const int hpg = H / G;
+    const int nchunk = a.nchunk;
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int chunk = wid % nchunk;
+    const int bg = wid / nchunk;
+    const int b = bg / G;
+    const int g = bg - b * G;
+    const int h0 = g * hpg + chunk * a.heads_per_chunk;
+    const int nh = min(a.heads_per_chunk, hpg - chunk * a.heads_per_chunk);
+    const bool lead = (g == 0 && chunk == 0);  // writes the per-sequence cursor outputs
+    const int T = (MODE == kSpec) ? a.n_pos : (MODE == kDecode ? 1 : 0);
+
+    // ---- cursors -------------------------------------------------------------------
+    int c = 0, hd = 0, cm = 0;
+    bool bad;
+    if constexpr (MODE == kSpec) {
+        hd = a.cursor_in[b];
+        cm = a.committed[b];
+        bad = hd < 0 || hd >= L || cm < 0 || cm > L;
+    } else {
+        c = a.cursor_in[b];
+        bad = c < 0 || c >= L;
+    }
+    if (bad) {
+        if (tid == 0) {
+            if (a.err_flags) atomicOr(a.err_flags, 1);
+            if (lead && MODE != kSpec) a.cursor_out[b] = c;
+        }
+        return;
+    }
+    const int nstored = (MODE == kSpec) ? cm : c;   // window rows taken from the ring
+    const int nrec = nstored + T;                    // window rows
+    const bool fold = (MODE == kFold) || (MODE == kDecode && c + 1 == L) ||
+                      (MODE == kSpec && cm + T > L);
+    const int nf = (MODE == kSpec) ? cm : nrec;      // the fold covers rows [0, nf)
+    const int st = fold ? nf : 0;                    // first row of every output window
+    const bool use_lp = LOWP && !fold;
+    // explicit flush of an empty buffer: the fp32 checkpoint stays as it is
+    const bool keep_ckpt = (MODE == kFold) && c == 0;
+    const bool idle = keep_ckpt && !LOWP;
+
+    const GroupSmem lay(P, N, L, T, a.heads_per_chunk, MODE, (int)sizeof(IO));
+    const int NR = lay.NR, T1 = lay.T1, US = lay.US;
+    IO* sB = reinterpret_cast<IO*>(smem + lay.oB);
+    float* sC = smem + lay.oC;
+    float* sdt = smem + lay.oDt;
+    float* sbeta = smem + lay.oBeta;
+    float* scf = smem + lay.oCf;
+    float* sdec = smem + lay.oDec;
+    float* sw = smem + lay.oW;
+    float* sdecf = smem + lay.oDecf;
+    float* sY = smem + lay.oY;
+    float* sG = smem + lay.oG;
+    float* sU = smem + lay.oU;
+    float* sA = smem + lay.oA;
+    float* sD = smem + lay.oD;
+
+    const int row0 = tid / LPR;
+    const int col4 = tid % LPR;
+    const IO* xin = reinterpret_cast<const IO*>(a.x);
+    const IO* zin = reinterpret_cast<const IO*>(a.z);
+    const IO* Bin = reinterpret_cast<const IO*>(a.B);
+    const IO* Cin = reinterpret_cast<const IO*>(a.C);
+    const IO* dtin = reinterpret_cast<const IO*>(a.dt_raw);
+    const IO* recX = reinterpret_cast<const IO*>(a.rec_x);
+    const IO* recB = reinterpret_cast<const IO*>(a.rec_B) + (size_t)(b * G + g) * L * N;
+    const size_t bH = (size_t)b * H;
+
+    auto slot_of = [&](int s) {
+        if constexpr (MODE == kSpec) {
+            const int t = hd + s;
+            return t < L ? t : t - L;
+        } else {
+            return s;
+        }
+    };
+    // row s of head h's x window: a ring record or one of this call's positions
+    auto xrow = [&](int h, int s) -> const IO* {
+        if (s < nstored) return recX + ((bH + h) * L + slot_of(s)) * P;
+        const int j = s - nstored;
+        return xin + ((MODE == kSpec) ? ((size_t)(b * T + j) * H + h) * P : (bH + h) * P);
+    };
+    auto pos_x = [&](int h, int j) -> size_t {   // x/z/out offset of head h, position j
+        return (MODE == kSpec) ? ((size_t)(b * T + j) * H + h) * P : (bH + h) * P;
+    };
+    auto pos_g = [&](int j) -> size_t {
+        return (MODE == kSpec) ? ((size_t)(b * T + j) * G + g) * N : (size_t)(b * G + g) * N;
+    };
+    auto pos_h = [&](int h, int j) -> size_t {
+        return (MODE == kSpec) ? (size_t)(b * T + j) * H + h : bH + h;
+    };
+
+    // ---- checkpoint tile loads (head hl into v / vl) -------------------------------------
+    auto issue_tile = [&](int hl, float4 (&v)[R], uint2 (&vl)[R]) {
+        const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
+        if (use_lp) {
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                if (!MASK || row0 + k * RPP < P)
+                    vl[k] = *reinterpret_cast<const uint2*>(a.ckpt_lp + t + (size_t)k * RPP * N);
+        } else if (!idle) {
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                if (!MASK || row0 + k * RPP < P)
+                    v[k] = *reinterpret_cast<const float4*>(a.ckpt + t + (size_t)k * RPP * N);
+        }
+    };
+    // fold rows of head hl: x_s[p] for s < nf, as 4-element chunks
+    Raw4 xf[kFoldXPerThread];
+    auto issue_foldx = [&](int hl) {
+#pragma unroll
+        for (int i = 0; i < kFoldXPerThread; ++i) {
+            const int task = tid + i * kThreads;
+            if (task < nf * P4) {
+                const int s = task / P4, p4 = task % P4;
+                xf[i] = io::ldraw4(xrow(h0 + hl, s), 4 * p4);
+            }
+        }
+    };
+
+    float4 va[R], vb[R];
+    uint2 la[R], lb[R];
+    issue_tile(0, va, la);
+    if (fold && !idle) issue_foldx(0);
+
+    // ---- prologue 1: stage the group's window -------------------------------------------
+    for (int task = tid; task < nrec * N4; task += kThreads) {
+        const int s = task / N4, n4 = task % N4;
+        const Raw4 r = (s < nstored) ? io::ldraw4(recB, (size_t)slot_of(s) * N + 4 * n4)
+                                     : io::ldraw4(Bin, pos_g(s - nstored) + 4 * n4);
+        *reinterpret_cast<Raw4*>(sB + s * N + 4 * n4) = r;
+    }
+    for (int task = tid; task < T * N4; task += kThreads) {
+        const int j = task / N4, n4 = task % N4;
+        *reinterpret_cast<float4*>(sC + j * N + 4 * n4) = io::cvt4(io::ldraw4(Cin, pos_g(j) + 4 * n4));
+    }
+    for (int task = tid; task < nh * nrec; task += kThreads) {
+        const int hl = task / nrec, s = task - hl * nrec;
+        const int h = h0 + hl;
+        float dt;
+        if (s < nstored) {
+            dt = a.rec_dt[(bH + h) * L + slot_of(s)];
+        } else {
+            dt = io::ld(dtin, pos_h(h, s - nstored)) + a.dt_bias[h];
+            if (a.dt_softplus) dt = softplus_f32(dt);
+        }
+        sdt[hl * NR + s] = dt;
+    }
+    for (int hl = tid; hl < nh; hl += kThreads) {
+        sA[hl] = a.A[h0 + hl];
+        if (MODE != kFold) sD[hl] = a.D[h0 + hl];
+    }
+    __syncthreads();
+
+    if constexpr (MODE != kFold) {
+        // ---- prologue 2: beta[j][s] = B_s . C_j, 16 lanes a pair -----------------------
+        for (int base = 0; base < T * nrec; base += kThreads / 16) {
+            const int pr = base + tid / 16;
+            const int part = tid & 15;
+            if (pr < T * nrec) {
+                const int j = pr / nrec, s = pr - j * nrec;
+                float beta = 0.f;
+                for (int n = part; n < N; n += 16) beta += io::ld(sB, s * N + n) * sC[j * N + n];
+                beta += __shfl_xor(beta, 8);
+                beta += __shfl_xor(beta, 4);
+                beta += __shfl_xor(beta, 2);
+                beta += __shfl_xor(beta, 1);
+                if (part == 0) sbeta[j * NR + s] = beta;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- prologue 3: per-head coefficients (log-space decay sums, newest row first) -------
+    for (int pr = tid; pr < nh * T; pr += kThreads) {
+        const int hl = pr / T, j = pr - hl * T;
+        const int e = nstored + j;          // position j's own row
+        const float Ah = sA[hl];
+        float lam = 0.f;
+        for (int s = e; s >= st; --s) {
+            const float dt = sdt[hl * NR + s];
+            scf[(hl * T1 + j) * NR + s] = dt * expf(Ah * lam) * sbeta[j * NR + s];
+            lam += dt;
+        }
+        sdec[hl * T1 + j] = expf(Ah * lam);   // 1 for an empty window
+    }
+    if (fold) {
+        for (int hl = tid; hl < nh; hl += kThreads) {
+            const float Ah = sA[hl];
+            float lam = 0.f;
+            for (int s = nf - 1; s >= 0; --s) {
+                const float dt = sdt[hl * NR + s];
+                sw[hl * NR + s] = dt * expf(Ah * lam);
+                lam += dt;
+            }
+            sdecf[hl] = expf(Ah * lam);
+        }
+    }
+    __syncthreads();
+
+    if constexpr (MODE != kFold) {
+        // ---- prologue 4: record terms and gates of every output ----------------------
+        //   Y[h][j][p] = sum_{s in window j} coef_s x_s[p] + D x_j[p],   Gt[h][j][p] = silu(z_j[p])
+        for (int task = tid; task < nh * T * P4; task += kThreads) {
+            const int p4 = task % P4;
+            const int hj = task / P4;
+            const int hl = hj / T, j = hj - hl * T;
+            const int h = h0 + hl;
+            const int e = nstored + j;
+            const float* cf = scf + (hl * T1 + j) * NR;
+            const float Dh = sD[hl];
+            const float4 xj = io::cvt4(io::ldraw4(xrow(h, e), 4 * p4));
+            const float4 zj = io::cvt4(io::ldraw4(zin, pos_x(h, j) + 4 * p4));
+            float4 y = make_float4(Dh * xj.x, Dh * xj.y, Dh * xj.z, Dh * xj.w);
+            for (int s0 = st; s0 <= e; s0 += kRecBatch) {
+                Raw4 xr[kRecBatch];
+#pragma unroll
+                for (int i = 0; i < kRecBatch; ++i)
+                    if (s0 + i <= e) xr[i] = io::ldraw4(xrow(h, s0 + i), 4 * p4);
+#pragma unroll
+                for (int i = 0; i < kRecBatch; ++i) {
+                    if (s0 + i <= e) {
+                        const float w = cf[s0 + i];
+                        const float4 xv = io::cvt4(xr[i]);
+                        y.x += w * xv.x; y.y += w * xv.y; y.z += w * xv.z; y.w += w * xv.w;
+                    }
+                }
+            }
+            const int o = (hl * T1 + j) * P + 4 * p4;
+            *reinterpret_cast<float4*>(sY + o) = y;
+            *reinterpret_cast<float4*>(sG + o) =
+                make_float4(silu_gate(1.f, zj.x), silu_gate(1.f, zj.y), silu_gate(1.f, zj.z), silu_gate(1.f, zj.w));
+        }
+        __syncthreads();
+    }
+
+    // ---- stream the heads' checkpoint tiles ---------------------------------------------
+    const int q = tid % LPR;
+    const int ridx = q / (LPR / R);
+    const int pw = row0 + ridx * RPP;                // row this lane writes
+    const bool writer = (q % (LPR / R)) == 0 && (!MASK || pw < P);
+
+    for (int hl = 0; hl < nh; ++hl) {
+        const bool more = hl + 1 < nh;
+        if (fold && !idle) {
+            // fold factors u_s[p] = w_s x_s[p] of this head, from the rows loaded last iteration
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kFoldXPerThread; ++i) {
+                const int task = tid + i * kThreads;
+                if (task < nf * P4) {
+                    const int s = task / P4, p4 = task % P4;
+                    const float w = sw[hl * NR + s];
+                    const float4 xv = io::cvt4(xf[i]);
+                    float* d = sU + (4 * p4) * US + s;
+                    d[0] = w * xv.x; d[US] = w * xv.y; d[2 * US] = w * xv.z; d[3 * US] = w * xv.w;
+                }
+            }
+            if (more) issue_foldx(hl + 1);
+        }
+        if (more) issue_tile(hl + 1, vb, lb);
+        if (fold && !idle) __syncthreads();
+
+        if (fold) {
+            if (!idle) {
+                const float decf = sdecf[hl];
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    va[k].x *= decf; va[k].y *= decf; va[k].z *= decf; va[k].w *= decf;
+                }
+                for (int s = 0; s < nf; ++s) {
+                    const float4 Bv = io::cvt4(*reinterpret_cast<const Raw4*>(sB + s * N + 4 * col4));
+#pragma unroll
+                    for (int k = 0; k < R; ++k) {
+                        if (!MASK || row0 + k * RPP < P) {
+                            const float u = sU[(row0 + k * RPP) * US + s];
+                            va[k].x += u * Bv.x; va[k].y += u * Bv.y; va[k].z += u * Bv.z; va[k].w += u * Bv.w;
+                        }
+                    }
+                }
+                const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    if (!MASK || row0 + k * RPP < P) {
+                        const size_t off = t + (size_t)k * RPP * N;
+                        if (!keep_ckpt) *reinterpret_cast<float4*>(a.ckpt + off) = va[k];
+                        if (LOWP) *reinterpret_cast<uint2*>(a.ckpt_lp + off) = f32x4_to_bf16x4(va[k]);
+                    }
+                }
+            }
+        } else if (use_lp) {
+#pragma unroll
+            for (int k = 0; k < R; ++k) va[k] = bf16x4_to_f32x4(la[k]);
+        }
+
+        if constexpr (MODE != kFold) {
+            const int h = h0 + hl;
+            for (int j = 0; j < T; ++j) {
+                const float4 Cv = *reinterpret_cast<const float4*>(sC + j * N + 4 * col4);
+                float acc[R];
+#pragma unroll
+                for (int k = 0; k < R; ++k) acc[k] = dot4(va[k], Cv);
+                const float r = row_reduce<R, LPR>(acc, lane);
+                if (writer) {
+                    const int o = (hl * T1 + j) * P + pw;
+                    a.out[pos_x(h, j) + pw] = (sdec[hl * T1 + j] * r + sY[o]) * sG[o];
+                }
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                va[k] = vb[k];
+                la[k] = lb[k];
+            }
+        }
+    }
+
+    // ---- append this step's records --------------------------------------------------
+    if constexpr (MODE != kFold) {
+        if (MODE == kSpec || !fold) {
+            // speculative rounds may overwrite ring slots that other heads read above
+            if (MODE == kSpec) __syncthreads();
+            const int slot0 = (MODE == kSpec) ? hd + cm : c;
+            for (int task = tid; task < nh * T * P4; task += kThreads) {
+                const int p4 = task % P4;
+                const int hj = task / P4;
+                const int hl = hj / T, j = hj - hl * T;
+                const int h = h0 + hl;
+                const int slot = (slot0 + j) % L;
+                io::straw4(reinterpret_cast<IO*>(a.rec_x), ((bH + h) * L + slot) * P + 4 * p4,
+                           io::ldraw4(xin, pos_x(h, j) + 4 * p4));
+            }
+            for (int task = tid; task < nh * T; task += kThreads) {
+                const int hl = task / T, j = task - hl * T;
+                a.rec_dt[(bH + h0 + hl) * L + (slot0 + j) % L] = sdt[hl * NR + nstored + j];
+            }
+            // the group's B records: with several workgroups per group the host appends
+            // them in a separate launch (speculative rounds only)
+            if (nchunk == 1 || (MODE != kSpec && chunk == 0)) {
+                for (int task = tid; task < T * N4; task += kThreads) {
+                    const int j = task / N4, n4 = task % N4;
+                    io::straw4(reinterpret_cast<IO*>(a.rec_B), ((size_t)(b * G + g) * L + (slot0 + j) % L) * N + 4 * n4,
+                               *reinterpret_cast<const Raw4*>(sB + (nstored + j) * N + 4 * n4));
+                }
+            }
+        }
+    }
+
+    if (tid == 0 && lead) {
+        if (MODE == kSpec) a.flushed[b] = fold ? 1 : 0;
+        else a.cursor_out[b] = (MODE == kFold || fold) ? 0 : c + 1;
+    }
+}
+
+// Appends the speculative round's B vectors to each group's ring (slots
+// (head + committed + j) % L) when a group's heads are split over several
+// workgroups.  Runs after the verify kernel on the same stream, so every head has
+// finished reading the slots it replaces.
+template <typename IO>
+__global__ void __launch_bounds__(kThreads) mamba2_spec_append_B_kernel(Mamba2Args a) {
+    const int G = a.ngroups, N = a.dstate, L = a.L, T = a.n_pos;
+    const size_t total = (size_t)a.batch * T * G * N;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+         i += (size_t)gridDim.x * kThreads) {
+        const int n = (int)(i % N);
+        size_t r = i / N;
+        const int g = (int)(r % G);
+        r /= G;
+        const int j = (int)(r % T);
+        const int b = (int)(r / T);
+        const int hd = a.cursor_in[b], cm = a.committed[b];
+        if (hd < 0 || hd >= L || cm < 0 || cm > L) continue;
+        const int slot = (hd + cm + j) % L;
+        reinterpret_cast<IO*>(a.rec_B)[((size_t)(b * G + g) * L + slot) * N + n] =
+            reinterpret_cast<const IO*>(a.B)[i];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Conventional read-update-write step ("Why SSM layers slow down hybrid models": load
+// the state, update it, read the output, store it -- every step), with the same tiling
+// so that it is a fair baseline.  SNAP: per-position snapshot baseline for speculative
+// decoding -- read snapshot slot_in[b], run the n_pos updates, store all n_pos states.
+// ---------------------------------------------------------------------------------------
+template <int P, int N, typename IO, bool SNAP>
+__global__ void __launch_bounds__(kThreads) mamba2_conventional_kernel(Mamba2ConvArgs a) {
+    using io = Io<IO>;
+    using Tl = Mamba2Tile<P, N>;
+    constexpr int LPR = Tl::LPR, RPP = Tl::RPP, R = Tl::R;
+    constexpr bool MASK = Tl::MASK;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int H = a.nheads, G = a.ngroups;
+    const int hpg = H / G;
+    const int bh = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = bh / H;
+    const int h = bh - b * H;
+    const int g = h / hpg;
+    const int T = SNAP ? a.n_pos : 1;
+    const int row0 = tid / LPR;
+    const int col4 = tid % LPR;
+    constexpr size_t PN = (size_t)P * N;
+
+    size_t src;
+    if constexpr (SNAP) {
+        int sl = a.slot_in[b];
+        sl = sl < 0 ? 0 : (sl >= T ? T - 1 : sl);
+        src = ((size_t)(b * T + sl) * H + h) * PN;
+    } else {
+        src = (size_t)bh * PN;
+    }
+    src += (size_t)row0 * N + 4 * col4;
+    float4 v[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+        if (!MASK || row0 + k * RPP < P)
+            v[k] = *reinterpret_cast<const float4*>(a.state + src + (size_t)k * RPP * N);
+    const float Ah = a.A[h], Dh = a.D[h], bias = a.dt_bias[h];
+    const IO* xin = reinterpret_cast<const IO*>(a.x);
+    const IO* zin = reinterpret_cast<const IO*>(a.z);
+    const IO* Bin = reinterpret_cast<const IO*>(a.B);
+    const IO* Cin = reinterpret_cast<const IO*>(a.C);
+    const IO* dtin = reinterpret_cast<const IO*>(a.dt_raw);
+    const int q = tid % LPR;
+    const int ridx = q / (LPR / R);
+    const int pw = row0 + ridx * RPP;
+    const bool writer = (q % (LPR / R)) == 0 && (!MASK || pw < P);
+
+    for (int j = 0; j < T; ++j) {
+        const size_t xo = SNAP ? ((size_t)(b * T + j) * H + h) * P : (size_t)bh * P;
+        const size_t go = SNAP ? ((size_t)(b * T + j) * G + g) * N : (size_t)(b * G + g) * N;
+        const size_t ho = SNAP ? (size_t)(b * T + j) * H + h : (size_t)bh;
+        float dt = io::ld(dtin, ho) + bias;
+        if (a.dt_softplus) dt = softplus_f32(dt);
+        const float dA = expf(dt * Ah);
+        const float4 Bv = io::ld4(Bin, go + 4 * col4);
+        const float4 Cv = io::ld4(Cin, go + 4 * col4);
+        float acc[R];
+        const size_t dst = (SNAP ? ((size_t)(b * T + j) * H + h) * PN : (size_t)bh * PN) +
+                           (size_t)row0 * N + 4 * col4;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int p = row0 + k * RPP;
+            if (!MASK || p < P) {
+                const float xd = dt * io::ld(xin, xo + p);
+                v[k].x = dA * v[k].x + xd * Bv.x;
+                v[k].y = dA * v[k].y + xd * Bv.y;
+                v[k].z = dA * v[k].z + xd * Bv.z;
+                v[k].w = dA * v[k].w + xd * Bv.w;
+                *reinterpret_cast<float4*>(a.state + dst + (size_t)k * RPP * N) = v[k];
+                acc[k] = dot4(v[k], Cv);
+            } else {
+                acc[k] = 0.f;
+            }
+        }
+        const float r = row_reduce<R, LPR>(acc, lane);
+        if (writer) {
+            const float y = r + Dh * io::ld(xin, xo + pw);
+            a.out[xo + pw] = silu_gate(y, io::ld(zin, xo + pw));
+        }
+    }
+}
+
+}  // namespace rssm

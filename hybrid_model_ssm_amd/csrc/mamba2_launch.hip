@@ -1,0 +1,80 @@
+// Shape checks, LDS sizing and launches of the Mamba2 kernels.
+#include "mamba2_kernels.h"
+#include "mamba2_shapes.h"
+
+namespace rssm {
+
+// ---------------------------------------------------------------------------------------
+// Dispatch over the compiled (dstate, rows-per-thread) set
+// ---------------------------------------------------------------------------------------
+bool mamba2_shape_supported(int P, int N) {
+#define X(PP, NN) \
+    if (P == PP && N == NN) return true;
+    RSSM_SHAPES(X)
+#undef X
+    return false;
+}
+
+// Heads of one group per workgroup: all of them up to kMaxHeadsPerWg, else chunks of
+// kMaxHeadsPerWg (the last chunk holds the remainder, at least one head).
+static void chunking(int hpg, int* nchunk, int* hc) {
+    *hc = hpg < kMaxHeadsPerWg ? hpg : kMaxHeadsPerWg;
+    *nchunk = (hpg + *hc - 1) / *hc;
+}
+
+size_t mamba2_replay_smem_bytes(int P, int N, int hpg, int L, int n_pos, int io_bytes) {
+    const int mode = n_pos > 0 ? kSpec : kDecode;
+    const int T = n_pos > 0 ? n_pos : 1;
+    if (P * L > kFoldXPerThread * 4 * kThreads) return 0;   // fold rows of one head
+    int nchunk, hc;
+    chunking(hpg, &nchunk, &hc);
+    return sizeof(float) * (size_t)GroupSmem(P, N, L, T, hc, mode, io_bytes).total;
+}
+
+size_t mamba2_max_smem_bytes() { return 64 * 1024; }
+
+static const void* find_replay(int P, int N, int io, bool lowp, int mode) {
+    if (io == kIoBF16) {
+        if (mode == kDecode) return replay_kernel_ptr_io1_mode0(P, N, lowp);
+        if (mode == kFold) return replay_kernel_ptr_io1_mode1(P, N, lowp);
+        return replay_kernel_ptr_io1_mode2(P, N, lowp);
+    }
+    if (mode == kDecode) return replay_kernel_ptr_io0_mode0(P, N, lowp);
+    if (mode == kFold) return replay_kernel_ptr_io0_mode1(P, N, lowp);
+    return replay_kernel_ptr_io0_mode2(P, N, lowp);
+}
+
+static const void* find_conv(int P, int N, int io, bool snap) {
+    return io == kIoBF16 ? conv_kernel_ptr_io1(P, N, snap) : conv_kernel_ptr_io0(P, N, snap);
+}
+
+hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int mode, hipStream_t stream) {
+    const void* fn = find_replay(a.headdim, a.dstate, io, a.ckpt_lp != nullptr, mode);
+    if (!fn) return hipErrorInvalidValue;
+    Mamba2Args args = a;
+    chunking(a.nheads / a.ngroups, &args.nchunk, &args.heads_per_chunk);
+    const int T = mode == kSpec ? a.n_pos : (mode == kDecode ? 1 : 0);
+    const size_t smem = sizeof(float) * (size_t)GroupSmem(a.headdim, a.dstate, a.L, T, args.heads_per_chunk, mode,
+                                                          io == kIoBF16 ? 2 : 4).total;
+    void* kargs[] = {&args};
+    const dim3 grid((unsigned)((size_t)a.batch * a.ngroups * args.nchunk));
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), kargs, smem, stream);
+    if (e != hipSuccess || mode != kSpec || args.nchunk == 1) return e;
+    const size_t total = (size_t)a.batch * a.n_pos * a.ngroups * a.dstate;
+    const size_t want = (total + kThreads - 1) / kThreads;
+    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+    const void* app = io == kIoBF16 ? (const void*)&mamba2_spec_append_B_kernel<uint16_t>
+                                    : (const void*)&mamba2_spec_append_B_kernel<float>;
+    return hipLaunchKernel(app, dim3(blocks), dim3(kThreads), kargs, 0, stream);
+}
+
+hipError_t launch_mamba2_conventional(const Mamba2ConvArgs& a, int io, bool snap, hipStream_t stream) {
+    const void* fn = find_conv(a.headdim, a.dstate, io, snap);
+    if (!fn) return hipErrorInvalidValue;
+    Mamba2ConvArgs args = a;
+    void* kargs[] = {&args};
+    const dim3 grid((unsigned)((size_t)a.batch * a.nheads));
+    return hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
+}
+
+}  // namespace rssm

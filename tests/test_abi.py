@@ -118,9 +118,11 @@ def test_mamba2_decode_rejects_bad_pointers(L):
     assert decode(L, err=fake(16) + 2, cout=fake(5)) == INV
 
 
-def test_mamba2_smem_limit_is_unsupported(L):
-    # dstate 256, headdim 64, L=64: the staged window exceeds 64 KiB of LDS
-    assert decode(L, desc=m2desc(dstate=256, buffer_len=64)) == UNS
+def test_mamba2_window_limit_is_unsupported(L):
+    # headdim 128 with L=64: one head's fold rows (headdim * L elements) exceed what the
+    # replay kernel stages per head
+    assert decode(L, desc=m2desc(headdim=128, buffer_len=64)) == UNS
+    assert decode(L, desc=m2desc(headdim=128, dstate=128, buffer_len=33)) == UNS
 
 
 def test_mamba2_flush_and_spec_validation(L):
