@@ -76,6 +76,31 @@ __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 v) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Streaming (non-temporal) accesses for data touched once per launch -- the checkpoint
+// stream.  They keep the checkpoint from displacing the small, reused vectors (records,
+// B/C) in the caches.
+// ---------------------------------------------------------------------------------------
+typedef float rssm_v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int rssm_v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4 ld_stream(const float* p) {
+    const rssm_v4f t = __builtin_nontemporal_load(reinterpret_cast<const rssm_v4f*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 ld_stream(const uint16_t* p) {
+    const rssm_v2u t = __builtin_nontemporal_load(reinterpret_cast<const rssm_v2u*>(p));
+    return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ void st_stream(float* p, float4 v) {
+    rssm_v4f t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<rssm_v4f*>(p));
+}
+__device__ __forceinline__ void st_stream(uint16_t* p, uint2 v) {
+    rssm_v2u t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<rssm_v2u*>(p));
+}
+
+// ---------------------------------------------------------------------------------------
 // Scalar math
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ float softplus_f32(float u) {

@@ -188,16 +188,14 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     // ---- checkpoint tile loads (head hl into v / vl) -------------------------------------
     auto issue_tile = [&](int hl, float4 (&v)[R], uint2 (&vl)[R]) {
         const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
-        if (use_lp) {
+        if (use_lp) {   // uniform per workgroup; the fold and non-fold loops are separate
 #pragma unroll
             for (int k = 0; k < R; ++k)
-                if (!MASK || row0 + k * RPP < P)
-                    vl[k] = *reinterpret_cast<const uint2*>(a.ckpt_lp + t + (size_t)k * RPP * N);
+                if (!MASK || row0 + k * RPP < P) vl[k] = ld_stream(a.ckpt_lp + t + (size_t)k * RPP * N);
         } else if (!idle) {
 #pragma unroll
             for (int k = 0; k < R; ++k)
-                if (!MASK || row0 + k * RPP < P)
-                    v[k] = *reinterpret_cast<const float4*>(a.ckpt + t + (size_t)k * RPP * N);
+                if (!MASK || row0 + k * RPP < P) v[k] = ld_stream(a.ckpt + t + (size_t)k * RPP * N);
         }
     };
     // fold rows of head hl: x_s[p] for s < nf, as 4-element chunks
@@ -330,15 +328,54 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     }
 
     // ---- stream the heads' checkpoint tiles ---------------------------------------------
+    // Each loop issues head hl+1's loads before working on head hl and peels the last
+    // head, so that every load is unconditional and the wait before head hl's work
+    // covers only loads issued before head hl+1's.
     const int q = tid % LPR;
     const int ridx = q / (LPR / R);
     const int pw = row0 + ridx * RPP;                // row this lane writes
     const bool writer = (q % (LPR / R)) == 0 && (!MASK || pw < P);
 
-    for (int hl = 0; hl < nh; ++hl) {
-        const bool more = hl + 1 < nh;
-        if (fold && !idle) {
-            // fold factors u_s[p] = w_s x_s[p] of this head, from the rows loaded last iteration
+    auto outputs = [&](int hl, const float4 (&v)[R]) {
+        if constexpr (MODE != kFold) {
+            const int h = h0 + hl;
+            for (int j = 0; j < T; ++j) {
+                const float4 Cv = *reinterpret_cast<const float4*>(sC + j * N + 4 * col4);
+                float acc[R];
+#pragma unroll
+                for (int k = 0; k < R; ++k) acc[k] = dot4(v[k], Cv);
+                const float r = row_reduce<R, LPR>(acc, lane);
+                if (writer) {
+                    const int o = (hl * T1 + j) * P + pw;
+                    a.out[pos_x(h, j) + pw] = (sdec[hl * T1 + j] * r + sY[o]) * sG[o];
+                }
+            }
+        }
+    };
+    auto rotate = [&]() {
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            va[k] = vb[k];
+            la[k] = lb[k];
+        }
+    };
+
+    if (!fold) {
+        auto body = [&](int hl) {
+            if (use_lp) {
+#pragma unroll
+                for (int k = 0; k < R; ++k) va[k] = bf16x4_to_f32x4(la[k]);
+            }
+            outputs(hl, va);
+        };
+        for (int hl = 0; hl + 1 < nh; ++hl) {
+            issue_tile(hl + 1, vb, lb);
+            body(hl);
+            rotate();
+        }
+        body(nh - 1);
+    } else if (!idle) {
+        auto stage_u = [&](int hl) {     // fold factors u_s[p] = w_s x_s[p] of head hl
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < kFoldXPerThread; ++i) {
@@ -351,64 +388,44 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                     d[0] = w * xv.x; d[US] = w * xv.y; d[2 * US] = w * xv.z; d[3 * US] = w * xv.w;
                 }
             }
-            if (more) issue_foldx(hl + 1);
-        }
-        if (more) issue_tile(hl + 1, vb, lb);
-        if (fold && !idle) __syncthreads();
-
-        if (fold) {
-            if (!idle) {
-                const float decf = sdecf[hl];
+        };
+        auto body = [&](int hl) {
+            __syncthreads();
+            const float decf = sdecf[hl];
 #pragma unroll
-                for (int k = 0; k < R; ++k) {
-                    va[k].x *= decf; va[k].y *= decf; va[k].z *= decf; va[k].w *= decf;
-                }
-                for (int s = 0; s < nf; ++s) {
-                    const float4 Bv = io::cvt4(*reinterpret_cast<const Raw4*>(sB + s * N + 4 * col4));
-#pragma unroll
-                    for (int k = 0; k < R; ++k) {
-                        if (!MASK || row0 + k * RPP < P) {
-                            const float u = sU[(row0 + k * RPP) * US + s];
-                            va[k].x += u * Bv.x; va[k].y += u * Bv.y; va[k].z += u * Bv.z; va[k].w += u * Bv.w;
-                        }
-                    }
-                }
-                const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
+            for (int k = 0; k < R; ++k) {
+                va[k].x *= decf; va[k].y *= decf; va[k].z *= decf; va[k].w *= decf;
+            }
+            for (int s = 0; s < nf; ++s) {
+                const float4 Bv = io::cvt4(*reinterpret_cast<const Raw4*>(sB + s * N + 4 * col4));
 #pragma unroll
                 for (int k = 0; k < R; ++k) {
                     if (!MASK || row0 + k * RPP < P) {
-                        const size_t off = t + (size_t)k * RPP * N;
-                        if (!keep_ckpt) *reinterpret_cast<float4*>(a.ckpt + off) = va[k];
-                        if (LOWP) *reinterpret_cast<uint2*>(a.ckpt_lp + off) = f32x4_to_bf16x4(va[k]);
+                        const float u = sU[(row0 + k * RPP) * US + s];
+                        va[k].x += u * Bv.x; va[k].y += u * Bv.y; va[k].z += u * Bv.z; va[k].w += u * Bv.w;
                     }
                 }
             }
-        } else if (use_lp) {
-#pragma unroll
-            for (int k = 0; k < R; ++k) va[k] = bf16x4_to_f32x4(la[k]);
-        }
-
-        if constexpr (MODE != kFold) {
-            const int h = h0 + hl;
-            for (int j = 0; j < T; ++j) {
-                const float4 Cv = *reinterpret_cast<const float4*>(sC + j * N + 4 * col4);
-                float acc[R];
-#pragma unroll
-                for (int k = 0; k < R; ++k) acc[k] = dot4(va[k], Cv);
-                const float r = row_reduce<R, LPR>(acc, lane);
-                if (writer) {
-                    const int o = (hl * T1 + j) * P + pw;
-                    a.out[pos_x(h, j) + pw] = (sdec[hl * T1 + j] * r + sY[o]) * sG[o];
-                }
-            }
-        }
-        if (more) {
+            const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
 #pragma unroll
             for (int k = 0; k < R; ++k) {
-                va[k] = vb[k];
-                la[k] = lb[k];
+                if (!MASK || row0 + k * RPP < P) {
+                    const size_t off = t + (size_t)k * RPP * N;
+                    if (!keep_ckpt) st_stream(a.ckpt + off, va[k]);
+                    if (LOWP) st_stream(a.ckpt_lp + off, f32x4_to_bf16x4(va[k]));
+                }
             }
+            outputs(hl, va);
+        };
+        for (int hl = 0; hl + 1 < nh; ++hl) {
+            stage_u(hl);
+            issue_foldx(hl + 1);
+            issue_tile(hl + 1, vb, lb);
+            body(hl);
+            rotate();
         }
+        stage_u(nh - 1);
+        body(nh - 1);
     }
 
     // ---- append this step's records --------------------------------------------------
