@@ -23,6 +23,7 @@ conventional).  ``ceiling`` reports plain device read and copy bandwidth.
 Auxiliary modes used to make the committed rocprofv3 summaries:
     --calibrate-copy        also run a plain 1 GiB device copy (counter calibration)
     --pmc-summarize FETCH_DIR WRITE_DIR  turn two rocprofv3 --pmc runs into a summary
+    --stats-summarize STATS_DIR          turn a rocprofv3 --kernel-trace --stats run into a summary
 """
 
 from __future__ import annotations
@@ -44,7 +45,8 @@ PEAK_GBPS = 8000.0
 HEADLINE = "mamba2_h128"
 KERNEL_SOURCES = ["hybrid_model_ssm_amd/csrc/mamba2_kernels.h", "hybrid_model_ssm_amd/csrc/device_common.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_pmc.txt")
-REPLAY_KERNEL_TAG = "mamba2_replay_kernel<128, 8, unsigned short, false, 0>"
+STATS_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_kernel_stats.txt")
+REPLAY_KERNEL_TAG = "mamba2_replay_kernel<64, 128, unsigned short, false, 0>"
 COPY_BYTES = 1 << 30
 MiB = float(1 << 20)
 
@@ -425,8 +427,8 @@ def cpu_baseline(torch, rs, synth, nseq, steps):
     for o, g in zip(outs, gpu_outs):
         worst = max(worst, float(np.max(np.abs(g - o) / (1e-4 * (1 + np.abs(o))))))
     return dict(value=nseq * steps / secs, unit="seq-tokens/s", cores=1, kind="oracle",
-                sample=f"{nseq} of {b.B} sequences x {steps} decode steps (one L={b.L} window incl. its flush) "
-                       f"of the {HEADLINE} workload, NumPy float64 replay form, one process",
+                sample=f"{nseq} of {b.B} sequences x {steps} decode steps ({steps // b.L} L={b.L} windows with "
+                       f"their flushes) of the {HEADLINE} workload, NumPy float64 replay form, one process",
                 seconds=secs, gpu_parity_max_violation=worst, gpu_parity_ok=worst <= 1.0)
 
 
@@ -490,6 +492,39 @@ def pmc_summarize(fetch_dir, write_dir, out_path, command):
     print("\n".join(lines))
 
 
+def stats_summarize(stats_dir, out_path, command, steps=0, warmup=0):
+    """Write the per-kernel summary of a ``rocprofv3 --kernel-trace --stats`` run."""
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_stats.csv under {stats_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
+    lines = ["# rocprofv3 --kernel-trace --stats: kernels of one bench.py run (sorted by total time)",
+             f"command: {command}",
+             f"kernel_source_sha256_16: {kernel_source_hash()}",
+             "calls | avg_us | min_us | max_us | total_ms | kernel"]
+    for r in rows:
+        lines.append("%5d | %8.1f | %8.1f | %8.1f | %8.2f | %s" % (
+            int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e6, r["Name"][:160]))
+    # the headline run is the first warmup+steps dispatches of the replay kernel; the same
+    # kernel instance also serves later workloads of the run, so take them from the trace
+    traces = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if traces and steps:
+        disp = [r for r in csv.DictReader(open(traces[0])) if REPLAY_KERNEL_TAG in r["Kernel_Name"]]
+        disp.sort(key=lambda r: int(r["Start_Timestamp"]))
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in disp[:warmup + steps]]
+        timed = dur[warmup:warmup + steps]
+        if timed:
+            lines.append(f"headline kernel: rssm::{REPLAY_KERNEL_TAG}")
+            lines.append(f"headline timed dispatches: {len(timed)} (after {warmup} warmup), "
+                         f"average {sum(timed) / len(timed):.1f} us, min {min(timed):.1f}, max {max(timed):.1f}")
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:12]))
+
+
 def committed_traffic():
     """Counter-measured bytes per launch from the committed summary, if it matches the source."""
     if not os.path.exists(PMC_SUMMARY):
@@ -513,12 +548,17 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--only", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=128)
+    ap.add_argument("--cpu-seqs", type=int, default=256)
+    ap.add_argument("--cpu-steps", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--stats-summarize", metavar="STATS_DIR")
     args = ap.parse_args(argv)
 
+    if args.stats_summarize:
+        stats_summarize(args.stats_summarize, STATS_SUMMARY, args.pmc_command, args.steps, args.warmup)
+        return 0
     if args.pmc_summarize:
         pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], PMC_SUMMARY, args.pmc_command)
         return 0
@@ -581,7 +621,7 @@ def main(argv=None):
     ceil = ceiling(torch, args.calibrate_copy) if (args.only == "all" or args.calibrate_copy) else None
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(torch, rs, synth, args.cpu_seqs, 16)
+        cpu = cpu_baseline(torch, rs, synth, args.cpu_seqs, args.cpu_steps)
         print(f"[bench] cpu baseline {cpu['value']:.4g} seq-tok/s in {cpu['seconds']:.1f}s", file=sys.stderr,
               flush=True)
         if not cpu["gpu_parity_ok"]:

@@ -1,0 +1,58 @@
+"""Host-side checks of bench.py: byte models, argument handling, profile parsing."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+MiB = 1 << 20
+
+
+def _window_avg(fn, L, **kw):
+    return sum(fn(c=c, L=L, **kw) for c in range(L)) / L / MiB
+
+
+def test_mamba2_byte_model_headline():
+    # B=256, H=128, P=64, N=128, G=8, L=16, bf16 io: state 1088 + io 17.06 + records 39.0 MiB
+    avg = _window_avg(lambda c, L: bench.mamba2_replay_bytes(256, 128, 64, 128, 8, L, 2, c), 16)
+    assert avg == pytest.approx(1144.1, abs=0.05)
+    lp = _window_avg(lambda c, L: bench.mamba2_replay_bytes(256, 128, 64, 128, 8, L, 2, c, True), 16)
+    assert lp == pytest.approx(696.1, abs=0.05)
+    assert bench.mamba2_conventional_bytes(256, 128, 64, 128, 8, 2) / MiB == pytest.approx(2065.06, abs=0.01)
+    # the state part alone: 15 reads + one read and write per window of a 1 GiB checkpoint
+    state_only = (15 * 1024 + 2048) / 16
+    assert state_only == 1088
+
+
+def test_mamba2_byte_model_h64_and_gdn():
+    assert _window_avg(lambda c, L: bench.mamba2_replay_bytes(256, 64, 64, 128, 8, L, 2, c), 16) == \
+        pytest.approx(574.65, abs=0.01)
+    assert _window_avg(lambda c, L: bench.gdn_replay_bytes(256, 32, 16, 128, 128, L, 2, c), 16) == \
+        pytest.approx(577.9, abs=0.05)
+    assert bench.gdn_conventional_bytes(256, 32, 16, 128, 128, 2) / MiB == pytest.approx(1032.06, abs=0.01)
+
+
+def test_spec_byte_model_flush_and_plain_rounds():
+    H, P, N, G, L, T = 128, 64, 128, 8, 16, 4
+    plain = bench.spec_round_bytes(H, P, N, G, L, 2, T, [0])
+    flush = bench.spec_round_bytes(H, P, N, G, L, 2, T, [13])
+    # a flushing round writes the checkpoint: one more P*N*4 per head
+    assert flush - plain - 13 * (H * (P * 2 + 4) + G * N * 2) == H * P * N * 4
+    assert bench.spec_baseline_bytes(1, H, P, N, G, 2, T) == H * (P * N * 4 * 5 + T * (2 * P * 2 + 2 + P * 4)) + \
+        G * T * 2 * N * 2
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_committed_counter_summary_parses():
+    traffic, src = bench.committed_traffic()
+    assert traffic is None or traffic > 1e9
+    assert isinstance(src, str)
