@@ -546,7 +546,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024, help="timed decode steps of the headline")
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--only", choices=["all", "headline"], default="all")
+    ap.add_argument("--only", default="all",
+                    help="all, headline, or a comma list of: conventional,bf16,h64,spec,gdn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--cpu-steps", type=int, default=32)
@@ -597,26 +598,33 @@ def main(argv=None):
 
     variants = {}
     conv = None
-    if args.only == "all":
+    groups = {"conventional", "bf16", "h64", "spec", "gdn"} if args.only == "all" else \
+        set() if args.only == "headline" else set(args.only.split(","))
+    if "conventional" in groups:
         conv, _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup, conventional=True)
         torch.cuda.empty_cache()
         variants["mamba2_h128_conventional"] = conv
+    if "bf16" in groups:
         variants["mamba2_h128_bf16_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup,
                                                            lowp=True)
         torch.cuda.empty_cache()
+    if "h64" in groups:
         variants["mamba2_h64_replay"], _ = time_mamba2(torch, rs, synth, "mamba2_h64", 256, 32)
         torch.cuda.empty_cache()
         variants["mamba2_h64_conventional"], _ = time_mamba2(torch, rs, synth, "mamba2_h64", 256, 32,
                                                              conventional=True)
         torch.cuda.empty_cache()
+    if "spec" in groups:
         variants["spec_h128_verify"] = time_spec(torch, rs, synth, 256, 32)
         torch.cuda.empty_cache()
         variants["spec_h128_snapshot_baseline"] = time_spec(torch, rs, synth, 256, 32, baseline=True)
         torch.cuda.empty_cache()
+    if "gdn" in groups:
         variants["gdn_hv32_replay"] = time_gdn(torch, rs, synth, 512, 32)
         torch.cuda.empty_cache()
         variants["gdn_hv32_conventional"] = time_gdn(torch, rs, synth, 512, 32, conventional=True)
         torch.cuda.empty_cache()
+    if variants:
         print("[bench] variants done", file=sys.stderr, flush=True)
     ceil = ceiling(torch, args.calibrate_copy) if (args.only == "all" or args.calibrate_copy) else None
     cpu = None

@@ -266,7 +266,8 @@ replayssm_status replayssm_gdn_decode(const replayssm_gdn_desc* desc, const repl
         aligned(out, 4));
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
-    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len) > rssm::mamba2_max_smem_bytes())
+    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len, desc->num_v_heads / desc->num_k_heads,
+                             desc->io_dtype == REPLAYSSM_BF16 ? 2 : 4) > rssm::mamba2_max_smem_bytes())
         return REPLAYSSM_ERR_UNSUPPORTED;
     rssm::GdnArgs a = gdn_args(desc);
     a.ckpt = state->ckpt; a.rec_k = state->rec_k; a.rec_v = state->rec_v;
@@ -286,7 +287,8 @@ replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const repla
         aligned(state->rec_alpha, 4) && aligned(state->rec_beta, 4));
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
-    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len) > rssm::mamba2_max_smem_bytes())
+    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len, desc->num_v_heads / desc->num_k_heads,
+                             desc->io_dtype == REPLAYSSM_BF16 ? 2 : 4) > rssm::mamba2_max_smem_bytes())
         return REPLAYSSM_ERR_UNSUPPORTED;
     rssm::GdnArgs a = gdn_args(desc);
     a.ckpt = state->ckpt; a.rec_k = state->rec_k; a.rec_v = state->rec_v;

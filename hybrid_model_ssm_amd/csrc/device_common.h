@@ -116,9 +116,11 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Workgroup -> tile mapping.  The hardware hands workgroups to the 8 XCDs round
-// robin (id % 8).  Remap so that consecutive logical tiles run on the same XCD and
-// share its L2 (the heads of one group read the same B/C vectors and records).
+// Workgroup -> tile mapping for kernels whose neighbouring workgroups share inputs (the
+// conventional kernels: the heads of one group read the same B/C).  The hardware hands
+// workgroups to the 8 XCDs round robin (id % 8); the remap puts consecutive logical
+// tiles on one XCD so they share its L2.  The replay kernels do not use it: a replay
+// workgroup owns its whole group, and there the hardware order streams faster.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     if (nblocks % kNumXcd) return bid;

@@ -66,6 +66,8 @@ struct GdnArgs {
     int32_t* err_flags;
     int32_t batch, hv, hk, dk, dv, L;
     float scale;
+    int32_t nchunk;            // workgroups per (sequence, q/k head)
+    int32_t vheads_per_chunk;
 };
 
 bool mamba2_shape_supported(int headdim, int dstate);
@@ -86,7 +88,7 @@ hipError_t launch_reset(int32_t batch, int32_t* head, int32_t* cursor, const int
                         int32_t n_seq, hipStream_t stream);
 
 bool gdn_shape_supported(int dk, int dv);
-size_t gdn_smem_bytes(int dk, int dv, int L);
+size_t gdn_smem_bytes(int dk, int dv, int L, int heads_ratio, int io_bytes);
 // mode: 0 = AR decode, 1 = fold stored records only
 hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t stream);
 hipError_t launch_gdn_conventional(const GdnArgs& a, int io, hipStream_t stream);

@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     const int H = a.nheads, G = a.ngroups, L = a.L;
     const int hpg = H / G;
     const int nchunk = a.nchunk;
-    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int wid = blockIdx.x;
     const int chunk = wid % nchunk;
     const int bg = wid / nchunk;
     const int b = bg / G;

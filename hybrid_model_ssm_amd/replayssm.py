@@ -19,7 +19,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libreplayssm.so")
+# the in-tree build; REPLAYSSM_LIB may name another build of the same library
+LIB_PATH = os.environ.get("REPLAYSSM_LIB") or os.path.join(_HERE, "libreplayssm.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 F32, BF16 = 0, 1
