@@ -128,32 +128,68 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Cross-lane exchange without LDS.  exchange<D>(a, b) pairs every lane with a partner
+// whose lane-id bit log2(D) is the opposite of its own (lanes stay within aligned groups
+// of 2D) and returns, in every lane, its own value of one operand plus the partner's
+// value of the same operand: lanes with the bit clear get a_own + a_partner, lanes with
+// the bit set get b_own + b_partner.  Distances 1..8 use DPP inside a 16-lane row
+// (quad_perm for 1 and 2, the half-row mirror for 4, a row rotation by 8 for 8);
+// 16 and 32 use the gfx950 permlane swaps, which exchange both operands at once.
+// ---------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+template <int D>
+__device__ __forceinline__ float exchange(float a, float b, int lane) {
+    if constexpr (D == 16 || D == 32) {
+        const auto r = (D == 16)
+            ? __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+            : __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        // lanes with the bit clear now hold (a_own, a_partner), the others (b_partner, b_own)
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const bool up = (lane & D) != 0;
+        const float send = up ? a : b;      // the partner keeps the operand this lane drops
+        const float keep = up ? b : a;
+        constexpr int CTRL = (D == 1) ? 0xB1 : (D == 2) ? 0x4E : (D == 4) ? 0x141 : 0x128;
+        return keep + dpp_mov<CTRL>(send);
+    }
+}
+
+// Sum over an aligned group of W lanes (W a power of two <= 64), returned to all of them.
+template <int W>
+__device__ __forceinline__ float group_allreduce(float x, int lane) {
+    if constexpr (W >= 64) x = exchange<32>(x, x, lane);
+    if constexpr (W >= 32) x = exchange<16>(x, x, lane);
+    if constexpr (W >= 16) x = exchange<8>(x, x, lane);
+    if constexpr (W >= 8) x = exchange<4>(x, x, lane);
+    if constexpr (W >= 4) x = exchange<2>(x, x, lane);
+    if constexpr (W >= 2) x = exchange<1>(x, x, lane);
+    return x;
+}
+
+// ---------------------------------------------------------------------------------------
 // Row reduction across the LPR consecutive lanes that share R rows.
 //
-// Each lane holds partial sums v[0..R) for R rows.  At each butterfly level a lane
-// keeps one half of its values and sends the other half to its partner, so R values
-// take R-1 exchanges in total instead of R*log2(LPR).  On return v[0] is the full
-// sum of row index  (lane % LPR) / (LPR / R);  the LPR/R lanes with the same row
-// index hold copies.  Requires R <= LPR, both powers of two, LPR <= 64, and the LPR
-// lanes aligned to a multiple of LPR.
+// Each lane holds partial sums v[0..R) for R rows.  At each level a lane keeps one half
+// of its values (the upper half when its level bit is set) and adds the partner's copy
+// of that half, so R values take R-1 exchanges in total instead of R*log2(LPR).  On
+// return v[0] is the full sum of row index  (lane % LPR) / (LPR / R);  the LPR/R lanes
+// with the same row index hold copies.  Requires R <= LPR, both powers of two,
+// LPR <= 64, and the LPR lanes aligned to a multiple of LPR.
 // ---------------------------------------------------------------------------------------
 template <int CNT, int D>
 struct RowReduce {
     __device__ static __forceinline__ void run(float* v, int lane) {
         if constexpr (D == 0) {
             static_assert(CNT == 1, "R must not exceed LPR");
-        } else if constexpr (CNT == 1) {
-            v[0] += __shfl_xor(v[0], D);
-            RowReduce<1, D / 2>::run(v, lane);
         } else {
-            const bool up = (lane & D) != 0;
 #pragma unroll
-            for (int i = 0; i < CNT / 2; ++i) {
-                const float send = up ? v[i] : v[i + CNT / 2];
-                const float keep = up ? v[i + CNT / 2] : v[i];
-                v[i] = keep + __shfl_xor(send, D);
-            }
-            RowReduce<CNT / 2, D / 2>::run(v, lane);
+            for (int i = 0; i < (CNT > 1 ? CNT / 2 : 1); ++i)
+                v[i] = exchange<D>(v[i], CNT > 1 ? v[i + CNT / 2] : v[i], lane);
+            RowReduce<(CNT > 1 ? CNT / 2 : 1), D / 2>::run(v, lane);
         }
     }
 };
@@ -180,14 +216,6 @@ __device__ __forceinline__ void row_allreduce(float (&v)[R], int lane) {
     const int base = lane & ~(LPR - 1);
 #pragma unroll
     for (int k = 0; k < R; ++k) v[k] = __shfl(mine, base + k * (LPR / R));
-}
-
-// Sum over a power-of-two group of W consecutive lanes, returned to all of them.
-template <int W>
-__device__ __forceinline__ float group_allreduce(float x) {
-#pragma unroll
-    for (int d = W / 2; d >= 1; d >>= 1) x += __shfl_xor(x, d);
-    return x;
 }
 
 }  // namespace rssm

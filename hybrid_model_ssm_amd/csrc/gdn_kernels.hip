@@ -174,7 +174,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 float kap = 0.f;
 #pragma unroll
                 for (int m = 0; m < UPL; ++m) kap += sK[s * DK + lane + m * kWave] * u[m];
-                kap = group_allreduce<kWave>(kap);
+                kap = group_allreduce<kWave>(kap, lane);
                 const float bk = be[s] * kap;
                 if (lane == 0) sCoef[wave * L + s] = bk;
                 const float as = al[s];
@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_conventional_kernel(GdnArgs a
     const float4 Qv = io::ld4(reinterpret_cast<const IO*>(a.q), qk_off + 4 * col4);
     const IO* vin = reinterpret_cast<const IO*>(a.v);
     const float al = a.alpha[bhv], be = a.beta[bhv];
-    const float kq = group_allreduce<LPR>(dot4(Kv, Qv));
+    const float kq = group_allreduce<LPR>(dot4(Kv, Qv), lane);
 
     float d[R], e[R];
 #pragma unroll

@@ -58,7 +58,7 @@ struct Mamba2Tile {
 // LDS layout of the replay kernel (in 4-byte words).
 struct GroupSmem {
     int NR, T1, US;
-    int oB, oC, oDt, oBeta, oCf, oDec, oW, oDecf, oY, oG, oU, oA, oD, total;
+    int oB, oC, oDt, oBeta, oCf, oDec, oW, oDecf, oY, oZ, oU, oA, oD, total;
     __host__ __device__ GroupSmem(int P, int N, int L, int T, int HC, int mode, int io_bytes) {
         NR = (mode == kSpec) ? L + T : L;   // most window rows
         T1 = T > 0 ? T : 1;
@@ -72,8 +72,8 @@ struct GroupSmem {
         oW = oDec + HC * T1;                // [HC][NR]      fold weights
         oDecf = oW + HC * NR;               // [HC]          fold decays
         oY = oDecf + HC;                    // [HC][T1][P]   record terms + D x of each output
-        oG = oY + HC * T1 * P;              // [HC][T1][P]   silu(z) of each output
-        oU = oG + HC * T1 * P;              // [P][US]       fold factors w_s x_s[p] of one head
+        oZ = oY + HC * T1 * P;              // [HC][T1][P] io  z of each output
+        oU = oZ + (HC * T1 * P * io_bytes + 3) / 4;  // [P][US]  fold factors w_s x_s[p] of one head
         oA = oU + P * US;                   // [HC]
         oD = oA + HC;                       // [HC]
         total = oD + HC;
@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     float* sw = smem + lay.oW;
     float* sdecf = smem + lay.oDecf;
     float* sY = smem + lay.oY;
-    float* sG = smem + lay.oG;
+    IO* sZ = reinterpret_cast<IO*>(smem + lay.oZ);
     float* sU = smem + lay.oU;
     float* sA = smem + lay.oA;
     float* sD = smem + lay.oD;
@@ -254,10 +254,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 const int j = pr / nrec, s = pr - j * nrec;
                 float beta = 0.f;
                 for (int n = part; n < N; n += 16) beta += io::ld(sB, s * N + n) * sC[j * N + n];
-                beta += __shfl_xor(beta, 8);
-                beta += __shfl_xor(beta, 4);
-                beta += __shfl_xor(beta, 2);
-                beta += __shfl_xor(beta, 1);
+                beta = group_allreduce<16>(beta, lane);
                 if (part == 0) sbeta[j * NR + s] = beta;
             }
         }
@@ -292,37 +289,57 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     __syncthreads();
 
     if constexpr (MODE != kFold) {
-        // ---- prologue 4: record terms and gates of every output ----------------------
-        //   Y[h][j][p] = sum_{s in window j} coef_s x_s[p] + D x_j[p],   Gt[h][j][p] = silu(z_j[p])
-        for (int task = tid; task < nh * T * P4; task += kThreads) {
+        // ---- prologue 4: record terms of every output, and z ---------------------------
+        //   Y[h][j][p] = sum_{s in window j} coef_s x_s[p] + D x_j[p]
+        // One task per (head, 4 columns, up to kPosBatch positions): each window row is
+        // loaded once and feeds every position whose window holds it.
+        constexpr int kPosBatch = 4;
+        const int njb = (T + kPosBatch - 1) / kPosBatch;
+        for (int task = tid; task < nh * njb * P4; task += kThreads) {
             const int p4 = task % P4;
-            const int hj = task / P4;
-            const int hl = hj / T, j = hj - hl * T;
+            const int hb = task / P4;
+            const int hl = hb / njb, j0 = (hb - hl * njb) * kPosBatch;
             const int h = h0 + hl;
-            const int e = nstored + j;
-            const float* cf = scf + (hl * T1 + j) * NR;
+            const int jn = min(kPosBatch, T - j0);
+            const int elast = nstored + j0 + jn - 1;        // last row any of these windows uses
             const float Dh = sD[hl];
-            const float4 xj = io::cvt4(io::ldraw4(xrow(h, e), 4 * p4));
-            const float4 zj = io::cvt4(io::ldraw4(zin, pos_x(h, j) + 4 * p4));
-            float4 y = make_float4(Dh * xj.x, Dh * xj.y, Dh * xj.z, Dh * xj.w);
-            for (int s0 = st; s0 <= e; s0 += kRecBatch) {
+            float4 y[kPosBatch];
+#pragma unroll
+            for (int jj = 0; jj < kPosBatch; ++jj) y[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int s0 = st; s0 <= elast; s0 += kRecBatch) {
                 Raw4 xr[kRecBatch];
 #pragma unroll
                 for (int i = 0; i < kRecBatch; ++i)
-                    if (s0 + i <= e) xr[i] = io::ldraw4(xrow(h, s0 + i), 4 * p4);
+                    if (s0 + i <= elast) xr[i] = io::ldraw4(xrow(h, s0 + i), 4 * p4);
 #pragma unroll
                 for (int i = 0; i < kRecBatch; ++i) {
-                    if (s0 + i <= e) {
-                        const float w = cf[s0 + i];
+                    const int sr = s0 + i;
+                    if (sr <= elast) {
                         const float4 xv = io::cvt4(xr[i]);
-                        y.x += w * xv.x; y.y += w * xv.y; y.z += w * xv.z; y.w += w * xv.w;
+#pragma unroll
+                        for (int jj = 0; jj < kPosBatch; ++jj) {
+                            const int j = j0 + jj;
+                            if (jj < jn && sr <= nstored + j) {
+                                float w = scf[(hl * T1 + j) * NR + sr];
+                                if (sr == nstored + j) w += Dh;     // position j's own row: + D x_j
+                                y[jj].x += w * xv.x; y[jj].y += w * xv.y; y[jj].z += w * xv.z; y[jj].w += w * xv.w;
+                            }
+                        }
                     }
                 }
             }
-            const int o = (hl * T1 + j) * P + 4 * p4;
-            *reinterpret_cast<float4*>(sY + o) = y;
-            *reinterpret_cast<float4*>(sG + o) =
-                make_float4(silu_gate(1.f, zj.x), silu_gate(1.f, zj.y), silu_gate(1.f, zj.z), silu_gate(1.f, zj.w));
+            // rows before st (flushed windows) still need D x_j for position j's own row
+            for (int jj = 0; jj < jn; ++jj) {
+                const int j = j0 + jj;
+                const int o = (hl * T1 + j) * P + 4 * p4;
+                float4 yv = y[jj];
+                if (nstored + j < st) {     // empty window (AR flush step): only D x_j
+                    const float4 xj = io::cvt4(io::ldraw4(xrow(h, nstored + j), 4 * p4));
+                    yv = make_float4(Dh * xj.x, Dh * xj.y, Dh * xj.z, Dh * xj.w);
+                }
+                *reinterpret_cast<float4*>(sY + o) = yv;
+                *reinterpret_cast<Raw4*>(sZ + o) = io::ldraw4(zin, pos_x(h, j) + 4 * p4);
+            }
         }
         __syncthreads();
     }
@@ -347,7 +364,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 const float r = row_reduce<R, LPR>(acc, lane);
                 if (writer) {
                     const int o = (hl * T1 + j) * P + pw;
-                    a.out[pos_x(h, j) + pw] = (sdec[hl * T1 + j] * r + sY[o]) * sG[o];
+                    a.out[pos_x(h, j) + pw] = silu_gate(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
                 }
             }
         }
