@@ -111,6 +111,13 @@ __device__ __forceinline__ float silu_gate(float y, float z) {
     return y * z / (1.0f + expf(-z));
 }
 
+// The same gate with the hardware exponential and reciprocal (relative error ~1e-7):
+// used on the per-output path of the replay kernels.  For z -> -inf the reciprocal of
+// +inf is 0, so the result goes to 0 like the exact form.
+__device__ __forceinline__ float silu_gate_fast(float y, float z) {
+    return (y * z) * __frcp_rn(1.0f + __expf(-z));
+}
+
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }

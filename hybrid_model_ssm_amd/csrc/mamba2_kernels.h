@@ -353,18 +353,39 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     const int pw = row0 + ridx * RPP;                // row this lane writes
     const bool writer = (q % (LPR / R)) == 0 && (!MASK || pw < P);
 
+    // Speculative verify reduces TB positions of a head in one transpose-reduce: R*TB
+    // values over LPR lanes, after which every lane owns one (row, position) output.
+    constexpr int TB = (MODE == kSpec) ? LPR / R : 1;
     auto outputs = [&](int hl, const float4 (&v)[R]) {
-        if constexpr (MODE != kFold) {
+        if constexpr (MODE == kDecode) {
             const int h = h0 + hl;
-            for (int j = 0; j < T; ++j) {
-                const float4 Cv = *reinterpret_cast<const float4*>(sC + j * N + 4 * col4);
-                float acc[R];
+            const float4 Cv = *reinterpret_cast<const float4*>(sC + 4 * col4);
+            float acc[R];
 #pragma unroll
-                for (int k = 0; k < R; ++k) acc[k] = dot4(v[k], Cv);
-                const float r = row_reduce<R, LPR>(acc, lane);
-                if (writer) {
-                    const int o = (hl * T1 + j) * P + pw;
-                    a.out[pos_x(h, j) + pw] = silu_gate(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
+            for (int k = 0; k < R; ++k) acc[k] = dot4(v[k], Cv);
+            const float r = row_reduce<R, LPR>(acc, lane);
+            if (writer) {
+                const int o = hl * T1 * P + pw;
+                a.out[pos_x(h, 0) + pw] = silu_gate_fast(sdec[hl * T1] * r + sY[o], io::ld(sZ, o));
+            }
+        } else if constexpr (MODE == kSpec) {
+            const int h = h0 + hl;
+            for (int j0 = 0; j0 < T; j0 += TB) {
+                float acc[R * TB];
+#pragma unroll
+                for (int jj = 0; jj < TB; ++jj) {
+                    const int j = min(j0 + jj, T - 1);
+                    const float4 Cv = *reinterpret_cast<const float4*>(sC + j * N + 4 * col4);
+#pragma unroll
+                    for (int k = 0; k < R; ++k) acc[jj * R + k] = dot4(v[k], Cv);
+                }
+                const float r = row_reduce<R * TB, LPR>(acc, lane);
+                const int vi = q / (LPR / (R * TB));          // value index this lane holds
+                const int j = j0 + vi / R;
+                const int p = row0 + (vi % R) * RPP;
+                if ((q % (LPR / (R * TB))) == 0 && j < T && (!MASK || p < P)) {
+                    const int o = (hl * T1 + j) * P + p;
+                    a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
                 }
             }
         }
