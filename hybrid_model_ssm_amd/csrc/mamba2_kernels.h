@@ -216,6 +216,20 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     issue_tile(0, va, la);
     if (fold && !idle) issue_foldx(0);
 
+    // this call's records, loaded now and stored after every head has read the ring
+    constexpr int kAppendPerThread = 4;
+    const int napp = (MODE == kFold || (MODE == kDecode && fold)) ? 0 : nh * T * P4;
+    Raw4 app[kAppendPerThread];
+#pragma unroll
+    for (int i = 0; i < kAppendPerThread; ++i) {
+        const int task = tid + i * kThreads;
+        if (task < napp) {
+            const int p4 = task % P4, hj = task / P4;
+            const int hl = hj / T, j = hj - hl * T;
+            app[i] = io::ldraw4(xin, pos_x(h0 + hl, j) + 4 * p4);
+        }
+    }
+
     // ---- prologue 1: stage the group's window -------------------------------------------
     for (int task = tid; task < nrec * N4; task += kThreads) {
         const int s = task / N4, n4 = task % N4;
@@ -406,6 +420,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
             }
             outputs(hl, va);
         };
+        // tile hl+1 is loaded while head hl is reduced
         for (int hl = 0; hl + 1 < nh; ++hl) {
             issue_tile(hl + 1, vb, lb);
             body(hl);
@@ -472,14 +487,22 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
             // speculative rounds may overwrite ring slots that other heads read above
             if (MODE == kSpec) __syncthreads();
             const int slot0 = (MODE == kSpec) ? hd + cm : c;
-            for (int task = tid; task < nh * T * P4; task += kThreads) {
-                const int p4 = task % P4;
-                const int hj = task / P4;
+#pragma unroll
+            for (int i = 0; i < kAppendPerThread; ++i) {
+                const int task = tid + i * kThreads;
+                if (task < napp) {
+                    const int p4 = task % P4, hj = task / P4;
+                    const int hl = hj / T, j = hj - hl * T;
+                    const int slot = (slot0 + j) % L;
+                    io::straw4(reinterpret_cast<IO*>(a.rec_x), ((bH + h0 + hl) * L + slot) * P + 4 * p4, app[i]);
+                }
+            }
+            for (int task = tid + kAppendPerThread * kThreads; task < napp; task += kThreads) {
+                const int p4 = task % P4, hj = task / P4;
                 const int hl = hj / T, j = hj - hl * T;
-                const int h = h0 + hl;
                 const int slot = (slot0 + j) % L;
-                io::straw4(reinterpret_cast<IO*>(a.rec_x), ((bH + h) * L + slot) * P + 4 * p4,
-                           io::ldraw4(xin, pos_x(h, j) + 4 * p4));
+                io::straw4(reinterpret_cast<IO*>(a.rec_x), ((bH + h0 + hl) * L + slot) * P + 4 * p4,
+                           io::ldraw4(xin, pos_x(h0 + hl, j) + 4 * p4));
             }
             for (int task = tid; task < nh * T; task += kThreads) {
                 const int hl = task / T, j = task - hl * T;
