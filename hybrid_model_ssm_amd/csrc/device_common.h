@@ -82,6 +82,7 @@ __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 v) {
 // ---------------------------------------------------------------------------------------
 typedef float rssm_v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int rssm_v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int rssm_v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ld_stream(const float* p) {
     const rssm_v4f t = __builtin_nontemporal_load(reinterpret_cast<const rssm_v4f*>(p));
@@ -90,6 +91,11 @@ __device__ __forceinline__ float4 ld_stream(const float* p) {
 __device__ __forceinline__ uint2 ld_stream(const uint16_t* p) {
     const rssm_v2u t = __builtin_nontemporal_load(reinterpret_cast<const rssm_v2u*>(p));
     return make_uint2(t.x, t.y);
+}
+// eight bf16 values (16 bytes)
+__device__ __forceinline__ uint4 ld_stream8(const uint16_t* p) {
+    const rssm_v4u t = __builtin_nontemporal_load(reinterpret_cast<const rssm_v4u*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
 }
 __device__ __forceinline__ void st_stream(float* p, float4 v) {
     rssm_v4f t = {v.x, v.y, v.z, v.w};

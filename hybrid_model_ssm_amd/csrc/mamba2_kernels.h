@@ -55,6 +55,17 @@ struct Mamba2Tile {
     static_assert(R >= 1 && R <= LPR && (R & (R - 1)) == 0, "tile shape");
 };
 
+// Mapping of a tile read from the bf16 copy: 16-byte loads of 8 elements, N/8 lanes
+// per row.
+template <int P, int N>
+struct Mamba2TileLp {
+    static constexpr int LPR = N / 8;
+    static constexpr int RPP = kThreads / LPR;
+    static constexpr int R = (P + RPP - 1) / RPP;
+    static constexpr bool MASK = (P % RPP) != 0;
+    static_assert(R >= 1 && R <= LPR && (R & (R - 1)) == 0, "bf16 tile shape");
+};
+
 // LDS layout of the replay kernel (in 4-byte words).
 struct GroupSmem {
     int NR, T1, US;
@@ -186,17 +197,24 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     };
 
     // ---- checkpoint tile loads (head hl into v / vl) -------------------------------------
-    auto issue_tile = [&](int hl, float4 (&v)[R], uint2 (&vl)[R]) {
-        const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
-        if (use_lp) {   // uniform per workgroup; the fold and non-fold loops are separate
-#pragma unroll
-            for (int k = 0; k < R; ++k)
-                if (!MASK || row0 + k * RPP < P) vl[k] = ld_stream(a.ckpt_lp + t + (size_t)k * RPP * N);
-        } else if (!idle) {
+    auto issue_tile = [&](int hl, float4 (&v)[R]) {
+        if (!idle) {
+            const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
 #pragma unroll
             for (int k = 0; k < R; ++k)
                 if (!MASK || row0 + k * RPP < P) v[k] = ld_stream(a.ckpt + t + (size_t)k * RPP * N);
         }
+    };
+    // tiles of the bf16 read copy (non-flush steps with LOWP), in their own mapping
+    using Tq = Mamba2TileLp<P, N>;
+    constexpr int RQ = Tq::R;
+    const int rowq0 = tid / Tq::LPR;
+    const int colq = tid % Tq::LPR;
+    auto issue_tile_lp = [&](int hl, uint4 (&v)[RQ]) {
+        const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)rowq0 * N + 8 * colq;
+#pragma unroll
+        for (int k = 0; k < RQ; ++k)
+            if (!Tq::MASK || rowq0 + k * Tq::RPP < P) v[k] = ld_stream8(a.ckpt_lp + t + (size_t)k * Tq::RPP * N);
     };
     // fold rows of head hl: x_s[p] for s < nf, as 4-element chunks
     Raw4 xf[kFoldXPerThread];
@@ -212,14 +230,17 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     };
 
     float4 va[R], vb[R];
-    uint2 la[R], lb[R];
-    issue_tile(0, va, la);
+    uint4 qa[RQ], qb[RQ];
+    if (use_lp) issue_tile_lp(0, qa);
+    else issue_tile(0, va);
     if (fold && !idle) issue_foldx(0);
 
     // this call's records, loaded now and stored after every head has read the ring
-    constexpr int kAppendPerThread = 4;
+    // (autoregressive decode only: in speculative mode they would stay live across the
+    // head loop and cost occupancy)
+    constexpr int kAppendPerThread = (MODE == kDecode) ? 2 : 0;
     const int napp = (MODE == kFold || (MODE == kDecode && fold)) ? 0 : nh * T * P4;
-    Raw4 app[kAppendPerThread];
+    Raw4 app[kAppendPerThread > 0 ? kAppendPerThread : 1];
 #pragma unroll
     for (int i = 0; i < kAppendPerThread; ++i) {
         const int task = tid + i * kThreads;
@@ -367,9 +388,10 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     const int pw = row0 + ridx * RPP;                // row this lane writes
     const bool writer = (q % (LPR / R)) == 0 && (!MASK || pw < P);
 
-    // Speculative verify reduces TB positions of a head in one transpose-reduce: R*TB
-    // values over LPR lanes, after which every lane owns one (row, position) output.
-    constexpr int TB = (MODE == kSpec) ? LPR / R : 1;
+    // Speculative verify reduces TB positions of a head in one transpose-reduce (R*TB
+    // values over LPR lanes; two positions keep the register budget of three waves per
+    // SIMD).
+    constexpr int TB = (MODE == kSpec) ? (LPR / R >= 2 ? 2 : 1) : 1;
     auto outputs = [&](int hl, const float4 (&v)[R]) {
         if constexpr (MODE == kDecode) {
             const int h = h0 + hl;
@@ -406,27 +428,58 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     };
     auto rotate = [&]() {
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            va[k] = vb[k];
-            la[k] = lb[k];
+        for (int k = 0; k < R; ++k) va[k] = vb[k];
+    };
+
+    // outputs of head hl from a bf16-copy tile: same arithmetic as `outputs`, in the
+    // 8-elements-per-lane mapping
+    auto outputs_lp = [&](int hl, const uint4 (&v)[RQ]) {
+        if constexpr (MODE != kFold) {
+            constexpr int LQ = Tq::LPR;
+            constexpr int TBQ = (MODE == kSpec) ? LQ / RQ : 1;
+            const int h = h0 + hl;
+            const int qq = tid % LQ;
+            for (int j0 = 0; j0 < T; j0 += TBQ) {
+                float acc[RQ * TBQ];
+#pragma unroll
+                for (int jj = 0; jj < TBQ; ++jj) {
+                    const int j = min(j0 + jj, T - 1);
+                    const float4 C0 = *reinterpret_cast<const float4*>(sC + j * N + 8 * colq);
+                    const float4 C1 = *reinterpret_cast<const float4*>(sC + j * N + 8 * colq + 4);
+#pragma unroll
+                    for (int k = 0; k < RQ; ++k)
+                        acc[jj * RQ + k] = dot4(bf16x4_to_f32x4(make_uint2(v[k].x, v[k].y)), C0) +
+                                           dot4(bf16x4_to_f32x4(make_uint2(v[k].z, v[k].w)), C1);
+                }
+                const float r = row_reduce<RQ * TBQ, LQ>(acc, lane);
+                const int vi = qq / (LQ / (RQ * TBQ));
+                const int j = j0 + vi / RQ;
+                const int p = rowq0 + (vi % RQ) * Tq::RPP;
+                if ((qq % (LQ / (RQ * TBQ))) == 0 && j < T && (!Tq::MASK || p < P)) {
+                    const int o = (hl * T1 + j) * P + p;
+                    a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
+                }
+            }
         }
     };
 
-    if (!fold) {
-        auto body = [&](int hl) {
-            if (use_lp) {
-#pragma unroll
-                for (int k = 0; k < R; ++k) va[k] = bf16x4_to_f32x4(la[k]);
-            }
-            outputs(hl, va);
-        };
+    if (!fold && use_lp) {
         // tile hl+1 is loaded while head hl is reduced
         for (int hl = 0; hl + 1 < nh; ++hl) {
-            issue_tile(hl + 1, vb, lb);
-            body(hl);
+            issue_tile_lp(hl + 1, qb);
+            outputs_lp(hl, qa);
+#pragma unroll
+            for (int k = 0; k < RQ; ++k) qa[k] = qb[k];
+        }
+        outputs_lp(nh - 1, qa);
+    } else if (!fold) {
+        // tile hl+1 is loaded while head hl is reduced
+        for (int hl = 0; hl + 1 < nh; ++hl) {
+            issue_tile(hl + 1, vb);
+            outputs(hl, va);
             rotate();
         }
-        body(nh - 1);
+        outputs(nh - 1, va);
     } else if (!idle) {
         auto stage_u = [&](int hl) {     // fold factors u_s[p] = w_s x_s[p] of head hl
             __syncthreads();
@@ -473,7 +526,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
         for (int hl = 0; hl + 1 < nh; ++hl) {
             stage_u(hl);
             issue_foldx(hl + 1);
-            issue_tile(hl + 1, vb, lb);
+            issue_tile(hl + 1, vb);
             body(hl);
             rotate();
         }
