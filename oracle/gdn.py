@@ -155,3 +155,91 @@ class GDNReplay:
                                                 np.stack([r[2] for r in rec]),
                                                 np.stack([r[3] for r in rec]))
             self.records[b] = []
+
+
+# --------------------------------------------------------------------------------------
+# speculative verification on a circular buffer
+# --------------------------------------------------------------------------------------
+
+class GDNSpec:
+    """Speculative verify for the gated delta rule, with the cursor rules of ``Mamba2Spec``.
+
+    The pages give Gated DeltaNet the same speculative treatment as Mamba2 ("ReplaySSM (a
+    vLLM research fork)" -- "Core implementation files": a GDN speculative decode kernel on
+    a circular buffer with its own commit and reset calls).  Per sequence the buffer holds
+    ``committed`` records from slot ``head``.  verify: if ``committed + n_pos > L`` the
+    committed records are folded into the checkpoint first (``flushed = 1``); the
+    positions' records go to slots ``(head + committed + j) % L``; position ``j``'s output
+    carries its q back through positions ``j..0`` and the committed records.  commit: if
+    the round flushed, ``head += committed`` and ``committed = 0``; then ``committed +=
+    n_keep``.  Records are kept per value head here (the q/k head's k expanded).
+    """
+
+    def __init__(self, ckpt, buffer_len, num_k_heads, scale=None):
+        self.ckpt = np.array(ckpt, dtype=np.float64, copy=True)
+        self.Bt, self.HV, self.dv, self.dk = self.ckpt.shape
+        self.HK = int(num_k_heads)
+        self.L = int(buffer_len)
+        self.scale = default_scale(self.dk) if scale is None else scale
+        self.ring_k = np.zeros((self.Bt, self.L, self.HV, self.dk))
+        self.ring_v = np.zeros((self.Bt, self.L, self.HV, self.dv))
+        self.ring_alpha = np.zeros((self.Bt, self.L, self.HV))
+        self.ring_beta = np.zeros((self.Bt, self.L, self.HV))
+        self.head = np.zeros(self.Bt, dtype=np.int64)
+        self.committed = np.zeros(self.Bt, dtype=np.int64)
+        self.flushed = np.zeros(self.Bt, dtype=np.int64)
+
+    def verify(self, q, k, v, alpha, beta):
+        """Inputs ``q, k [Bt,n_pos,HK,dk]``, ``v [Bt,n_pos,HV,dv]``, ``alpha, beta [Bt,n_pos,HV]``.
+        Returns ``(out [Bt,n_pos,HV,dv], flushed [Bt])``."""
+        n_pos = np.asarray(q).shape[1]
+        if not 1 <= n_pos <= self.L:
+            raise ValueError("need 1 <= n_pos <= buffer_len")
+        qh = heads_of_kgroups(q, self.HV)
+        kh = heads_of_kgroups(k, self.HV)
+        v = np.asarray(v, dtype=np.float64)
+        alpha = np.asarray(alpha, dtype=np.float64)
+        beta = np.asarray(beta, dtype=np.float64)
+        out = np.empty((self.Bt, n_pos, self.HV, self.dv))
+        for b in range(self.Bt):
+            head, com = int(self.head[b]), int(self.committed[b])
+            slots = [(head + i) % self.L for i in range(com)]
+            ks = [self.ring_k[b, s] for s in slots]
+            vs = [self.ring_v[b, s] for s in slots]
+            als = [self.ring_alpha[b, s] for s in slots]
+            bes = [self.ring_beta[b, s] for s in slots]
+            if com + n_pos > self.L:
+                if com:
+                    self.ckpt[b] = fold_matrix_form(self.ckpt[b], np.stack(ks), np.stack(vs),
+                                                    np.stack(als), np.stack(bes))
+                ks, vs, als, bes = [], [], [], []
+                self.flushed[b] = 1
+            else:
+                self.flushed[b] = 0
+            for j in range(n_pos):
+                slot = (head + com + j) % self.L
+                self.ring_k[b, slot] = kh[b, j]
+                self.ring_v[b, slot] = v[b, j]
+                self.ring_alpha[b, slot] = alpha[b, j]
+                self.ring_beta[b, slot] = beta[b, j]
+                ks.append(kh[b, j])
+                vs.append(v[b, j])
+                als.append(alpha[b, j])
+                bes.append(beta[b, j])
+                u, acc = carry_back(qh[b, j], np.stack(ks), np.stack(vs), np.stack(als), np.stack(bes))
+                out[b, j] = self.scale * (np.einsum("hij,hj->hi", self.ckpt[b], u) + acc)
+        return out, self.flushed.copy()
+
+    def commit(self, n_keep):
+        n_keep = np.asarray(n_keep, dtype=np.int64)
+        for b in range(self.Bt):
+            if self.flushed[b]:
+                self.head[b] = (self.head[b] + self.committed[b]) % self.L
+                self.committed[b] = 0
+            self.committed[b] += n_keep[b]
+            self.flushed[b] = 0
+
+    def reset(self, seqs=None):
+        for b in range(self.Bt) if seqs is None else seqs:
+            self.head[b] = 0
+            self.committed[b] = 0

@@ -131,3 +131,54 @@ def test_synth_gdn_inputs_shapes_and_ranges():
     assert np.all((s["alpha"] > 0) & (s["alpha"] < 1))
     assert np.allclose(np.linalg.norm(s["k"].astype(np.float64), axis=-1), 1.0, atol=1e-2)
     assert np.array_equal(synth.round_bf16(s["q"]), s["q"])
+
+
+def test_gdn_spec_outputs_equal_conventional_on_kept_and_draft_streams():
+    rng = np.random.default_rng(24)
+    Bt, HV, HK, dk, dv, L, T = 2, 4, 2, 6, 5, 7, 3
+    S0 = 0.1 * rng.standard_normal((Bt, HV, dv, dk))
+    spec = og.GDNSpec(S0, L, HK)
+    S_kept = S0.copy()
+    n_flush = 0
+    for r in range(30):
+        steps = [_rand_step(rng, Bt, HV, HK, dk, dv) for _ in range(T)]
+        ins = {key: np.stack([s[key] for s in steps], 1) for key in steps[0]}
+        com_before = spec.committed.copy()
+        ck_before = spec.ckpt.copy()
+        out, flushed = spec.verify(**ins)
+        assert np.array_equal(flushed.astype(bool), com_before + T > L)
+        n_flush += int(flushed.sum())
+        for b in range(Bt):
+            if not flushed[b]:
+                assert np.array_equal(spec.ckpt[b], ck_before[b])   # output-only verify
+        S = S_kept.copy()
+        states = []
+        for j in range(T):
+            S, o = og.conventional_step(S, **steps[j])
+            states.append(S)
+            assert np.max(np.abs(out[:, j] - o)) <= 1e-12
+        n_keep = rng.integers(1, T + 1, size=Bt)
+        spec.commit(n_keep)
+        S_kept = np.stack([states[n_keep[b] - 1][b] for b in range(Bt)])
+        assert np.all((spec.committed >= 1) & (spec.committed <= L))
+    assert n_flush > 0
+    # folding what remains reproduces the kept conventional state
+    for b in range(Bt):
+        com, head = int(spec.committed[b]), int(spec.head[b])
+        slots = [(head + i) % L for i in range(com)]
+        ck = og.fold_matrix_form(spec.ckpt[b], spec.ring_k[b, slots], spec.ring_v[b, slots],
+                                 spec.ring_alpha[b, slots], spec.ring_beta[b, slots])
+        assert np.max(np.abs(ck - S_kept[b])) <= 1e-12
+
+
+def test_gdn_spec_hand_example_single_position(golden_dir):
+    # one position per round is the autoregressive hand example (buffer 2 -> flush every 2)
+    g = json.load(open(os.path.join(golden_dir, "gdn_hand.json")))
+    spec = og.GDNSpec(np.array(g["S0"])[None, None], g["buffer_len"], 1, scale=g["scale"])
+    for st in g["steps"]:
+        ins = dict(q=np.array(st["q"])[None, None, None], k=np.array(st["k"])[None, None, None],
+                   v=np.array(st["v"])[None, None, None], alpha=np.array([[[st["alpha"]]]]),
+                   beta=np.array([[[st["beta"]]]]))
+        out, _ = spec.verify(**ins)
+        assert np.allclose(out[0, 0, 0], np.array(st["o"]), atol=1e-12)
+        spec.commit([1])
