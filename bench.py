@@ -17,8 +17,8 @@ sample of the same workload and checks the GPU outputs for that sample.
 Measured beside the headline, each with its own timed region: the in-library
 conventional read-update-write kernel on the same inputs, the bf16 read copy, the
 B=256/H=64 layer, speculative verification (4 positions, commit) against the
-per-position snapshot baseline, and the Gated DeltaNet layer (replay and
-conventional).  ``ceiling`` reports plain device read and copy bandwidth.
+per-position snapshot baseline, and the Gated DeltaNet layer (replay decode and
+conventional; speculative verification against its snapshot baseline).  ``ceiling`` reports plain device read and copy bandwidth.
 
 Auxiliary modes used to make the committed rocprofv3 summaries:
     --calibrate-copy        also run a plain 1 GiB device copy (counter calibration)
@@ -108,6 +108,21 @@ def gdn_replay_bytes(B, HV, HK, dk, dv, L, io, c):
 
 def gdn_conventional_bytes(B, HV, HK, dk, dv, io):
     return B * HV * (2 * dv * dk * 4 + dv * io + 8 + dv * 4) + B * HK * 2 * dk * io
+
+
+def gdn_spec_round_bytes(HV, HK, dk, dv, L, io, T, committed):
+    """One Gated DeltaNet verify round; ``committed`` holds each sequence's committed count."""
+    tot = 0
+    for cm in committed:
+        state = dv * dk * 4 * (2 if cm + T > L else 1)
+        per_hv = state + T * (dv * io + 8 + dv * 4) + cm * (dv * io + 8) + T * (dv * io + 8)
+        per_hk = T * 2 * dk * io + cm * dk * io + T * dk * io
+        tot += HV * per_hv + HK * per_hk
+    return tot
+
+
+def gdn_spec_baseline_bytes(B, HV, HK, dk, dv, io, T):
+    return B * HV * (dv * dk * 4 * (1 + T) + T * (dv * io + 8 + dv * 4)) + B * HK * T * 2 * dk * io
 
 
 # ------------------------------------------------------------------------------------
@@ -372,6 +387,89 @@ def time_gdn(torch, rs, synth, steps, warmup, conventional=False):
                 frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS)
 
 
+def time_gdn_spec(torch, rs, synth, rounds, warmup, baseline=False):
+    import ctypes
+    import numpy as np
+    w = synth.WORKLOADS["gdn_spec_hv32"]
+    B, HV, HK, dk, dv, L, T = (w[k] for k in ("batch", "num_v_heads", "num_k_heads", "dk", "dv", "buffer_len",
+                                               "n_pos"))
+    io = 2
+    gen = synth.gdn_inputs("gdn_spec_hv32")
+    st = gen.static
+    dev = "cuda"
+    t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    pool_n = 32
+    pool, keeps = [], []
+    for _ in range(pool_n):
+        s = gen.step(n_pos=T)
+        pool.append({"q": t(s["q"], torch.bfloat16), "k": t(s["k"], torch.bfloat16), "v": t(s["v"], torch.bfloat16),
+                     "alpha": t(s["alpha"], torch.float32), "beta": t(s["beta"], torch.float32)})
+        keeps.append(gen.accepted(T - 1) + 1)
+    keep_dev = [torch.from_numpy(k.astype(np.int32)).to(dev) for k in keeps]
+    keys = ("q", "k", "v", "alpha", "beta")
+    out = torch.empty(B, T, HV, dv, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    Lb = rs.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    d = desc.c()
+    if baseline:
+        snaps = torch.empty(B, T, HV, dv, dk, dtype=torch.float32, device=dev)
+        snaps[:, 0] = t(st.ckpt, torch.float32)
+        slots = [torch.from_numpy((keeps[(r - 1) % pool_n] - 1).astype(np.int32)).to(dev) for r in range(pool_n)]
+        slots[0] = torch.zeros(B, dtype=torch.int32, device=dev)
+
+        def launch(r):
+            p = pool[r % pool_n]
+            _check(Lb.replayssm_gdn_spec_baseline(ctypes.byref(d), snaps.data_ptr(), slots[r % pool_n].data_ptr(), T,
+                                                  *(p[k].data_ptr() for k in keys), out.data_ptr(), stream),
+                   "gdn_spec_baseline")
+        keep_state = [snaps]
+    else:
+        state = rs.GdnState.allocate(desc, ckpt=t(st.ckpt, torch.float32))
+        s_c = state.c()
+        head = torch.zeros(B, dtype=torch.int32, device=dev)
+        com = torch.zeros(B, dtype=torch.int32, device=dev)
+        flushed = torch.zeros(B, dtype=torch.int32, device=dev)
+
+        def launch(r):
+            p = pool[r % pool_n]
+            _check(Lb.replayssm_gdn_spec_verify(ctypes.byref(d), ctypes.byref(s_c), head.data_ptr(), com.data_ptr(), T,
+                                                *(p[k].data_ptr() for k in keys), out.data_ptr(), flushed.data_ptr(),
+                                                err.data_ptr(), stream), "gdn_spec_verify")
+            _check(Lb.replayssm_commit(B, L, T, head.data_ptr(), com.data_ptr(), flushed.data_ptr(),
+                                       keep_dev[r % pool_n].data_ptr(), err.data_ptr(), stream), "commit")
+        keep_state = [state, s_c]
+    for r in range(warmup):
+        launch(r)
+    secs, wall = Timer(torch).run(launch, warmup, rounds)
+    accepted = sum(int(keeps[r % pool_n].sum()) for r in range(warmup, warmup + rounds))
+    hd = np.zeros(B, np.int64)
+    cm = np.zeros(B, np.int64)
+    nbytes = 0
+    n_flush = 0
+    for r in range(warmup + rounds):
+        fl = cm + T > L
+        if r >= warmup:
+            nbytes += gdn_spec_baseline_bytes(B, HV, HK, dk, dv, io, T) if baseline else \
+                gdn_spec_round_bytes(HV, HK, dk, dv, L, io, T, cm)
+            n_flush += int(fl.sum())
+        hd = np.where(fl, (hd + cm) % L, hd)
+        cm = np.where(fl, 0, cm) + keeps[r % pool_n]
+    if not baseline:
+        if not (np.array_equal(head.cpu().numpy(), hd.astype(np.int32)) and
+                np.array_equal(com.cpu().numpy(), cm.astype(np.int32))):
+            raise RuntimeError("speculative cursors disagree with the host model")
+        if err.item() != 0:
+            raise RuntimeError("device error flag set")
+    del keep_state
+    return dict(accepted_tokens_per_s=accepted / secs, positions_per_s=B * T * rounds / secs,
+                ms_per_round=secs * 1e3 / rounds, rounds=rounds, bytes_per_round_MiB=nbytes / rounds / MiB,
+                hbm_gbps=nbytes / secs / 1e9, frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS,
+                accepted_per_round=accepted / rounds / B,
+                flush_fraction=(n_flush / (B * rounds)) if not baseline else None)
+
+
 def ceiling(torch, calibrate_copy=False):
     n = COPY_BYTES // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -547,7 +645,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1024, help="timed decode steps of the headline")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--only", default="all",
-                    help="all, headline, or a comma list of: conventional,bf16,h64,spec,gdn")
+                    help="all, headline, or a comma list of: conventional,bf16,h64,spec,gdn,gdn_spec")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--cpu-steps", type=int, default=32)
@@ -598,7 +696,7 @@ def main(argv=None):
 
     variants = {}
     conv = None
-    groups = {"conventional", "bf16", "h64", "spec", "gdn"} if args.only == "all" else \
+    groups = {"conventional", "bf16", "h64", "spec", "gdn", "gdn_spec"} if args.only == "all" else \
         set() if args.only == "headline" else set(args.only.split(","))
     if "conventional" in groups:
         conv, _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup, conventional=True)
@@ -623,6 +721,11 @@ def main(argv=None):
         variants["gdn_hv32_replay"] = time_gdn(torch, rs, synth, 512, 32)
         torch.cuda.empty_cache()
         variants["gdn_hv32_conventional"] = time_gdn(torch, rs, synth, 512, 32, conventional=True)
+        torch.cuda.empty_cache()
+    if "gdn_spec" in groups:
+        variants["gdn_spec_hv32_verify"] = time_gdn_spec(torch, rs, synth, 256, 32)
+        torch.cuda.empty_cache()
+        variants["gdn_spec_hv32_snapshot_baseline"] = time_gdn_spec(torch, rs, synth, 256, 32, baseline=True)
         torch.cuda.empty_cache()
     if variants:
         print("[bench] variants done", file=sys.stderr, flush=True)

@@ -89,8 +89,33 @@ replayssm_status check_gdn_desc(const replayssm_gdn_desc* d, bool need_L) {
     return REPLAYSSM_OK;
 }
 
-rssm::GdnArgs gdn_args(const replayssm_gdn_desc* d) {
+replayssm_status check_gdn_state(const replayssm_gdn_state* s) {
+    REQ(s && s->ckpt && s->rec_k && s->rec_v && s->rec_alpha && s->rec_beta);
+    REQ(aligned(s->ckpt, 16) && aligned(s->rec_k, 16) && aligned(s->rec_v, 16) &&
+        aligned(s->rec_alpha, 4) && aligned(s->rec_beta, 4));
+    return REPLAYSSM_OK;
+}
+
+replayssm_status check_gdn_inputs(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* out) {
+    REQ(q && k && v && alpha && beta && out);
+    REQ(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(alpha, 4) && aligned(beta, 4) &&
+        aligned(out, 4));
+    return REPLAYSSM_OK;
+}
+
+// whether the replay kernel's LDS staging of one workgroup fits
+bool gdn_fits(const replayssm_gdn_desc* d, int mode, int n_pos) {
+    return rssm::gdn_smem_bytes(d->dk, d->dv, d->buffer_len, d->num_v_heads / d->num_k_heads, mode, n_pos,
+                                d->io_dtype == REPLAYSSM_BF16 ? 2 : 4) <= rssm::mamba2_max_smem_bytes();
+}
+
+rssm::GdnArgs gdn_args(const replayssm_gdn_desc* d, const replayssm_gdn_state* s) {
     rssm::GdnArgs a{};
+    if (s) {
+        a.ckpt = s->ckpt; a.rec_k = s->rec_k; a.rec_v = s->rec_v;
+        a.rec_alpha = s->rec_alpha; a.rec_beta = s->rec_beta;
+    }
     a.batch = d->batch;
     a.hv = d->num_v_heads;
     a.hk = d->num_k_heads;
@@ -258,20 +283,12 @@ replayssm_status replayssm_gdn_decode(const replayssm_gdn_desc* desc, const repl
                                       hipStream_t stream) {
     replayssm_status st = check_gdn_desc(desc, true);
     if (st != REPLAYSSM_OK) return st;
-    REQ(state && state->ckpt && state->rec_k && state->rec_v && state->rec_alpha && state->rec_beta);
-    REQ(aligned(state->ckpt, 16) && aligned(state->rec_k, 16) && aligned(state->rec_v, 16) &&
-        aligned(state->rec_alpha, 4) && aligned(state->rec_beta, 4));
-    REQ(q && k && v && alpha && beta && out);
-    REQ(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(alpha, 4) && aligned(beta, 4) &&
-        aligned(out, 4));
+    if ((st = check_gdn_state(state)) != REPLAYSSM_OK) return st;
+    if ((st = check_gdn_inputs(q, k, v, alpha, beta, out)) != REPLAYSSM_OK) return st;
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
-    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len, desc->num_v_heads / desc->num_k_heads,
-                             desc->io_dtype == REPLAYSSM_BF16 ? 2 : 4) > rssm::mamba2_max_smem_bytes())
-        return REPLAYSSM_ERR_UNSUPPORTED;
-    rssm::GdnArgs a = gdn_args(desc);
-    a.ckpt = state->ckpt; a.rec_k = state->rec_k; a.rec_v = state->rec_v;
-    a.rec_alpha = state->rec_alpha; a.rec_beta = state->rec_beta;
+    if (!gdn_fits(desc, 0, 1)) return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::GdnArgs a = gdn_args(desc, state);
     a.cursor_in = cursor_in; a.cursor_out = cursor_out;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out; a.err_flags = err_flags;
     return hip_status(rssm::launch_gdn_replay(a, desc->io_dtype, 0, stream));
@@ -282,19 +299,37 @@ replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const repla
                                      hipStream_t stream) {
     replayssm_status st = check_gdn_desc(desc, true);
     if (st != REPLAYSSM_OK) return st;
-    REQ(state && state->ckpt && state->rec_k && state->rec_v && state->rec_alpha && state->rec_beta);
-    REQ(aligned(state->ckpt, 16) && aligned(state->rec_k, 16) && aligned(state->rec_v, 16) &&
-        aligned(state->rec_alpha, 4) && aligned(state->rec_beta, 4));
+    if ((st = check_gdn_state(state)) != REPLAYSSM_OK) return st;
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
-    if (rssm::gdn_smem_bytes(desc->dk, desc->dv, desc->buffer_len, desc->num_v_heads / desc->num_k_heads,
-                             desc->io_dtype == REPLAYSSM_BF16 ? 2 : 4) > rssm::mamba2_max_smem_bytes())
-        return REPLAYSSM_ERR_UNSUPPORTED;
-    rssm::GdnArgs a = gdn_args(desc);
-    a.ckpt = state->ckpt; a.rec_k = state->rec_k; a.rec_v = state->rec_v;
-    a.rec_alpha = state->rec_alpha; a.rec_beta = state->rec_beta;
+    if (!gdn_fits(desc, 1, 0)) return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::GdnArgs a = gdn_args(desc, state);
     a.cursor_in = cursor_in; a.cursor_out = cursor_out; a.err_flags = err_flags;
     return hip_status(rssm::launch_gdn_replay(a, desc->io_dtype, 1, stream));
+}
+
+replayssm_status replayssm_gdn_spec_verify(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
+                                           const int32_t* head, const int32_t* committed, int32_t n_pos,
+                                           const void* q, const void* k, const void* v,
+                                           const float* alpha, const float* beta, float* out,
+                                           int32_t* flushed, int32_t* err_flags, hipStream_t stream) {
+    replayssm_status st = check_gdn_desc(desc, true);
+    if (st != REPLAYSSM_OK) return st;
+    if ((st = check_gdn_state(state)) != REPLAYSSM_OK) return st;
+    if ((st = check_gdn_inputs(q, k, v, alpha, beta, out)) != REPLAYSSM_OK) return st;
+    REQ(n_pos >= 1 && n_pos <= desc->buffer_len);
+    REQ((int64_t)desc->batch * n_pos * desc->num_v_heads <= INT_MAX / 2);
+    REQ(head && committed && flushed && head != committed);
+    REQ((const int32_t*)flushed != head && (const int32_t*)flushed != committed);
+    REQ(aligned(head, 4) && aligned(committed, 4) && aligned(flushed, 4) && aligned(err_flags, 4));
+    if (!gdn_fits(desc, 2, n_pos)) return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::GdnArgs a = gdn_args(desc, state);
+    a.cursor_in = head;
+    a.committed = committed;
+    a.flushed = flushed;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out; a.err_flags = err_flags;
+    a.n_pos = n_pos;
+    return hip_status(rssm::launch_gdn_replay(a, desc->io_dtype, 2, stream));
 }
 
 replayssm_status replayssm_gdn_conventional_decode(const replayssm_gdn_desc* desc, float* state,
@@ -304,13 +339,29 @@ replayssm_status replayssm_gdn_conventional_decode(const replayssm_gdn_desc* des
     replayssm_status st = check_gdn_desc(desc, false);
     if (st != REPLAYSSM_OK) return st;
     REQ(state && aligned(state, 16));
-    REQ(q && k && v && alpha && beta && out);
-    REQ(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(alpha, 4) && aligned(beta, 4) &&
-        aligned(out, 4));
-    rssm::GdnArgs a = gdn_args(desc);
+    if ((st = check_gdn_inputs(q, k, v, alpha, beta, out)) != REPLAYSSM_OK) return st;
+    rssm::GdnArgs a = gdn_args(desc, nullptr);
     a.ckpt = state;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out;
-    return hip_status(rssm::launch_gdn_conventional(a, desc->io_dtype, stream));
+    return hip_status(rssm::launch_gdn_conventional(a, desc->io_dtype, false, stream));
+}
+
+replayssm_status replayssm_gdn_spec_baseline(const replayssm_gdn_desc* desc, float* snapshots,
+                                             const int32_t* slot_in, int32_t n_pos, const void* q,
+                                             const void* k, const void* v, const float* alpha,
+                                             const float* beta, float* out, hipStream_t stream) {
+    replayssm_status st = check_gdn_desc(desc, false);
+    if (st != REPLAYSSM_OK) return st;
+    REQ(snapshots && aligned(snapshots, 16) && slot_in && aligned(slot_in, 4));
+    if ((st = check_gdn_inputs(q, k, v, alpha, beta, out)) != REPLAYSSM_OK) return st;
+    REQ(n_pos >= 1 && n_pos <= REPLAYSSM_MAX_BUFFER_LEN);
+    REQ((int64_t)desc->batch * n_pos * desc->num_v_heads <= INT_MAX / 2);
+    rssm::GdnArgs a = gdn_args(desc, nullptr);
+    a.ckpt = snapshots;
+    a.cursor_in = slot_in;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out;
+    a.n_pos = n_pos;
+    return hip_status(rssm::launch_gdn_conventional(a, desc->io_dtype, true, stream));
 }
 
 }  // extern "C"

@@ -27,7 +27,8 @@ namespace rssm {
 constexpr int kGdnThreads = 256;
 constexpr int kGdnDecode = 0;
 constexpr int kGdnFold = 1;
-constexpr int kGdnMaxVHeads = 4;   // value heads per workgroup (one carry-back wave each)
+constexpr int kGdnSpec = 2;
+constexpr int kGdnMaxVHeads = 4;   // value heads per workgroup
 
 template <int DK>
 struct GdnShape {
@@ -37,26 +38,39 @@ struct GdnShape {
     static constexpr int DVT = RPP * R;
 };
 
-// LDS layout (4-byte words) of the replay kernel.
+// LDS layout (4-byte words) of the replay kernel.  NR bounds the window rows (stored
+// records plus this call's positions), T1 the positions.
 struct GdnSmem {
-    int oK, oV, oAl, oBe, oQ, oU, oCoef, oAcc, total;
-    __host__ __device__ GdnSmem(int DK, int DV, int L, int NV, int io_bytes) {
-        oK = 0;                                    // [L][DK]      k rows of the window
-        oV = oK + L * DK;                          // [NV][L][DV]  v rows (io dtype)
-        oAl = oV + (NV * L * DV * io_bytes + 3) / 4;   // [NV][L]
-        oBe = oAl + NV * L;                        // [NV][L]
-        oQ = oBe + NV * L;                         // [DK]
-        oU = oQ + DK;                              // [NV][DK]     carried-back q
-        oCoef = oU + NV * DK;                      // [NV][L]      beta_s kappa_s
-        oAcc = oCoef + NV * L;                     // [NV][DV]     sum_s beta_s kappa_s v_s
-        total = oAcc + NV * DV;
+    int NR, T1, oK, oV, oAl, oBe, oQ, oU, oCoef, oAcc, total;
+    __host__ __device__ GdnSmem(int DK, int DV, int L, int T, int mode, int NV, int io_bytes) {
+        NR = (mode == kGdnSpec) ? L + T : L;
+        T1 = T > 1 ? T : 1;
+        oK = 0;                                    // [NR][DK]      k rows of the window
+        oV = oK + NR * DK;                         // [NV][NR][DV]  v rows (io dtype)
+        oAl = oV + (NV * NR * DV * io_bytes + 3) / 4;   // [NV][NR]
+        oBe = oAl + NV * NR;                       // [NV][NR]
+        oQ = oBe + NV * NR;                        // [T1][DK]
+        oU = oQ + T1 * DK;                         // [NV][T1][DK]  carried-back q
+        oCoef = oU + NV * T1 * DK;                 // [NV][T1][NR]  beta_s kappa_s
+        oAcc = oCoef + NV * T1 * NR;               // [NV][T1][DV]  sum_s beta_s kappa_s v_s
+        total = oAcc + NV * T1 * DV;
     }
 };
 
 // One workgroup per (sequence, q/k head, chunk of its value heads).  The k records and
-// q are shared by the value heads of one q/k head and staged once; each value head's
-// carry-back chain runs on its own wave; the workgroup then streams the value heads'
+// q are shared by the value heads of one q/k head and staged once.  The carry-back
+// chains run on the workgroup's waves (several chains of a wave in lockstep) while the
+// first checkpoint tile is in flight; the workgroup then streams the value heads'
 // [64, dk] checkpoint tiles, loading the next tile while it reduces the current one.
+//
+// Modes:
+//   kGdnDecode  one autoregressive step; the record is stored at the cursor, and the
+//               step that fills the buffer folds it into the checkpoint
+//   kGdnFold    fold the stored records only (no outputs)
+//   kGdnSpec    speculative verification of n_pos positions on the circular buffer:
+//               window row s < committed is ring slot (head + s) % L, row committed + j
+//               is position j; if committed + n_pos > L the committed rows are folded
+//               first and every position's chain starts after them.
 template <int DK, int DV, typename IO, int MODE>
 __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     using io = Io<IO>;
@@ -66,6 +80,10 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     constexpr int NTILE = DV / DVT;
     constexpr int UPL = DK / kWave;  // u elements per lane in a carry-back wave
     constexpr int DK4 = DK / 4, DV4 = DV / 4;
+    constexpr int NWAVE = kGdnThreads / kWave;
+    // chains a wave runs in lockstep, and positions reduced together per tile
+    constexpr int TC = (MODE == kGdnSpec) ? 2 : 1;
+    constexpr int TB = (MODE == kGdnSpec) ? (LPR / R >= 2 ? 2 : 1) : 1;
     extern __shared__ float smem[];
 
     const int tid = threadIdx.x;
@@ -82,21 +100,37 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     const int hv0 = hk * rv + chunk * a.vheads_per_chunk;
     const int nv = min(a.vheads_per_chunk, rv - chunk * a.vheads_per_chunk);
     const bool lead = (hk == 0 && chunk == 0);
+    const int T = (MODE == kGdnSpec) ? a.n_pos : (MODE == kGdnDecode ? 1 : 0);
 
-    const int c = a.cursor_in[b];
-    if (c < 0 || c >= L) {
+    // ---- cursors -------------------------------------------------------------------
+    int c = 0, hd = 0, cm = 0;
+    bool bad;
+    if constexpr (MODE == kGdnSpec) {
+        hd = a.cursor_in[b];
+        cm = a.committed[b];
+        bad = hd < 0 || hd >= L || cm < 0 || cm > L;
+    } else {
+        c = a.cursor_in[b];
+        bad = c < 0 || c >= L;
+    }
+    if (bad) {
         if (tid == 0) {
             if (a.err_flags) atomicOr(a.err_flags, 1);
-            if (lead) a.cursor_out[b] = c;
+            if (lead && MODE != kGdnSpec) a.cursor_out[b] = c;
         }
         return;
     }
-    const int nrec = (MODE == kGdnDecode) ? c + 1 : c;
-    const bool fold = (MODE == kGdnFold) || (c + 1 == L);
+    const int nstored = (MODE == kGdnSpec) ? cm : c;   // window rows taken from the ring
+    const int nrec = nstored + T;                       // window rows
+    const bool fold = (MODE == kGdnFold) || (MODE == kGdnDecode && c + 1 == L) ||
+                      (MODE == kGdnSpec && cm + T > L);
+    const int nf = (MODE == kGdnSpec) ? cm : nrec;      // the fold covers rows [0, nf)
+    const int st = fold ? nf : 0;                       // first row of every chain
     const bool idle = (MODE == kGdnFold) && c == 0;
     const size_t bHV = (size_t)b * HV;
 
-    const GdnSmem lay(DK, DV, L, a.vheads_per_chunk, (int)sizeof(IO));
+    const GdnSmem lay(DK, DV, L, T, MODE, a.vheads_per_chunk, (int)sizeof(IO));
+    const int NR = lay.NR, T1 = lay.T1;
     float* sK = smem + lay.oK;
     IO* sV = reinterpret_cast<IO*>(smem + lay.oV);
     float* sAl = smem + lay.oAl;
@@ -122,14 +156,29 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     if (!idle) issue_tile(0, va);
 
     // ---- stage the window -------------------------------------------------------------
+    auto slot_of = [&](int s) {
+        if constexpr (MODE == kGdnSpec) {
+            const int t = hd + s;
+            return t < L ? t : t - L;
+        } else {
+            return s;
+        }
+    };
+    auto pos_qk = [&](int j) -> size_t {      // q/k offset of position j
+        return (MODE == kGdnSpec) ? ((size_t)(b * T + j) * HK + hk) * DK : ((size_t)b * HK + hk) * DK;
+    };
+    auto pos_h = [&](int vl, int j) -> size_t {   // alpha/beta index of value head vl, position j
+        return (MODE == kGdnSpec) ? (size_t)(b * T + j) * HV + hv0 + vl : bHV + hv0 + vl;
+    };
     const IO* recK = reinterpret_cast<const IO*>(a.rec_k) + ((size_t)b * HK + hk) * L * DK;
-    const IO* kin = reinterpret_cast<const IO*>(a.k) + ((size_t)b * HK + hk) * DK;
-    const IO* qin = reinterpret_cast<const IO*>(a.q) + ((size_t)b * HK + hk) * DK;
+    const IO* kin = reinterpret_cast<const IO*>(a.k);
+    const IO* qin = reinterpret_cast<const IO*>(a.q);
     const IO* vin = reinterpret_cast<const IO*>(a.v);
     const IO* recV = reinterpret_cast<const IO*>(a.rec_v);
     for (int task = tid; task < nrec * DK4; task += kGdnThreads) {
         const int s = task / DK4, j4 = task % DK4;
-        const Raw4 r = (s < c) ? io::ldraw4(recK, (size_t)s * DK + 4 * j4) : io::ldraw4(kin, 4 * j4);
+        const Raw4 r = (s < nstored) ? io::ldraw4(recK, (size_t)slot_of(s) * DK + 4 * j4)
+                                     : io::ldraw4(kin, pos_qk(s - nstored) + 4 * j4);
         *reinterpret_cast<float4*>(sK + s * DK + 4 * j4) = io::cvt4(r);
     }
     for (int task = tid; task < nv * nrec * DV4; task += kGdnThreads) {
@@ -137,18 +186,21 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         const int vs = task / DV4;
         const int vl = vs / nrec, s = vs - vl * nrec;
         const size_t hv = bHV + hv0 + vl;
-        const Raw4 r = (s < c) ? io::ldraw4(recV, (hv * L + s) * DV + 4 * i4) : io::ldraw4(vin, hv * DV + 4 * i4);
-        *reinterpret_cast<Raw4*>(sV + (vl * L + s) * DV + 4 * i4) = r;
+        const Raw4 r = (s < nstored) ? io::ldraw4(recV, (hv * L + slot_of(s)) * DV + 4 * i4)
+                                     : io::ldraw4(vin, pos_h(vl, s - nstored) * DV + 4 * i4);
+        *reinterpret_cast<Raw4*>(sV + (vl * NR + s) * DV + 4 * i4) = r;
     }
     for (int task = tid; task < nv * nrec; task += kGdnThreads) {
         const int vl = task / nrec, s = task - vl * nrec;
         const size_t hv = bHV + hv0 + vl;
-        sAl[vl * L + s] = (s < c) ? a.rec_alpha[hv * L + s] : a.alpha[hv];
-        sBe[vl * L + s] = (s < c) ? a.rec_beta[hv * L + s] : a.beta[hv];
+        const bool rec = s < nstored;
+        sAl[vl * NR + s] = rec ? a.rec_alpha[hv * L + slot_of(s)] : a.alpha[pos_h(vl, s - nstored)];
+        sBe[vl * NR + s] = rec ? a.rec_beta[hv * L + slot_of(s)] : a.beta[pos_h(vl, s - nstored)];
     }
-    if (MODE == kGdnDecode)
-        for (int j4 = tid; j4 < DK4; j4 += kGdnThreads)
-            *reinterpret_cast<float4*>(sQ + 4 * j4) = io::cvt4(io::ldraw4(qin, 4 * j4));
+    for (int task = tid; task < T * DK4; task += kGdnThreads) {
+        const int j = task / DK4, j4 = task % DK4;
+        *reinterpret_cast<float4*>(sQ + j * DK + 4 * j4) = io::cvt4(io::ldraw4(qin, pos_qk(j) + 4 * j4));
+    }
     __syncthreads();
 
     const int q = tid % LPR;
@@ -157,85 +209,122 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     const bool writer = (q % (LPR / R)) == 0;
     const float scale = a.scale;
 
+    // ---- carry each position's q back through its window --------------------------------
+    // Position j's chain covers rows nstored + j down to st.  A wave runs TC chains of
+    // one value head in lockstep over the rows (they share k_s, alpha_s and beta_s).
+    if (T > 0) {
+        const int ngrp = (T + TC - 1) / TC;
+        for (int task = wave; task < nv * ngrp; task += NWAVE) {
+            const int vl = task / ngrp, j0 = (task - vl * ngrp) * TC;
+            float u[TC][UPL];
+#pragma unroll
+            for (int cc = 0; cc < TC; ++cc) {
+                const int j = min(j0 + cc, T - 1);
+#pragma unroll
+                for (int m = 0; m < UPL; ++m) u[cc][m] = sQ[j * DK + lane + m * kWave];
+            }
+            const float* al = sAl + vl * NR;
+            const float* be = sBe + vl * NR;
+            const int jtop = min(j0 + TC, T) - 1;
+            for (int s = nstored + jtop; s >= st; --s) {
+                float kap[TC];
+#pragma unroll
+                for (int cc = 0; cc < TC; ++cc) {
+                    kap[cc] = 0.f;
+#pragma unroll
+                    for (int m = 0; m < UPL; ++m) kap[cc] += sK[s * DK + lane + m * kWave] * u[cc][m];
+                }
+#pragma unroll
+                for (int cc = 0; cc < TC; ++cc) kap[cc] = group_allreduce<kWave>(kap[cc], lane);
+                const float as = al[s], bs = be[s];
+#pragma unroll
+                for (int cc = 0; cc < TC; ++cc) {
+                    const int j = min(j0 + cc, T - 1);
+                    const bool on = s <= nstored + j;     // row s lies in position j's window
+                    const float bk = on ? bs * kap[cc] : 0.f;
+                    if (lane == 0 && j0 + cc < T) sCoef[(vl * T1 + j) * NR + s] = bk;
+                    if (on) {
+#pragma unroll
+                        for (int m = 0; m < UPL; ++m) u[cc][m] = as * (u[cc][m] - bk * sK[s * DK + lane + m * kWave]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int cc = 0; cc < TC; ++cc) {
+                if (j0 + cc < T) {
+#pragma unroll
+                    for (int m = 0; m < UPL; ++m) sU[(vl * T1 + j0 + cc) * DK + lane + m * kWave] = u[cc][m];
+                }
+            }
+        }
+        __syncthreads();
+        // ---- record terms sum_s beta_s kappa_s v_s[i] of every (value head, position) --
+        for (int task = tid; task < nv * T * DV; task += kGdnThreads) {
+            const int i = task % DV, vj = task / DV;
+            const int vl = vj / T, j = vj - vl * T;
+            float acc = 0.f;
+            for (int s = st; s <= nstored + j; ++s)
+                acc += sCoef[(vl * T1 + j) * NR + s] * io::ld(sV, (vl * NR + s) * DV + i);
+            sAcc[(vl * T1 + j) * DV + i] = acc;
+        }
+        __syncthreads();
+    }
+
+    // outputs of unit u from its tile: scale * (ckpt u_j + acc_j) for every position j
+    auto out_index = [&](int vl, int j, int i) -> size_t {
+        return (MODE == kGdnSpec) ? ((size_t)(b * T + j) * HV + hv0 + vl) * DV + i
+                                  : (bHV + hv0 + vl) * DV + i;
+    };
+    auto outputs = [&](int u, const float4 (&v)[R]) {
+        const int vl = u / NTILE, tl = u % NTILE;
+        if constexpr (MODE == kGdnDecode) {
+            const float4 Uv = *reinterpret_cast<const float4*>(sU + vl * DK + 4 * col4);
+            float acc[R];
+#pragma unroll
+            for (int k = 0; k < R; ++k) acc[k] = dot4(v[k], Uv);
+            const float r = row_reduce<R, LPR>(acc, lane);
+            if (writer) {
+                const int i = tl * DVT + iw;
+                a.out[out_index(vl, 0, i)] = scale * (r + sAcc[vl * DV + i]);
+            }
+        } else if constexpr (MODE == kGdnSpec) {
+            for (int j0 = 0; j0 < T; j0 += TB) {
+                float acc[R * TB];
+#pragma unroll
+                for (int jj = 0; jj < TB; ++jj) {
+                    const int j = min(j0 + jj, T - 1);
+                    const float4 Uv = *reinterpret_cast<const float4*>(sU + (vl * T1 + j) * DK + 4 * col4);
+#pragma unroll
+                    for (int k = 0; k < R; ++k) acc[jj * R + k] = dot4(v[k], Uv);
+                }
+                const float r = row_reduce<R * TB, LPR>(acc, lane);
+                const int vi = q / (LPR / (R * TB));          // value index this lane holds
+                const int j = j0 + vi / R;
+                const int i = tl * DVT + row0 + (vi % R) * RPP;
+                if ((q % (LPR / (R * TB))) == 0 && j < T)
+                    a.out[out_index(vl, j, i)] = scale * (r + sAcc[(vl * T1 + j) * DV + i]);
+            }
+        }
+    };
     auto rotate = [&]() {
 #pragma unroll
         for (int k = 0; k < R; ++k) va[k] = vb[k];
     };
 
     if (!fold) {
-        // ---- carry q back through each value head's window (one wave per value head) --
-        if (wave < nv) {
-            float u[UPL];
-#pragma unroll
-            for (int m = 0; m < UPL; ++m) u[m] = sQ[lane + m * kWave];
-            const float* al = sAl + wave * L;
-            const float* be = sBe + wave * L;
-            for (int s = nrec - 1; s >= 0; --s) {
-                float kap = 0.f;
-#pragma unroll
-                for (int m = 0; m < UPL; ++m) kap += sK[s * DK + lane + m * kWave] * u[m];
-                kap = group_allreduce<kWave>(kap, lane);
-                const float bk = be[s] * kap;
-                if (lane == 0) sCoef[wave * L + s] = bk;
-                const float as = al[s];
-#pragma unroll
-                for (int m = 0; m < UPL; ++m) u[m] = as * (u[m] - bk * sK[s * DK + lane + m * kWave]);
-            }
-#pragma unroll
-            for (int m = 0; m < UPL; ++m) sU[wave * DK + lane + m * kWave] = u[m];
-        }
-        __syncthreads();
-        // ---- record terms sum_s beta_s kappa_s v_s[i] of every value head --------------
-        for (int task = tid; task < nv * DV; task += kGdnThreads) {
-            const int vl = task / DV, i = task % DV;
-            float acc = 0.f;
-            for (int s = 0; s < nrec; ++s) acc += sCoef[vl * L + s] * io::ld(sV, (vl * L + s) * DV + i);
-            sAcc[vl * DV + i] = acc;
-        }
-        __syncthreads();
-
-        auto body = [&](int u) {
-            const int vl = u / NTILE, tl = u % NTILE;
-            const float4 Uv = *reinterpret_cast<const float4*>(sU + vl * DK + 4 * col4);
-            float acc[R];
-#pragma unroll
-            for (int k = 0; k < R; ++k) acc[k] = dot4(va[k], Uv);
-            const float r = row_reduce<R, LPR>(acc, lane);
-            if (writer) {
-                const int i = tl * DVT + iw;
-                a.out[(bHV + hv0 + vl) * DV + i] = scale * (r + sAcc[vl * DV + i]);
-            }
-        };
         for (int u = 0; u + 1 < nunit; ++u) {
             issue_tile(u + 1, vb);
-            body(u);
+            outputs(u, va);
             rotate();
         }
-        body(nunit - 1);
-
-        // ---- append the step's record -----------------------------------------------
-        for (int task = tid; task < nv * DV4; task += kGdnThreads) {
-            const int vl = task / DV4, i4 = task % DV4;
-            const size_t hv = bHV + hv0 + vl;
-            io::straw4(reinterpret_cast<IO*>(a.rec_v), (hv * L + c) * DV + 4 * i4, io::ldraw4(vin, hv * DV + 4 * i4));
-        }
-        for (int vl = tid; vl < nv; vl += kGdnThreads) {
-            const size_t hv = bHV + hv0 + vl;
-            a.rec_alpha[hv * L + c] = a.alpha[hv];
-            a.rec_beta[hv * L + c] = a.beta[hv];
-        }
-        if (chunk == 0) {
-            for (int j4 = tid; j4 < DK4; j4 += kGdnThreads)
-                io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)b * HK + hk) * L + c) * DK + 4 * j4,
-                           io::ldraw4(kin, 4 * j4));
-        }
+        outputs(nunit - 1, va);
     } else if (!idle) {
-        // ---- flush: apply the window's updates row by row, oldest first ------------------
+        // ---- fold rows [0, nf) into the checkpoint row by row, oldest first -------------
         auto body = [&](int u) {
             const int vl = u / NTILE, tl = u % NTILE;
-            const float* al = sAl + vl * L;
-            const float* be = sBe + vl * L;
-            for (int s = 0; s < nrec; ++s) {
+            const float* al = sAl + vl * NR;
+            const float* be = sBe + vl * NR;
+            for (int s = 0; s < nf; ++s) {
                 const float4 Kv = *reinterpret_cast<const float4*>(sK + s * DK + 4 * col4);
                 float d[R];
 #pragma unroll
@@ -245,7 +334,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
                 for (int k = 0; k < R; ++k) {
                     const float bd = bs * d[k];
-                    const float bv = bs * io::ld(sV, (vl * L + s) * DV + tl * DVT + row0 + k * RPP);
+                    const float bv = bs * io::ld(sV, (vl * NR + s) * DV + tl * DVT + row0 + k * RPP);
                     va[k].x = as * (va[k].x - bd * Kv.x) + bv * Kv.x;
                     va[k].y = as * (va[k].y - bd * Kv.y) + bv * Kv.y;
                     va[k].z = as * (va[k].z - bd * Kv.z) + bv * Kv.z;
@@ -255,14 +344,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
             const size_t t = tile_base(u);
 #pragma unroll
             for (int k = 0; k < R; ++k) st_stream(a.ckpt + t + (size_t)k * RPP * DK, va[k]);
-            if (MODE == kGdnDecode) {
-                const float4 Qv = *reinterpret_cast<const float4*>(sQ + 4 * col4);
-                float acc[R];
-#pragma unroll
-                for (int k = 0; k < R; ++k) acc[k] = dot4(va[k], Qv);
-                const float r = row_reduce<R, LPR>(acc, lane);
-                if (writer) a.out[(bHV + hv0 + vl) * DV + tl * DVT + iw] = scale * r;
-            }
+            outputs(u, va);
         };
         for (int u = 0; u + 1 < nunit; ++u) {
             issue_tile(u + 1, vb);
@@ -272,13 +354,92 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         body(nunit - 1);
     }
 
-    if (tid == 0 && lead) a.cursor_out[b] = fold ? 0 : c + 1;
+    // ---- append this call's records ---------------------------------------------------
+    if constexpr (MODE == kGdnDecode) {
+        if (!fold) {
+            for (int task = tid; task < nv * DV4; task += kGdnThreads) {
+                const int vl = task / DV4, i4 = task % DV4;
+                const size_t hv = bHV + hv0 + vl;
+                io::straw4(reinterpret_cast<IO*>(a.rec_v), (hv * L + c) * DV + 4 * i4,
+                           io::ldraw4(vin, hv * DV + 4 * i4));
+            }
+            for (int vl = tid; vl < nv; vl += kGdnThreads) {
+                const size_t hv = bHV + hv0 + vl;
+                a.rec_alpha[hv * L + c] = a.alpha[hv];
+                a.rec_beta[hv * L + c] = a.beta[hv];
+            }
+            if (chunk == 0) {
+                for (int j4 = tid; j4 < DK4; j4 += kGdnThreads)
+                    io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)b * HK + hk) * L + c) * DK + 4 * j4,
+                               io::ldraw4(kin, pos_qk(0) + 4 * j4));
+            }
+        }
+    } else if constexpr (MODE == kGdnSpec) {
+        // Every ring row this workgroup reads was staged before the first barrier, so
+        // position slots may replace committed ones here (rounds that fold).
+        const int slot0 = hd + cm;
+        for (int task = tid; task < nv * T * DV4; task += kGdnThreads) {
+            const int i4 = task % DV4, vj = task / DV4;
+            const int vl = vj / T, j = vj - vl * T;
+            const size_t hv = bHV + hv0 + vl;
+            io::straw4(reinterpret_cast<IO*>(a.rec_v), (hv * L + (slot0 + j) % L) * DV + 4 * i4,
+                       *reinterpret_cast<const Raw4*>(sV + (vl * NR + nstored + j) * DV + 4 * i4));
+        }
+        for (int task = tid; task < nv * T; task += kGdnThreads) {
+            const int vl = task / T, j = task - vl * T;
+            const size_t hv = bHV + hv0 + vl;
+            a.rec_alpha[hv * L + (slot0 + j) % L] = sAl[vl * NR + nstored + j];
+            a.rec_beta[hv * L + (slot0 + j) % L] = sBe[vl * NR + nstored + j];
+        }
+        // the q/k head's k records: with several workgroups per q/k head the host
+        // appends them in a separate launch
+        if (nchunk == 1) {
+            for (int task = tid; task < T * DK4; task += kGdnThreads) {
+                const int j = task / DK4, j4 = task % DK4;
+                io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)b * HK + hk) * L + (slot0 + j) % L) * DK + 4 * j4,
+                           io::ldraw4(kin, pos_qk(j) + 4 * j4));
+            }
+        }
+    }
+
+    if (tid == 0 && lead) {
+        if (MODE == kGdnSpec) a.flushed[b] = fold ? 1 : 0;
+        else a.cursor_out[b] = fold ? 0 : c + 1;
+    }
+}
+
+// Appends a speculative round's k vectors to each q/k head's ring (slots
+// (head + committed + j) % L) when a q/k head's value heads are split over several
+// workgroups.  Runs after the verify kernel on the same stream, so every workgroup has
+// finished reading the slots it replaces.
+template <int DK, typename IO>
+__global__ void __launch_bounds__(kGdnThreads) gdn_spec_append_k_kernel(GdnArgs a) {
+    using io = Io<IO>;
+    constexpr int DK4 = DK / 4;
+    const int HK = a.hk, L = a.L, T = a.n_pos;
+    const size_t total = (size_t)a.batch * T * HK * DK4;
+    for (size_t i = (size_t)blockIdx.x * kGdnThreads + threadIdx.x; i < total;
+         i += (size_t)gridDim.x * kGdnThreads) {
+        const int j4 = (int)(i % DK4);
+        size_t r = i / DK4;
+        const int hk = (int)(r % HK);
+        r /= HK;
+        const int j = (int)(r % T);
+        const int b = (int)(r / T);
+        const int hd = a.cursor_in[b], cm = a.committed[b];
+        if (hd < 0 || hd >= L || cm < 0 || cm > L) continue;
+        const int slot = (hd + cm + j) % L;
+        io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)b * HK + hk) * L + slot) * DK + 4 * j4,
+                   io::ldraw4(reinterpret_cast<const IO*>(a.k), (((size_t)b * T + j) * HK + hk) * DK + 4 * j4));
+    }
 }
 
 // Conventional step: S <- alpha (S - beta (S k) k^T) + beta v k^T, o = scale S q, with
 // one read and one write of the state.  Uses S_new q = alpha (S q - beta (S k)(k.q)) +
-// beta v (k.q), so both row dots come from the state as loaded.
-template <int DK, typename IO>
+// beta v (k.q), so both row dots come from the state as loaded.  SNAP: per-position
+// snapshot baseline for speculative decoding -- read snapshot slot_in[b] of
+// [B, n_pos, HV, dv, dk], run the n_pos updates and store the state after each.
+template <int DK, typename IO, bool SNAP>
 __global__ void __launch_bounds__(kGdnThreads) gdn_conventional_kernel(GdnArgs a) {
     using io = Io<IO>;
     using S = GdnShape<DK>;
@@ -296,46 +457,62 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_conventional_kernel(GdnArgs a
     const int i0 = tile * DVT;
     const int row0 = tid / LPR;
     const int col4 = tid - row0 * LPR;
-    const size_t tbase = ((size_t)bhv * dv + i0) * DK;
+    const int T = SNAP ? a.n_pos : 1;
+    const size_t SS = (size_t)dv * DK;   // one value head's state
 
+    size_t src;
+    if constexpr (SNAP) {
+        int sl = a.cursor_in[b];
+        sl = sl < 0 ? 0 : (sl >= T ? T - 1 : sl);
+        src = ((size_t)(b * T + sl) * HV + hv) * SS;
+    } else {
+        src = (size_t)bhv * SS;
+    }
+    src += (size_t)i0 * DK + 4 * col4;
     float4 v[R];
 #pragma unroll
     for (int k = 0; k < R; ++k)
-        v[k] = *reinterpret_cast<const float4*>(a.ckpt + tbase + (size_t)(row0 + k * RPP) * DK + 4 * col4);
-    const size_t qk_off = (size_t)(b * HK + hk) * DK;
-    const float4 Kv = io::ld4(reinterpret_cast<const IO*>(a.k), qk_off + 4 * col4);
-    const float4 Qv = io::ld4(reinterpret_cast<const IO*>(a.q), qk_off + 4 * col4);
+        v[k] = *reinterpret_cast<const float4*>(a.ckpt + src + (size_t)(row0 + k * RPP) * DK);
     const IO* vin = reinterpret_cast<const IO*>(a.v);
-    const float al = a.alpha[bhv], be = a.beta[bhv];
-    const float kq = group_allreduce<LPR>(dot4(Kv, Qv), lane);
-
-    float d[R], e[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        d[k] = dot4(v[k], Kv);
-        e[k] = dot4(v[k], Qv);
-    }
-    row_allreduce<R, LPR>(d, lane);
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const float bd = be * d[k];
-        const float bv = be * io::ld(vin, (size_t)bhv * dv + i0 + row0 + k * RPP);
-        v[k].x = al * (v[k].x - bd * Kv.x) + bv * Kv.x;
-        v[k].y = al * (v[k].y - bd * Kv.y) + bv * Kv.y;
-        v[k].z = al * (v[k].z - bd * Kv.z) + bv * Kv.z;
-        v[k].w = al * (v[k].w - bd * Kv.w) + bv * Kv.w;
-        *reinterpret_cast<float4*>(a.ckpt + tbase + (size_t)(row0 + k * RPP) * DK + 4 * col4) = v[k];
-    }
     const int q = tid % LPR;
     const int ridx = q / (LPR / R);
     const int iw = row0 + ridx * RPP;
-    float dsel = d[0];
+
+    for (int j = 0; j < T; ++j) {
+        const size_t ph = SNAP ? (size_t)(b * T + j) * HV + hv : (size_t)bhv;       // value head, position
+        const size_t qk_off = (SNAP ? (size_t)(b * T + j) * HK + hk : (size_t)b * HK + hk) * DK;
+        const float4 Kv = io::ld4(reinterpret_cast<const IO*>(a.k), qk_off + 4 * col4);
+        const float4 Qv = io::ld4(reinterpret_cast<const IO*>(a.q), qk_off + 4 * col4);
+        const float al = a.alpha[ph], be = a.beta[ph];
+        const float kq = group_allreduce<LPR>(dot4(Kv, Qv), lane);
+
+        float d[R], e[R];
 #pragma unroll
-    for (int k = 1; k < R; ++k) dsel = (k == ridx) ? d[k] : dsel;
-    const float r = row_reduce<R, LPR>(e, lane);
-    if ((q % (LPR / R)) == 0) {
-        const float vi = io::ld(vin, (size_t)bhv * dv + i0 + iw);
-        a.out[(size_t)bhv * dv + i0 + iw] = a.scale * (al * (r - be * dsel * kq) + be * vi * kq);
+        for (int k = 0; k < R; ++k) {
+            d[k] = dot4(v[k], Kv);
+            e[k] = dot4(v[k], Qv);
+        }
+        row_allreduce<R, LPR>(d, lane);
+        const size_t dst = (SNAP ? ((size_t)(b * T + j) * HV + hv) * SS : (size_t)bhv * SS) +
+                           (size_t)i0 * DK + 4 * col4;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const float bd = be * d[k];
+            const float bv = be * io::ld(vin, ph * dv + i0 + row0 + k * RPP);
+            v[k].x = al * (v[k].x - bd * Kv.x) + bv * Kv.x;
+            v[k].y = al * (v[k].y - bd * Kv.y) + bv * Kv.y;
+            v[k].z = al * (v[k].z - bd * Kv.z) + bv * Kv.z;
+            v[k].w = al * (v[k].w - bd * Kv.w) + bv * Kv.w;
+            *reinterpret_cast<float4*>(a.ckpt + dst + (size_t)(row0 + k * RPP) * DK) = v[k];
+        }
+        float dsel = d[0];
+#pragma unroll
+        for (int k = 1; k < R; ++k) dsel = (k == ridx) ? d[k] : dsel;
+        const float r = row_reduce<R, LPR>(e, lane);
+        if ((q % (LPR / R)) == 0) {
+            const float vi = io::ld(vin, ph * dv + i0 + iw);
+            a.out[ph * dv + i0 + iw] = a.scale * (al * (r - be * dsel * kq) + be * vi * kq);
+        }
     }
 }
 
@@ -348,19 +525,23 @@ static void gdn_chunking(int rv, int* nchunk, int* per) {
     *nchunk = (rv + *per - 1) / *per;
 }
 
-size_t gdn_smem_bytes(int dk, int dv, int L, int rv, int io_bytes) {
+size_t gdn_smem_bytes(int dk, int dv, int L, int rv, int mode, int n_pos, int io_bytes) {
     int nchunk, per;
     gdn_chunking(rv, &nchunk, &per);
-    return sizeof(float) * (size_t)GdnSmem(dk, dv, L, per, io_bytes).total;
+    const int T = (mode == kGdnSpec) ? n_pos : (mode == kGdnDecode ? 1 : 0);
+    return sizeof(float) * (size_t)GdnSmem(dk, dv, L, T, mode, per, io_bytes).total;
+}
+
+template <int DK, int DV, typename IO>
+static const void* gdn_pick_mode(int mode) {
+    if (mode == kGdnFold) return (const void*)&gdn_replay_kernel<DK, DV, IO, kGdnFold>;
+    if (mode == kGdnSpec) return (const void*)&gdn_replay_kernel<DK, DV, IO, kGdnSpec>;
+    return (const void*)&gdn_replay_kernel<DK, DV, IO, kGdnDecode>;
 }
 
 template <int DK, int DV>
 static const void* gdn_pick(int io, int mode) {
-    if (io == kIoBF16)
-        return mode == kGdnFold ? (const void*)&gdn_replay_kernel<DK, DV, uint16_t, kGdnFold>
-                                : (const void*)&gdn_replay_kernel<DK, DV, uint16_t, kGdnDecode>;
-    return mode == kGdnFold ? (const void*)&gdn_replay_kernel<DK, DV, float, kGdnFold>
-                            : (const void*)&gdn_replay_kernel<DK, DV, float, kGdnDecode>;
+    return io == kIoBF16 ? gdn_pick_mode<DK, DV, uint16_t>(mode) : gdn_pick_mode<DK, DV, float>(mode);
 }
 
 hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t stream) {
@@ -372,22 +553,45 @@ hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t str
     if (!fn) return hipErrorInvalidValue;
     GdnArgs args = a;
     gdn_chunking(a.hv / a.hk, &args.nchunk, &args.vheads_per_chunk);
-    const size_t smem = gdn_smem_bytes(a.dk, a.dv, a.L, a.hv / a.hk, io == kIoBF16 ? 2 : 4);
+    if (mode != kGdnSpec) args.n_pos = (mode == kGdnDecode) ? 1 : 0;
+    const size_t smem = gdn_smem_bytes(a.dk, a.dv, a.L, a.hv / a.hk, mode, args.n_pos, io == kIoBF16 ? 2 : 4);
     void* kargs[] = {&args};
     const dim3 grid((unsigned)((size_t)a.batch * a.hk * args.nchunk));
-    return hipLaunchKernel(fn, grid, dim3(kGdnThreads), kargs, smem, stream);
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(kGdnThreads), kargs, smem, stream);
+    if (e != hipSuccess || mode != kGdnSpec || args.nchunk == 1) return e;
+    const void* app = nullptr;
+    if (a.dk == 64)
+        app = io == kIoBF16 ? (const void*)&gdn_spec_append_k_kernel<64, uint16_t>
+                            : (const void*)&gdn_spec_append_k_kernel<64, float>;
+    else
+        app = io == kIoBF16 ? (const void*)&gdn_spec_append_k_kernel<128, uint16_t>
+                            : (const void*)&gdn_spec_append_k_kernel<128, float>;
+    const size_t total = (size_t)a.batch * args.n_pos * a.hk * (a.dk / 4);
+    const size_t want = (total + kGdnThreads - 1) / kGdnThreads;
+    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+    return hipLaunchKernel(app, dim3(blocks), dim3(kGdnThreads), kargs, 0, stream);
 }
 
-hipError_t launch_gdn_conventional(const GdnArgs& a, int io, hipStream_t stream) {
+hipError_t launch_gdn_conventional(const GdnArgs& a, int io, bool snapshots, hipStream_t stream) {
     const void* fn = nullptr;
-    if (a.dk == 64)
-        fn = io == kIoBF16 ? (const void*)&gdn_conventional_kernel<64, uint16_t>
-                           : (const void*)&gdn_conventional_kernel<64, float>;
-    else if (a.dk == 128)
-        fn = io == kIoBF16 ? (const void*)&gdn_conventional_kernel<128, uint16_t>
-                           : (const void*)&gdn_conventional_kernel<128, float>;
+    if (a.dk == 64) {
+        if (io == kIoBF16)
+            fn = snapshots ? (const void*)&gdn_conventional_kernel<64, uint16_t, true>
+                           : (const void*)&gdn_conventional_kernel<64, uint16_t, false>;
+        else
+            fn = snapshots ? (const void*)&gdn_conventional_kernel<64, float, true>
+                           : (const void*)&gdn_conventional_kernel<64, float, false>;
+    } else if (a.dk == 128) {
+        if (io == kIoBF16)
+            fn = snapshots ? (const void*)&gdn_conventional_kernel<128, uint16_t, true>
+                           : (const void*)&gdn_conventional_kernel<128, uint16_t, false>;
+        else
+            fn = snapshots ? (const void*)&gdn_conventional_kernel<128, float, true>
+                           : (const void*)&gdn_conventional_kernel<128, float, false>;
+    }
     if (!fn) return hipErrorInvalidValue;
     GdnArgs args = a;
+    if (!snapshots) args.n_pos = 1;
     void* kargs[] = {&args};
     const dim3 grid((unsigned)((size_t)a.batch * a.hv * (a.dv / 64)));
     return hipLaunchKernel(fn, grid, dim3(kGdnThreads), kargs, 0, stream);

@@ -55,16 +55,18 @@ struct GdnArgs {
     void* rec_v;          // [B,HV,L,dv]
     float* rec_alpha;     // [B,HV,L]
     float* rec_beta;      // [B,HV,L]
-    const int32_t* cursor_in;
-    int32_t* cursor_out;
-    const void* q;        // [B,HK,dk]
-    const void* k;        // [B,HK,dk]
-    const void* v;        // [B,HV,dv]
-    const float* alpha;   // [B,HV]
-    const float* beta;    // [B,HV]
-    float* out;           // [B,HV,dv]
+    const int32_t* cursor_in;   // AR cursor, or the speculative head
+    int32_t* cursor_out;        // AR only
+    const int32_t* committed;   // speculative only
+    int32_t* flushed;           // speculative only
+    const void* q;        // [B,(T,)HK,dk]
+    const void* k;        // [B,(T,)HK,dk]
+    const void* v;        // [B,(T,)HV,dv]
+    const float* alpha;   // [B,(T,)HV]
+    const float* beta;    // [B,(T,)HV]
+    float* out;           // [B,(T,)HV,dv]
     int32_t* err_flags;
-    int32_t batch, hv, hk, dk, dv, L;
+    int32_t batch, hv, hk, dk, dv, L, n_pos;
     float scale;
     int32_t nchunk;            // workgroups per (sequence, q/k head)
     int32_t vheads_per_chunk;
@@ -88,9 +90,10 @@ hipError_t launch_reset(int32_t batch, int32_t* head, int32_t* cursor, const int
                         int32_t n_seq, hipStream_t stream);
 
 bool gdn_shape_supported(int dk, int dv);
-size_t gdn_smem_bytes(int dk, int dv, int L, int heads_ratio, int io_bytes);
-// mode: 0 = AR decode, 1 = fold stored records only
+size_t gdn_smem_bytes(int dk, int dv, int L, int heads_ratio, int mode, int n_pos, int io_bytes);
+// mode: 0 = AR decode, 1 = fold stored records only, 2 = speculative verify
 hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t stream);
-hipError_t launch_gdn_conventional(const GdnArgs& a, int io, hipStream_t stream);
+// snapshots: per-position snapshot baseline (ckpt = snapshots, cursor_in = slot_in)
+hipError_t launch_gdn_conventional(const GdnArgs& a, int io, bool snapshots, hipStream_t stream);
 
 }  // namespace rssm

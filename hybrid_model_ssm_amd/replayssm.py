@@ -32,7 +32,7 @@ EXPORTED = (
     "replayssm_mamba2_decode", "replayssm_mamba2_flush", "replayssm_mamba2_spec_verify",
     "replayssm_commit", "replayssm_reset_cursors", "replayssm_selective_state_update",
     "replayssm_mamba2_spec_baseline", "replayssm_gdn_decode", "replayssm_gdn_flush",
-    "replayssm_gdn_conventional_decode",
+    "replayssm_gdn_spec_verify", "replayssm_gdn_conventional_decode", "replayssm_gdn_spec_baseline",
 )
 
 
@@ -98,7 +98,9 @@ def lib():
         "replayssm_mamba2_spec_baseline": [D, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_decode": [GD, GS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_flush": [GD, GS, _P, _P, _P, _P],
+        "replayssm_gdn_spec_verify": [GD, GS, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_conventional_decode": [GD, _P, _P, _P, _P, _P, _P, _P, _P],
+        "replayssm_gdn_spec_baseline": [GD, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -337,6 +339,19 @@ def gdn_flush(desc, state, cursor_in, cursor_out, err_flags=None, stream=None):
     _check(st, "replayssm_gdn_flush")
 
 
+def gdn_spec_verify(desc, state, head, committed, n_pos, q, k, v, alpha, beta, out, flushed,
+                    err_flags=None, stream=None):
+    io = desc.torch_io
+    st = lib().replayssm_gdn_spec_verify(
+        ctypes.byref(desc.c()), ctypes.byref(state.c()),
+        _ptr(head, torch.int32, "head"), _ptr(committed, torch.int32, "committed"), int(n_pos),
+        _ptr(q, io, "q"), _ptr(k, io, "k"), _ptr(v, io, "v"),
+        _ptr(alpha, torch.float32, "alpha"), _ptr(beta, torch.float32, "beta"),
+        _ptr(out, torch.float32, "out"), _ptr(flushed, torch.int32, "flushed"),
+        _ptr(err_flags, torch.int32, "err_flags"), _stream(stream))
+    _check(st, "replayssm_gdn_spec_verify")
+
+
 def gdn_conventional_decode(desc, state, q, k, v, alpha, beta, out, stream=None):
     io = desc.torch_io
     st = lib().replayssm_gdn_conventional_decode(
@@ -345,3 +360,14 @@ def gdn_conventional_decode(desc, state, q, k, v, alpha, beta, out, stream=None)
         _ptr(alpha, torch.float32, "alpha"), _ptr(beta, torch.float32, "beta"),
         _ptr(out, torch.float32, "out"), _stream(stream))
     _check(st, "replayssm_gdn_conventional_decode")
+
+
+def gdn_spec_baseline(desc, snapshots, slot_in, n_pos, q, k, v, alpha, beta, out, stream=None):
+    io = desc.torch_io
+    st = lib().replayssm_gdn_spec_baseline(
+        ctypes.byref(desc.c()), _ptr(snapshots, torch.float32, "snapshots"),
+        _ptr(slot_in, torch.int32, "slot_in"), int(n_pos),
+        _ptr(q, io, "q"), _ptr(k, io, "k"), _ptr(v, io, "v"),
+        _ptr(alpha, torch.float32, "alpha"), _ptr(beta, torch.float32, "beta"),
+        _ptr(out, torch.float32, "out"), _stream(stream))
+    _check(st, "replayssm_gdn_spec_baseline")

@@ -53,6 +53,8 @@ WORKLOADS = {
                              ngroups=8, buffer_len=16, rounds=256, n_pos=4, io="bf16", seed=1003),
     "gdn_hv32": dict(kind="gdn", batch=256, num_v_heads=32, num_k_heads=16, dk=128, dv=128,
                      buffer_len=16, steps=512, io="bf16", seed=1004),
+    "gdn_spec_hv32": dict(kind="gdn_spec", batch=256, num_v_heads=32, num_k_heads=16, dk=128, dv=128,
+                          buffer_len=16, rounds=256, n_pos=4, io="bf16", seed=1005),
 }
 
 
@@ -131,20 +133,26 @@ class GDNInputs:
         ckpt = self.rng.standard_normal((batch, num_v_heads, dv, dk), dtype=np.float32) * np.float32(ckpt_std)
         self.static = GDNStatic(ckpt.astype(np.float32))
 
-    def step(self):
+    def step(self, n_pos=None):
+        """One step's inputs (or one speculative round's, with a position axis after batch)."""
         rng = self.rng
         Bt, HV, HK, dk, dv = self.batch, self.HV, self.HK, self.dk, self.dv
-        q = rng.standard_normal((Bt, HK, dk), dtype=np.float32)
-        k = rng.standard_normal((Bt, HK, dk), dtype=np.float32)
+        lead = (Bt,) if n_pos is None else (Bt, n_pos)
+        q = rng.standard_normal(lead + (HK, dk), dtype=np.float32)
+        k = rng.standard_normal(lead + (HK, dk), dtype=np.float32)
         q = q / np.linalg.norm(q, axis=-1, keepdims=True)
         k = k / np.linalg.norm(k, axis=-1, keepdims=True)
-        v = rng.standard_normal((Bt, HV, dv), dtype=np.float32)
-        bl = rng.standard_normal((Bt, HV))
-        al = rng.standard_normal((Bt, HV))
+        v = rng.standard_normal(lead + (HV, dv), dtype=np.float32)
+        bl = rng.standard_normal(lead + (HV,))
+        al = rng.standard_normal(lead + (HV,))
         beta = (1.0 / (1.0 + np.exp(-bl))).astype(np.float32)
         sp = np.log1p(np.exp(al - 2.0))
         alpha = np.exp(-sp).astype(np.float32)
         return dict(q=_io(q, self.io), k=_io(k, self.io), v=_io(v, self.io), alpha=alpha, beta=beta)
+
+    def accepted(self, n_drafts):
+        """Accepted draft count per sequence, ``k ~ U{0..n_drafts}``; keep ``k + 1`` positions."""
+        return self.rng.integers(0, n_drafts + 1, size=self.batch).astype(np.int32)
 
 
 def mamba2_inputs(name, **over):

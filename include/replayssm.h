@@ -301,11 +301,52 @@ replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const repla
                                      const int32_t* cursor_in, int32_t* cursor_out,
                                      int32_t* err_flags, hipStream_t stream);
 
+/*
+ * Gated DeltaNet speculative verification over n_pos positions on the circular
+ * buffer (the GDN speculative decode kernel of "Core implementation files", with
+ * its own commit and reset calls; rollback as in "ReplaySSM" README, "Cheap
+ * rollback").  Cursor rules as replayssm_mamba2_spec_verify: with hd = head[b]
+ * (0 <= hd < L) and cm = committed[b] (0 <= cm <= L), if cm + n_pos > L the cm
+ * committed records (slots (hd + i) % L) are folded into the checkpoint, which is
+ * stored, and flushed[b] = 1; otherwise flushed[b] = 0 and the checkpoint is not
+ * written.  Position j's record goes to slot (hd + cm + j) % L, and its output
+ * carries q_j back through positions j..0 and then the committed records (none
+ * after a fold):  o_j = scale (ckpt u_j + acc_j).  head and committed are NOT
+ * changed here; replayssm_commit applies the round and replayssm_reset_cursors
+ * starts new sequences.
+ *
+ *   q, k io [batch, n_pos, num_k_heads, dk];  v io [batch, n_pos, num_v_heads, dv];
+ *   alpha, beta f32 [batch, n_pos, num_v_heads];
+ *   out f32 [batch, n_pos, num_v_heads, dv];  flushed int32 [batch] written;
+ *   head, committed int32 [batch] read only.  1 <= n_pos <= buffer_len; shapes
+ *   whose staging exceeds one workgroup's LDS give REPLAYSSM_ERR_UNSUPPORTED.
+ *   Invalid cursors: REPLAYSSM_DEVERR_CURSOR is ORed into err_flags and that
+ *   sequence's outputs, records, checkpoint and flushed[b] are left untouched.
+ */
+replayssm_status replayssm_gdn_spec_verify(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
+                                           const int32_t* head, const int32_t* committed, int32_t n_pos,
+                                           const void* q, const void* k, const void* v,
+                                           const float* alpha, const float* beta, float* out,
+                                           int32_t* flushed, int32_t* err_flags, hipStream_t stream);
+
 /* Conventional GDN step: state f32 [batch, num_v_heads, dv, dk] updated in place. */
 replayssm_status replayssm_gdn_conventional_decode(const replayssm_gdn_desc* desc, float* state,
                                                    const void* q, const void* k, const void* v,
                                                    const float* alpha, const float* beta,
                                                    float* out, hipStream_t stream);
+
+/*
+ * Conventional Gated DeltaNet speculative baseline: one state snapshot per position
+ * ("Why SSM layers slow down hybrid models": a snapshot is stored after every draft
+ * token).  Reads snapshot slot_in[b] (clamped to [0, n_pos)) of snapshots f32
+ * [batch, n_pos, num_v_heads, dv, dk], runs the n_pos gated delta updates in order
+ * and writes the state after position j into slot j; outputs as
+ * replayssm_gdn_spec_verify.  The next round passes slot_in[b] = n_keep[b] - 1.
+ */
+replayssm_status replayssm_gdn_spec_baseline(const replayssm_gdn_desc* desc, float* snapshots,
+                                             const int32_t* slot_in, int32_t n_pos, const void* q,
+                                             const void* k, const void* v, const float* alpha,
+                                             const float* beta, float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("replayssm_mamba2_decode", "replayssm_mamba2_flush", "replayssm_mamba2_spec_verify",
               "replayssm_commit", "replayssm_reset_cursors", "replayssm_gdn_decode", "replayssm_gdn_flush",
-              "replayssm_selective_state_update"):
+              "replayssm_gdn_spec_verify", "replayssm_selective_state_update"):
         assert n in names
     assert set(names) == set(rs.EXPORTED)
 
@@ -188,6 +188,26 @@ def test_gdn_validation(L):
     assert L.replayssm_gdn_flush(ctypes.byref(gdesc()), ctypes.byref(s), fake(6), fake(6), None, None) == INV
     assert L.replayssm_gdn_conventional_decode(ctypes.byref(gdesc()), None, fake(8), fake(9), fake(10),
                                                fake(11), fake(12), fake(13), None) == INV
+
+    def spec(desc, hd=fake(6), cm=fake(7), n_pos=4, fl=fake(14)):
+        return L.replayssm_gdn_spec_verify(ctypes.byref(desc), ctypes.byref(s), hd, cm, n_pos, fake(8), fake(9),
+                                           fake(10), fake(11), fake(12), fake(13), fl, None, None)
+    assert spec(gdesc(), n_pos=0) == INV
+    assert spec(gdesc(), n_pos=17) == INV                    # beyond buffer_len
+    assert spec(gdesc(), cm=fake(6)) == INV                  # head aliases committed
+    assert spec(gdesc(), fl=fake(7)) == INV                  # flushed aliases committed
+    assert spec(gdesc(), fl=None) == INV
+    assert spec(gdesc(dk=96)) == UNS
+    # staging of 64 + 64 rows for four value heads exceeds one workgroup's LDS
+    assert spec(gdesc(buffer_len=64, num_v_heads=16, io_dtype=rs.F32), n_pos=64) == UNS
+
+    def snap(desc, sn=fake(1), slot=fake(2), n_pos=4):
+        return L.replayssm_gdn_spec_baseline(ctypes.byref(desc), sn, slot, n_pos, fake(8), fake(9), fake(10),
+                                             fake(11), fake(12), fake(13), None)
+    assert snap(gdesc(), n_pos=0) == INV
+    assert snap(gdesc(), sn=None) == INV
+    assert snap(gdesc(), slot=None) == INV
+    assert snap(gdesc(dv=96)) == UNS
 
 
 def test_binding_refuses_host_tensors(L):

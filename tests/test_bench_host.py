@@ -47,6 +47,17 @@ def test_spec_byte_model_flush_and_plain_rounds():
         G * T * 2 * N * 2
 
 
+def test_gdn_spec_byte_model():
+    HV, HK, dk, dv, L, T = 32, 16, 128, 128, 16, 4
+    plain = bench.gdn_spec_round_bytes(HV, HK, dk, dv, L, 2, T, [0])
+    fold = bench.gdn_spec_round_bytes(HV, HK, dk, dv, L, 2, T, [13])
+    # a folding round writes the checkpoint (dv*dk*4 per value head) and reads 13 records
+    assert fold - plain - 13 * (HV * (dv * 2 + 8) + HK * dk * 2) == HV * dv * dk * 4
+    assert plain == HV * (dv * dk * 4 + T * (dv * 2 + 8 + dv * 4) + T * (dv * 2 + 8)) + HK * (T * 3 * dk * 2)
+    assert bench.gdn_spec_baseline_bytes(1, HV, HK, dk, dv, 2, T) == \
+        HV * (dv * dk * 4 * 5 + T * (dv * 2 + 8 + dv * 4)) + HK * T * 2 * dk * 2
+
+
 def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
