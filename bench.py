@@ -16,9 +16,10 @@ sample of the same workload and checks the GPU outputs for that sample.
 
 Measured beside the headline, each with its own timed region: the in-library
 conventional read-update-write kernel on the same inputs, the bf16 read copy, the
-B=256/H=64 layer, speculative verification (4 positions, commit) against the
-per-position snapshot baseline, and the Gated DeltaNet layer (replay decode and
-conventional; speculative verification against its snapshot baseline).  ``ceiling`` reports plain device read and copy bandwidth.
+state-and-output decode route, the B=256/H=64 layer, speculative verification (4
+positions, commit) against the per-position snapshot baseline, and the Gated DeltaNet
+layer (replay decode and conventional; speculative verification against its snapshot
+baseline).  ``ceiling`` reports plain device read and copy bandwidth.
 
 Auxiliary modes used to make the committed rocprofv3 summaries:
     --calibrate-copy        also run a plain 1 GiB device copy (counter calibration)
@@ -159,7 +160,8 @@ def _check(st, name):
 class Mamba2Bench:
     """Device buffers and pre-marshalled launch arguments for one Mamba2 workload."""
 
-    def __init__(self, torch, rs, synth, name, pool=32, lowp=False, conventional=False, seed_override=None):
+    def __init__(self, torch, rs, synth, name, pool=32, lowp=False, conventional=False, seed_override=None,
+                 state_and_output=False):
         import ctypes
         self.torch, self.rs = torch, rs
         w = dict(synth.WORKLOADS[name])
@@ -211,7 +213,7 @@ class Mamba2Bench:
                                   *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
                                   self.bias.data_ptr(), self.A.data_ptr(), self.D.data_ptr(),
                                   self.out.data_ptr(), self.err.data_ptr(), stream))
-            self.fn = L.replayssm_mamba2_decode
+            self.fn = L.replayssm_mamba2_decode_state_and_output if state_and_output else L.replayssm_mamba2_decode
 
     def launch(self, i):
         a = self.args[i % len(self.args)]
@@ -645,7 +647,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1024, help="timed decode steps of the headline")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--only", default="all",
-                    help="all, headline, or a comma list of: conventional,bf16,h64,spec,gdn,gdn_spec")
+                    help="all, headline, or a comma list of: conventional,bf16,so,h64,spec,gdn,gdn_spec")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--cpu-steps", type=int, default=32)
@@ -696,7 +698,7 @@ def main(argv=None):
 
     variants = {}
     conv = None
-    groups = {"conventional", "bf16", "h64", "spec", "gdn", "gdn_spec"} if args.only == "all" else \
+    groups = {"conventional", "bf16", "so", "h64", "spec", "gdn", "gdn_spec"} if args.only == "all" else \
         set() if args.only == "headline" else set(args.only.split(","))
     if "conventional" in groups:
         conv, _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup, conventional=True)
@@ -705,6 +707,10 @@ def main(argv=None):
     if "bf16" in groups:
         variants["mamba2_h128_bf16_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup,
                                                            lowp=True)
+        torch.cuda.empty_cache()
+    if "so" in groups:
+        variants["mamba2_h128_state_and_output"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps,
+                                                                  args.warmup, state_and_output=True)
         torch.cuda.empty_cache()
     if "h64" in groups:
         variants["mamba2_h64_replay"], _ = time_mamba2(torch, rs, synth, "mamba2_h64", 256, 32)

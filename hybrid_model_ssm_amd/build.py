@@ -28,7 +28,7 @@ LIB = os.path.join(PKG, "libreplayssm.so")
 SOURCES = [("api.cpp", "api", []), ("mamba2_launch.hip", "mamba2_launch", []),
            ("gdn_kernels.hip", "gdn_kernels", []), ("cursor_kernels.hip", "cursor_kernels", [])]
 SOURCES += [("mamba2_inst.hip", f"mamba2_inst_io{io}_part{part}", [f"-DRSSM_IO={io}", f"-DRSSM_PART={part}"])
-            for io in (0, 1) for part in (0, 1, 2, 3)]
+            for io in (0, 1) for part in (0, 1, 2, 3, 4)]
 ARCH = "gfx950"
 
 

@@ -128,6 +128,31 @@ rssm::GdnArgs gdn_args(const replayssm_gdn_desc* d, const replayssm_gdn_state* s
 
 }  // namespace
 
+// One autoregressive decode step; mode 0 is the output-only route, mode 3 the
+// state-and-output route (same arguments, same cursor and record rules).
+static replayssm_status mamba2_decode_route(int mode, const replayssm_mamba2_desc* desc,
+                                            const replayssm_mamba2_state* state,
+                                            const int32_t* cursor_in, int32_t* cursor_out,
+                                            const void* x, const void* z, const void* B,
+                                            const void* C, const void* dt_raw, const float* dt_bias,
+                                            const float* A, const float* D, float* out,
+                                            int32_t* err_flags, hipStream_t stream) {
+    replayssm_status st = check_mamba2_desc(desc, true);
+    if (st != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_state(desc, state)) != REPLAYSSM_OK) return st;
+    if ((st = check_mamba2_inputs(desc, x, z, B, C, dt_raw, dt_bias, A, D, out)) != REPLAYSSM_OK) return st;
+    REQ(cursor_in && cursor_out && cursor_in != cursor_out);
+    REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
+    if (!replay_fits(desc, 0)) return REPLAYSSM_ERR_UNSUPPORTED;
+    rssm::Mamba2Args a = mamba2_args(desc, state);
+    a.cursor_in = cursor_in;
+    a.cursor_out = cursor_out;
+    a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
+    a.n_pos = 1;
+    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, mode, stream));
+}
+
 extern "C" {
 
 const char* replayssm_status_string(replayssm_status status) {
@@ -149,20 +174,20 @@ replayssm_status replayssm_mamba2_decode(const replayssm_mamba2_desc* desc,
                                          const void* C, const void* dt_raw, const float* dt_bias,
                                          const float* A, const float* D, float* out,
                                          int32_t* err_flags, hipStream_t stream) {
-    replayssm_status st = check_mamba2_desc(desc, true);
-    if (st != REPLAYSSM_OK) return st;
-    if ((st = check_mamba2_state(desc, state)) != REPLAYSSM_OK) return st;
-    if ((st = check_mamba2_inputs(desc, x, z, B, C, dt_raw, dt_bias, A, D, out)) != REPLAYSSM_OK) return st;
-    REQ(cursor_in && cursor_out && cursor_in != cursor_out);
-    REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
-    if (!replay_fits(desc, 0)) return REPLAYSSM_ERR_UNSUPPORTED;
-    rssm::Mamba2Args a = mamba2_args(desc, state);
-    a.cursor_in = cursor_in;
-    a.cursor_out = cursor_out;
-    a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
-    a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
-    a.n_pos = 1;
-    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, 0, stream));
+    return mamba2_decode_route(0, desc, state, cursor_in, cursor_out, x, z, B, C, dt_raw, dt_bias, A, D, out,
+                               err_flags, stream);
+}
+
+replayssm_status replayssm_mamba2_decode_state_and_output(const replayssm_mamba2_desc* desc,
+                                                          const replayssm_mamba2_state* state,
+                                                          const int32_t* cursor_in, int32_t* cursor_out,
+                                                          const void* x, const void* z, const void* B,
+                                                          const void* C, const void* dt_raw,
+                                                          const float* dt_bias, const float* A,
+                                                          const float* D, float* out, int32_t* err_flags,
+                                                          hipStream_t stream) {
+    return mamba2_decode_route(3, desc, state, cursor_in, cursor_out, x, z, B, C, dt_raw, dt_bias, A, D, out,
+                               err_flags, stream);
 }
 
 replayssm_status replayssm_mamba2_flush(const replayssm_mamba2_desc* desc,

@@ -78,7 +78,8 @@ size_t mamba2_replay_smem_bytes(int headdim, int dstate, int heads_per_group, in
                                 int io_bytes);
 size_t mamba2_max_smem_bytes();
 
-// mode: 0 = AR decode step, 1 = fold stored records only (flush), 2 = speculative verify
+// mode: 0 = AR decode step, 1 = fold stored records only (flush), 2 = speculative verify,
+//       3 = AR decode step by the state-and-output route
 hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int mode, hipStream_t stream);
 hipError_t launch_mamba2_conventional(const Mamba2ConvArgs& a, int io, bool snapshots,
                                       hipStream_t stream);

@@ -1,6 +1,6 @@
 // Instantiates one slice of the Mamba2 kernel templates so that the slices compile in
 // parallel.  Built several times with RSSM_IO (0: f32 io, 1: bf16 io) and RSSM_PART
-// (0..2: replay kernel mode, 3: conventional kernels).
+// (0..3: replay kernel mode, 4: conventional kernels).
 #include "mamba2_kernels.h"
 #include "mamba2_shapes.h"
 
@@ -19,7 +19,7 @@ using InstIo = uint16_t;
 using InstIo = float;
 #endif
 
-#if RSSM_PART < 3
+#if RSSM_PART < 4
 const void* RSSM_REPLAY_PTR_NAME(RSSM_IO, RSSM_PART)(int P, int N, bool lowp) {
 #define X(PP, NN)                                                                          \
     if (P == PP && N == NN)                                                                \

@@ -30,6 +30,11 @@
 //   kSpec    speculative verification over n_pos positions on the circular buffer
 //            ("ReplaySSM" README, benefit "Cheap rollback": output-only verification,
 //            rejected inputs dropped by moving a pointer)
+//   kDecodeSO  one autoregressive step by the state-and-output route ("ReplaySSM (a
+//            vLLM research fork)", "Core implementation files", names it beside the
+//            default output-only route): every step rebuilds the current state
+//            decay * Hc + sum_s w_s x_s B_s^T of the whole window in registers and reads
+//            the output from it; only the step that fills the buffer stores it.
 
 #pragma once
 
@@ -41,6 +46,7 @@ namespace rssm {
 constexpr int kDecode = 0;
 constexpr int kFold = 1;
 constexpr int kSpec = 2;
+constexpr int kDecodeSO = 3;
 constexpr int kThreads = 256;
 constexpr int kMaxHeadsPerWg = 16;
 constexpr int kFoldXPerThread = 4;  // 4-element loads per thread for one head's fold rows
@@ -114,7 +120,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     const int h0 = g * hpg + chunk * a.heads_per_chunk;
     const int nh = min(a.heads_per_chunk, hpg - chunk * a.heads_per_chunk);
     const bool lead = (g == 0 && chunk == 0);  // writes the per-sequence cursor outputs
-    const int T = (MODE == kSpec) ? a.n_pos : (MODE == kDecode ? 1 : 0);
+    const int T = (MODE == kSpec) ? a.n_pos : (MODE == kFold ? 0 : 1);
 
     // ---- cursors -------------------------------------------------------------------
     int c = 0, hd = 0, cm = 0;
@@ -136,14 +142,18 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     }
     const int nstored = (MODE == kSpec) ? cm : c;   // window rows taken from the ring
     const int nrec = nstored + T;                    // window rows
-    const bool fold = (MODE == kFold) || (MODE == kDecode && c + 1 == L) ||
-                      (MODE == kSpec && cm + T > L);
+    // flush: the checkpoint is rewritten; fold: the window is applied to the tile in
+    // registers (every step of the state-and-output route)
+    const bool flush = (MODE == kFold) || ((MODE == kDecode || MODE == kDecodeSO) && c + 1 == L) ||
+                       (MODE == kSpec && cm + T > L);
+    const bool fold = flush || MODE == kDecodeSO;
     const int nf = (MODE == kSpec) ? cm : nrec;      // the fold covers rows [0, nf)
     const int st = fold ? nf : 0;                    // first row of every output window
     const bool use_lp = LOWP && !fold;
     // explicit flush of an empty buffer: the fp32 checkpoint stays as it is
-    const bool keep_ckpt = (MODE == kFold) && c == 0;
-    const bool idle = keep_ckpt && !LOWP;
+    const bool keep_ckpt = ((MODE == kFold) && c == 0) || !flush;
+    const bool store_lp = LOWP && flush;
+    const bool idle = (MODE == kFold) && c == 0 && !LOWP;
 
     const GroupSmem lay(P, N, L, T, a.heads_per_chunk, MODE, (int)sizeof(IO));
     const int NR = lay.NR, T1 = lay.T1, US = lay.US;
@@ -239,7 +249,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     // (autoregressive decode only: in speculative mode they would stay live across the
     // head loop and cost occupancy)
     constexpr int kAppendPerThread = (MODE == kDecode) ? 2 : 0;
-    const int napp = (MODE == kFold || (MODE == kDecode && fold)) ? 0 : nh * T * P4;
+    const int napp = (MODE == kFold || (MODE != kSpec && flush)) ? 0 : nh * T * P4;
     Raw4 app[kAppendPerThread > 0 ? kAppendPerThread : 1];
 #pragma unroll
     for (int i = 0; i < kAppendPerThread; ++i) {
@@ -393,7 +403,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     // SIMD).
     constexpr int TB = (MODE == kSpec) ? (LPR / R >= 2 ? 2 : 1) : 1;
     auto outputs = [&](int hl, const float4 (&v)[R]) {
-        if constexpr (MODE == kDecode) {
+        if constexpr (MODE == kDecode || MODE == kDecodeSO) {
             const int h = h0 + hl;
             const float4 Cv = *reinterpret_cast<const float4*>(sC + 4 * col4);
             float acc[R];
@@ -518,7 +528,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 if (!MASK || row0 + k * RPP < P) {
                     const size_t off = t + (size_t)k * RPP * N;
                     if (!keep_ckpt) st_stream(a.ckpt + off, va[k]);
-                    if (LOWP) st_stream(a.ckpt_lp + off, f32x4_to_bf16x4(va[k]));
+                    if (store_lp) st_stream(a.ckpt_lp + off, f32x4_to_bf16x4(va[k]));
                 }
             }
             outputs(hl, va);
@@ -536,7 +546,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
 
     // ---- append this step's records --------------------------------------------------
     if constexpr (MODE != kFold) {
-        if (MODE == kSpec || !fold) {
+        if (MODE == kSpec || !flush) {
             // speculative rounds may overwrite ring slots that other heads read above
             if (MODE == kSpec) __syncthreads();
             const int slot0 = (MODE == kSpec) ? hd + cm : c;
@@ -574,8 +584,8 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     }
 
     if (tid == 0 && lead) {
-        if (MODE == kSpec) a.flushed[b] = fold ? 1 : 0;
-        else a.cursor_out[b] = (MODE == kFold || fold) ? 0 : c + 1;
+        if (MODE == kSpec) a.flushed[b] = flush ? 1 : 0;
+        else a.cursor_out[b] = flush ? 0 : c + 1;
     }
 }
 

@@ -37,11 +37,13 @@ static const void* find_replay(int P, int N, int io, bool lowp, int mode) {
     if (io == kIoBF16) {
         if (mode == kDecode) return replay_kernel_ptr_io1_mode0(P, N, lowp);
         if (mode == kFold) return replay_kernel_ptr_io1_mode1(P, N, lowp);
-        return replay_kernel_ptr_io1_mode2(P, N, lowp);
+        if (mode == kSpec) return replay_kernel_ptr_io1_mode2(P, N, lowp);
+        return replay_kernel_ptr_io1_mode3(P, N, lowp);
     }
     if (mode == kDecode) return replay_kernel_ptr_io0_mode0(P, N, lowp);
     if (mode == kFold) return replay_kernel_ptr_io0_mode1(P, N, lowp);
-    return replay_kernel_ptr_io0_mode2(P, N, lowp);
+    if (mode == kSpec) return replay_kernel_ptr_io0_mode2(P, N, lowp);
+    return replay_kernel_ptr_io0_mode3(P, N, lowp);
 }
 
 static const void* find_conv(int P, int N, int io, bool snap) {
@@ -53,7 +55,7 @@ hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int mode, hipStream
     if (!fn) return hipErrorInvalidValue;
     Mamba2Args args = a;
     chunking(a.nheads / a.ngroups, &args.nchunk, &args.heads_per_chunk);
-    const int T = mode == kSpec ? a.n_pos : (mode == kDecode ? 1 : 0);
+    const int T = mode == kSpec ? a.n_pos : (mode == kFold ? 0 : 1);
     const size_t smem = sizeof(float) * (size_t)GroupSmem(a.headdim, a.dstate, a.L, T, args.heads_per_chunk, mode,
                                                           io == kIoBF16 ? 2 : 4).total;
     void* kargs[] = {&args};

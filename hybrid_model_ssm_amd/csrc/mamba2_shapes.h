@@ -16,9 +16,11 @@ namespace rssm {
 const void* replay_kernel_ptr_io0_mode0(int P, int N, bool lowp);
 const void* replay_kernel_ptr_io0_mode1(int P, int N, bool lowp);
 const void* replay_kernel_ptr_io0_mode2(int P, int N, bool lowp);
+const void* replay_kernel_ptr_io0_mode3(int P, int N, bool lowp);
 const void* replay_kernel_ptr_io1_mode0(int P, int N, bool lowp);
 const void* replay_kernel_ptr_io1_mode1(int P, int N, bool lowp);
 const void* replay_kernel_ptr_io1_mode2(int P, int N, bool lowp);
+const void* replay_kernel_ptr_io1_mode3(int P, int N, bool lowp);
 const void* conv_kernel_ptr_io0(int P, int N, bool snap);
 const void* conv_kernel_ptr_io1(int P, int N, bool snap);
 }  // namespace rssm

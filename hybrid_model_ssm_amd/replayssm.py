@@ -29,7 +29,8 @@ MAX_BUFFER_LEN = 64
 
 EXPORTED = (
     "replayssm_status_string", "replayssm_version",
-    "replayssm_mamba2_decode", "replayssm_mamba2_flush", "replayssm_mamba2_spec_verify",
+    "replayssm_mamba2_decode", "replayssm_mamba2_decode_state_and_output", "replayssm_mamba2_flush",
+    "replayssm_mamba2_spec_verify",
     "replayssm_commit", "replayssm_reset_cursors", "replayssm_selective_state_update",
     "replayssm_mamba2_spec_baseline", "replayssm_gdn_decode", "replayssm_gdn_flush",
     "replayssm_gdn_spec_verify", "replayssm_gdn_conventional_decode", "replayssm_gdn_spec_baseline",
@@ -90,6 +91,7 @@ def lib():
     GD, GS = ctypes.POINTER(GdnDescC), ctypes.POINTER(GdnStateC)
     sig = {
         "replayssm_mamba2_decode": [D, S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "replayssm_mamba2_decode_state_and_output": [D, S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_mamba2_flush": [D, S, _P, _P, _P, _P, _P],
         "replayssm_mamba2_spec_verify": [D, S, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_commit": [_I, _I, _I, _P, _P, _P, _P, _P, _P],
@@ -259,6 +261,18 @@ def mamba2_decode(desc, state, cursor_in, cursor_out, x, z, B, C, dt_raw, dt_bia
         _ptr(dt_bias, torch.float32, "dt_bias"), _ptr(A, torch.float32, "A"), _ptr(D, torch.float32, "D"),
         _ptr(out, torch.float32, "out"), _ptr(err_flags, torch.int32, "err_flags"), _stream(stream))
     _check(st, "replayssm_mamba2_decode")
+
+
+def mamba2_decode_state_and_output(desc, state, cursor_in, cursor_out, x, z, B, C, dt_raw, dt_bias, A, D, out,
+                                   err_flags=None, stream=None):
+    io = desc.torch_io
+    st = lib().replayssm_mamba2_decode_state_and_output(
+        ctypes.byref(desc.c()), ctypes.byref(state.c()),
+        _ptr(cursor_in, torch.int32, "cursor_in"), _ptr(cursor_out, torch.int32, "cursor_out"),
+        _ptr(x, io, "x"), _ptr(z, io, "z"), _ptr(B, io, "B"), _ptr(C, io, "C"), _ptr(dt_raw, io, "dt_raw"),
+        _ptr(dt_bias, torch.float32, "dt_bias"), _ptr(A, torch.float32, "A"), _ptr(D, torch.float32, "D"),
+        _ptr(out, torch.float32, "out"), _ptr(err_flags, torch.int32, "err_flags"), _stream(stream))
+    _check(st, "replayssm_mamba2_decode_state_and_output")
 
 
 def mamba2_flush(desc, state, cursor_in, cursor_out, A, err_flags=None, stream=None):

@@ -150,6 +150,27 @@ replayssm_status replayssm_mamba2_decode(const replayssm_mamba2_desc* desc,
                                          float* out, int32_t* err_flags, hipStream_t stream);
 
 /*
+ * The same decode step by the state-and-output route (named beside the default
+ * output-only route in "Core implementation files"; the pages give no formula for it).
+ * Every step rebuilds the current state in registers,
+ *   h = decay * ckpt + sum_s w_s outer(x_s, B_s)   over the window of c + 1 records,
+ * and reads the output from it: y = h . C_t + D[h] x_t, out = y * z * sigmoid(z).  Only
+ * the step that fills the buffer (c + 1 == L) stores h as the new checkpoint (and
+ * refreshes ckpt_lp); other steps append their record and store no state.  Cursor,
+ * record and error rules, arguments and shapes are those of replayssm_mamba2_decode;
+ * it reads the fp32 checkpoint on every step (ckpt_lp is only refreshed).  The two
+ * routes give the same outputs up to rounding and may be mixed from step to step.
+ */
+replayssm_status replayssm_mamba2_decode_state_and_output(const replayssm_mamba2_desc* desc,
+                                                          const replayssm_mamba2_state* state,
+                                                          const int32_t* cursor_in, int32_t* cursor_out,
+                                                          const void* x, const void* z, const void* B,
+                                                          const void* C, const void* dt_raw,
+                                                          const float* dt_bias, const float* A,
+                                                          const float* D, float* out, int32_t* err_flags,
+                                                          hipStream_t stream);
+
+/*
  * Fold the 0..L-1 records each sequence holds into its checkpoint (same fold as
  * the flush step, over the stored records only), refresh ckpt_lp when it is set,
  * and set cursor_out[b] = 0.  With c = 0 the checkpoint is left bit-unchanged and
