@@ -27,10 +27,12 @@ Modules:
 * ``oracle.mamba2`` -- conventional recurrence, replay form, speculative cursor
   model.
 * ``oracle.gdn`` -- gated delta rule, conventional and replay form.
+* ``oracle.readcopy`` -- the low-precision read copies of the checkpoint (bf16,
+  fp16, and E4M3 fp8 with row scales).
 
 Every function's pins (closed forms, invariants, brute force) live in
 ``tests/test_oracle_*.py``. Functions with no such pin would be marked "parity
 unpinned" here; at present every function has at least one pin.
 """
 
-from . import gdn, mamba2  # noqa: F401
+from . import gdn, mamba2, readcopy  # noqa: F401
