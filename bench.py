@@ -15,11 +15,11 @@ source, else null.  ``cpu_baseline`` times the fp64 CPU oracle (replay form) on 
 sample of the same workload and checks the GPU outputs for that sample.
 
 Measured beside the headline, each with its own timed region: the in-library
-conventional read-update-write kernel on the same inputs, the bf16 read copy, the
-state-and-output decode route, the B=256/H=64 layer, speculative verification (4
-positions, commit) against the per-position snapshot baseline, and the Gated DeltaNet
-layer (replay decode and conventional; speculative verification against its snapshot
-baseline).  ``ceiling`` reports plain device read and copy bandwidth.
+conventional read-update-write kernel on the same inputs, the bf16, fp16 and fp8 read
+copies, the state-and-output decode route, the B=256/H=64 layer, speculative
+verification (4 positions, commit) against the per-position snapshot baseline, and the
+Gated DeltaNet layer (replay decode and conventional; speculative verification against
+its snapshot baseline).  ``ceiling`` reports plain device read and copy bandwidth.
 
 Auxiliary modes used to make the committed rocprofv3 summaries:
     --calibrate-copy        also run a plain 1 GiB device copy (counter calibration)
@@ -64,13 +64,22 @@ def kernel_source_hash():
 # algorithmic byte models (what the method must move per launch)
 # ------------------------------------------------------------------------------------
 
+def lp_copy_bytes(P, N, lowp):
+    """Bytes of one head's read copy: 2 per element (bf16, fp16), or 1 per element plus
+    a 4-byte scale per row (fp8)."""
+    kind = "bf16" if lowp is True else lowp
+    if not kind:
+        return 0
+    return P * N + 4 * P if kind == "fp8" else 2 * P * N
+
+
 def mamba2_replay_bytes(B, H, P, N, G, L, io, c, lowp=False):
     """One decode step for B sequences all at cursor c (records stored before it)."""
     fold = c + 1 == L
     if fold:
-        state = P * N * 4 * 2 + (P * N * 2 if lowp else 0)
+        state = P * N * 4 * 2 + lp_copy_bytes(P, N, lowp)
     else:
-        state = P * N * (2 if lowp else 4)
+        state = lp_copy_bytes(P, N, lowp) if lowp else P * N * 4
     per_h = state + 2 * P * io + io + P * 4 + c * (P * io + 4) + (0 if fold else P * io + 4)
     per_g = 2 * N * io + c * N * io + (0 if fold else N * io)
     return B * H * per_h + B * G * per_g
@@ -86,9 +95,9 @@ def spec_round_bytes(H, P, N, G, L, io, T, committed, lowp=False):
     for cm in committed:
         fold = cm + T > L
         if fold:
-            state = 2 * P * N * 4 + (P * N * 2 if lowp else 0)
+            state = 2 * P * N * 4 + lp_copy_bytes(P, N, lowp)
         else:
-            state = P * N * (2 if lowp else 4)
+            state = lp_copy_bytes(P, N, lowp) if lowp else P * N * 4
         per_h = state + T * (2 * P * io + io + P * 4) + cm * (P * io + 4) + T * (P * io + 4)
         per_g = T * 2 * N * io + cm * N * io + T * N * io
         tot += H * per_h + G * per_g
@@ -203,7 +212,7 @@ class Mamba2Bench:
             self.cur = [torch.zeros(self.B, dtype=torch.int32, device=dev) for _ in range(2)]
             d, s = self.desc.c(), self.state.c()
             self._keep = [d, s]
-            if lowp:  # create the bf16 read copy: a flush of the empty buffer (cursors stay 0)
+            if lowp:  # create the read copy: a flush of the empty buffer (cursors stay 0)
                 rs.mamba2_flush(self.desc, self.state, self.cur[0], self.cur[1], self.A, self.err)
             self.args = []
             for i in range(2 * pool):
@@ -647,7 +656,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1024, help="timed decode steps of the headline")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--only", default="all",
-                    help="all, headline, or a comma list of: conventional,bf16,so,h64,spec,gdn,gdn_spec")
+                    help="all, headline, or a comma list of: conventional,bf16,f16,fp8,so,h64,spec,gdn,gdn_spec")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--cpu-steps", type=int, default=32)
@@ -698,7 +707,7 @@ def main(argv=None):
 
     variants = {}
     conv = None
-    groups = {"conventional", "bf16", "so", "h64", "spec", "gdn", "gdn_spec"} if args.only == "all" else \
+    groups = {"conventional", "bf16", "f16", "fp8", "so", "h64", "spec", "gdn", "gdn_spec"} if args.only == "all" else \
         set() if args.only == "headline" else set(args.only.split(","))
     if "conventional" in groups:
         conv, _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup, conventional=True)
@@ -708,6 +717,11 @@ def main(argv=None):
         variants["mamba2_h128_bf16_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup,
                                                            lowp=True)
         torch.cuda.empty_cache()
+    for kind in ("f16", "fp8"):
+        if kind in groups:
+            variants[f"mamba2_h128_{kind}_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps,
+                                                                  args.warmup, lowp=kind)
+            torch.cuda.empty_cache()
     if "so" in groups:
         variants["mamba2_h128_state_and_output"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps,
                                                                   args.warmup, state_and_output=True)

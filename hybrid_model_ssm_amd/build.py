@@ -24,11 +24,14 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libreplayssm.so")
 
 # (source, object name, extra defines); the Mamba2 kernel templates are instantiated in
-# slices (io dtype x replay mode, and the conventional kernels) that compile in parallel.
+# slices (io dtype x replay mode x read copy, and the conventional kernels) that compile
+# in parallel.
 SOURCES = [("api.cpp", "api", []), ("mamba2_launch.hip", "mamba2_launch", []),
            ("gdn_kernels.hip", "gdn_kernels", []), ("cursor_kernels.hip", "cursor_kernels", [])]
-SOURCES += [("mamba2_inst.hip", f"mamba2_inst_io{io}_part{part}", [f"-DRSSM_IO={io}", f"-DRSSM_PART={part}"])
-            for io in (0, 1) for part in (0, 1, 2, 3, 4)]
+SOURCES += [("mamba2_inst.hip", f"mamba2_inst_io{io}_part{part}_lp{lp}",
+             [f"-DRSSM_IO={io}", f"-DRSSM_PART={part}", f"-DRSSM_LP={lp}"])
+            for io in (0, 1) for part in (0, 1, 2, 3) for lp in (0, 1, 2, 3)]
+SOURCES += [("mamba2_inst.hip", f"mamba2_inst_io{io}_conv", [f"-DRSSM_IO={io}", "-DRSSM_PART=4"]) for io in (0, 1)]
 ARCH = "gfx950"
 
 

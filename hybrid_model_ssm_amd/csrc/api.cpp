@@ -38,7 +38,13 @@ replayssm_status check_mamba2_state(const replayssm_mamba2_desc* d, const replay
     REQ(aligned(s->ckpt, 16) && aligned(s->rec_x, 16) && aligned(s->rec_B, 16) && aligned(s->rec_dt, 4));
     REQ(s->ckpt_lp == nullptr || aligned(s->ckpt_lp, 16));
     REQ(s->ckpt_lp != (void*)s->ckpt);
-    (void)d;
+    if (s->ckpt_lp != nullptr) {
+        REQ(s->lp_dtype == REPLAYSSM_BF16 || s->lp_dtype == REPLAYSSM_F16 || s->lp_dtype == REPLAYSSM_FP8_E4M3);
+        if (s->lp_dtype == REPLAYSSM_FP8_E4M3) {
+            REQ(s->lp_scale != nullptr && aligned(s->lp_scale, 4));
+            if (d->dstate % 16 != 0) return REPLAYSSM_ERR_UNSUPPORTED;
+        }
+    }
     return REPLAYSSM_OK;
 }
 
@@ -53,6 +59,12 @@ replayssm_status check_mamba2_inputs(const replayssm_mamba2_desc* d, const void*
     return REPLAYSSM_OK;
 }
 
+// kind of read copy for the kernels: 0 none, 1 bf16, 2 fp16, 3 fp8
+int lp_kind(const replayssm_mamba2_state* s) {
+    if (s->ckpt_lp == nullptr) return 0;
+    return s->lp_dtype == REPLAYSSM_BF16 ? 1 : s->lp_dtype == REPLAYSSM_F16 ? 2 : 3;
+}
+
 // The replay kernel stages one head's window and the group's records in LDS.
 bool replay_fits(const replayssm_mamba2_desc* d, int n_pos) {
     const size_t bytes = rssm::mamba2_replay_smem_bytes(d->headdim, d->dstate, d->nheads / d->ngroups,
@@ -63,7 +75,8 @@ bool replay_fits(const replayssm_mamba2_desc* d, int n_pos) {
 rssm::Mamba2Args mamba2_args(const replayssm_mamba2_desc* d, const replayssm_mamba2_state* s) {
     rssm::Mamba2Args a{};
     a.ckpt = s->ckpt;
-    a.ckpt_lp = static_cast<uint16_t*>(s->ckpt_lp);
+    a.ckpt_lp = s->ckpt_lp;
+    a.lp_scale = s->lp_scale;
     a.rec_x = s->rec_x;
     a.rec_B = s->rec_B;
     a.rec_dt = s->rec_dt;
@@ -150,7 +163,7 @@ static replayssm_status mamba2_decode_route(int mode, const replayssm_mamba2_des
     a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
     a.n_pos = 1;
-    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, mode, stream));
+    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, lp_kind(state), mode, stream));
 }
 
 extern "C" {
@@ -207,7 +220,7 @@ replayssm_status replayssm_mamba2_flush(const replayssm_mamba2_desc* desc,
     a.A = A;
     a.err_flags = err_flags;
     a.n_pos = 0;
-    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, 1, stream));
+    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, lp_kind(state), 1, stream));
 }
 
 replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
@@ -235,7 +248,7 @@ replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
     a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
     a.n_pos = n_pos;
-    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, 2, stream));
+    return hip_status(rssm::launch_mamba2_replay(a, desc->io_dtype, lp_kind(state), 2, stream));
 }
 
 replayssm_status replayssm_commit(int32_t batch, int32_t buffer_len, int32_t n_pos, int32_t* head,

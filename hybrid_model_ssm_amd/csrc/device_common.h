@@ -76,6 +76,72 @@ __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 v) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Low-precision read copies of the checkpoint ("ReplaySSM" README, benefit "Separate
+// state precisions": non-flush steps read a low-precision copy, flushes read and write
+// the fp32 checkpoint and refresh the copy).
+//   bf16, fp16   round to nearest even from the fp32 checkpoint
+//   fp8 e4m3     OCP 8-bit float (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+//                largest finite 448, code 0x7f/0xff not a number) with one fp32 scale per
+//                checkpoint row: scale = amax / 448, code = e4m3(h * (448 / amax)) rounded
+//                to nearest even (a zero row has scale 0 and codes 0)
+// ---------------------------------------------------------------------------------------
+constexpr int kLpNone = 0;
+constexpr int kLpBF16 = 1;
+constexpr int kLpF16 = 2;
+constexpr int kLpFP8 = 3;
+
+typedef _Float16 rssm_h2 __attribute__((ext_vector_type(2)));
+
+// two fp16 values in one 32-bit word -> float2 (low half first)
+__device__ __forceinline__ float2 f16x2_bits_to_f32(uint32_t w) {
+    const rssm_h2 h = __builtin_bit_cast(rssm_h2, w);
+    return make_float2((float)h.x, (float)h.y);
+}
+
+__device__ __forceinline__ uint2 f32x4_to_f16x4(float4 v) {
+    rssm_h2 a, b;
+    a.x = (_Float16)v.x; a.y = (_Float16)v.y;   // round to nearest even
+    b.x = (_Float16)v.z; b.y = (_Float16)v.w;
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+// Two e4m3 codes (bits 0-7 and 8-15 of the result's source pair) turned into fp16 bit
+// patterns whose values are 2^-8 times the e4m3 values: the sign goes to bit 15 and
+// the 7 exponent/mantissa bits to bits 7-13, which re-biases the exponent from 7 to 15
+// (normal and subnormal codes alike).  x holds code0 << 8 | code1 << 24.
+__device__ __forceinline__ uint32_t e4m3_pair_to_f16_bits(uint32_t x) {
+    return (x & 0x80008000u) | ((x >> 1) & 0x3f803f80u);
+}
+
+// four e4m3 codes (little-endian bytes of w) -> 2^-8 times their values
+__device__ __forceinline__ float4 e4m3x4_to_f32x4_scaled(uint32_t w) {
+    const uint32_t lo = ((w & 0xffu) << 8) | ((w & 0xff00u) << 16);
+    const uint32_t hi = ((w >> 8) & 0xff00u) | (w & 0xff000000u);
+    const float2 a = f16x2_bits_to_f32(e4m3_pair_to_f16_bits(lo));
+    const float2 b = f16x2_bits_to_f32(e4m3_pair_to_f16_bits(hi));
+    return make_float4(a.x, a.y, b.x, b.y);
+}
+
+// e4m3 code of x rounded to nearest even, saturated to +-448
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fminf(fabsf(x), 448.0f);
+    uint32_t m;
+    if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+        m = (uint32_t)__builtin_rintf(a * 512.0f);   // 8 becomes the smallest normal code
+    } else {                                   // keep 3 mantissa bits, re-bias 127 -> 7
+        const uint32_t u = __float_as_uint(a);
+        m = ((u + 0x7ffffu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+    }
+    return sign | m;
+}
+
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float4 v, float inv) {
+    return f32_to_e4m3(v.x * inv) | (f32_to_e4m3(v.y * inv) << 8) | (f32_to_e4m3(v.z * inv) << 16) |
+           (f32_to_e4m3(v.w * inv) << 24);
+}
+
+// ---------------------------------------------------------------------------------------
 // Streaming (non-temporal) accesses for data touched once per launch -- the checkpoint
 // stream.  They keep the checkpoint from displacing the small, reused vectors (records,
 // B/C) in the caches.
@@ -100,6 +166,13 @@ __device__ __forceinline__ uint4 ld_stream8(const uint16_t* p) {
 __device__ __forceinline__ void st_stream(float* p, float4 v) {
     rssm_v4f t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<rssm_v4f*>(p));
+}
+__device__ __forceinline__ void st_stream(uint8_t* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
+    const rssm_v4u t = __builtin_nontemporal_load(reinterpret_cast<const rssm_v4u*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
 }
 __device__ __forceinline__ void st_stream(uint16_t* p, uint2 v) {
     rssm_v2u t = {v.x, v.y};
@@ -180,6 +253,25 @@ __device__ __forceinline__ float group_allreduce(float x, int lane) {
     if constexpr (W >= 8) x = exchange<4>(x, x, lane);
     if constexpr (W >= 4) x = exchange<2>(x, x, lane);
     if constexpr (W >= 2) x = exchange<1>(x, x, lane);
+    return x;
+}
+
+// Maximum over an aligned group of W lanes, returned to all of them (same partners as
+// group_allreduce).
+template <int W>
+__device__ __forceinline__ float group_allmax(float x, int lane) {
+    if constexpr (W >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (W >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (W >= 16) x = fmaxf(x, dpp_mov<0x128>(x));
+    if constexpr (W >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
+    if constexpr (W >= 4) x = fmaxf(x, dpp_mov<0x4E>(x));
+    if constexpr (W >= 2) x = fmaxf(x, dpp_mov<0xB1>(x));
     return x;
 }
 

@@ -10,7 +10,8 @@ enum IoType { kIoF32 = 0, kIoBF16 = 1 };
 
 struct Mamba2Args {
     float* ckpt;          // [B,H,P,N] f32
-    uint16_t* ckpt_lp;    // [B,H,P,N] bf16 or null
+    void* ckpt_lp;        // [B,H,P,N] low-precision read copy (bf16, fp16 or fp8) or null
+    float* lp_scale;      // [B,H,P] row scales of an fp8 copy
     void* rec_x;          // [B,H,L,P] io
     void* rec_B;          // [B,G,L,N] io
     float* rec_dt;        // [B,H,L]
@@ -80,7 +81,8 @@ size_t mamba2_max_smem_bytes();
 
 // mode: 0 = AR decode step, 1 = fold stored records only (flush), 2 = speculative verify,
 //       3 = AR decode step by the state-and-output route
-hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int mode, hipStream_t stream);
+// lp: kind of read copy (0 none, 1 bf16, 2 fp16, 3 fp8 with row scales)
+hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int lp, int mode, hipStream_t stream);
 hipError_t launch_mamba2_conventional(const Mamba2ConvArgs& a, int io, bool snapshots,
                                       hipStream_t stream);
 

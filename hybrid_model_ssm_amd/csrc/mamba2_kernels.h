@@ -61,15 +61,15 @@ struct Mamba2Tile {
     static_assert(R >= 1 && R <= LPR && (R & (R - 1)) == 0, "tile shape");
 };
 
-// Mapping of a tile read from the bf16 copy: 16-byte loads of 8 elements, N/8 lanes
-// per row.
-template <int P, int N>
+// Mapping of a tile read from a low-precision copy: 16-byte loads of EPL elements
+// (8 for bf16/fp16, 16 for fp8), N/EPL lanes per row.
+template <int P, int N, int EPL>
 struct Mamba2TileLp {
-    static constexpr int LPR = N / 8;
+    static constexpr int LPR = N / EPL;
     static constexpr int RPP = kThreads / LPR;
     static constexpr int R = (P + RPP - 1) / RPP;
     static constexpr bool MASK = (P % RPP) != 0;
-    static_assert(R >= 1 && R <= LPR && (R & (R - 1)) == 0, "bf16 tile shape");
+    static_assert(R >= 1 && R <= LPR && (R & (R - 1)) == 0, "low-precision tile shape");
 };
 
 // LDS layout of the replay kernel (in 4-byte words).
@@ -97,8 +97,10 @@ struct GroupSmem {
     }
 };
 
-template <int P, int N, typename IO, bool LOWP, int MODE>
+// LP: kind of low-precision read copy (kLpNone, kLpBF16, kLpF16, kLpFP8)
+template <int P, int N, typename IO, int LP, int MODE>
 __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
+    constexpr bool LOWP = LP != kLpNone;
     using io = Io<IO>;
     using Raw4 = typename io::Raw4;
     using Tl = Mamba2Tile<P, N>;
@@ -215,16 +217,28 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 if (!MASK || row0 + k * RPP < P) v[k] = ld_stream(a.ckpt + t + (size_t)k * RPP * N);
         }
     };
-    // tiles of the bf16 read copy (non-flush steps with LOWP), in their own mapping
-    using Tq = Mamba2TileLp<P, N>;
+    // tiles of the low-precision read copy (non-flush steps with LOWP), in their own
+    // mapping; with fp8, also the scale of the row each lane writes
+    constexpr int EPL = (LP == kLpFP8) ? 16 : 8;
+    using Tq = Mamba2TileLp<P, N, EPL>;
     constexpr int RQ = Tq::R;
+    constexpr int TBQ = (MODE == kSpec) ? Tq::LPR / RQ : 1;   // positions per reduce
     const int rowq0 = tid / Tq::LPR;
     const int colq = tid % Tq::LPR;
-    auto issue_tile_lp = [&](int hl, uint4 (&v)[RQ]) {
-        const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)rowq0 * N + 8 * colq;
+    // the row this lane writes after the transpose-reduce (fixed for the whole call)
+    const int pq = rowq0 + ((colq / (Tq::LPR / (RQ * TBQ))) % RQ) * Tq::RPP;
+    auto issue_tile_lp = [&](int hl, uint4 (&v)[RQ], float& sc) {
+        const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)rowq0 * N + EPL * colq;
 #pragma unroll
-        for (int k = 0; k < RQ; ++k)
-            if (!Tq::MASK || rowq0 + k * Tq::RPP < P) v[k] = ld_stream8(a.ckpt_lp + t + (size_t)k * Tq::RPP * N);
+        for (int k = 0; k < RQ; ++k) {
+            if (!Tq::MASK || rowq0 + k * Tq::RPP < P) {
+                if constexpr (LP == kLpFP8)
+                    v[k] = ld_stream16(reinterpret_cast<const uint8_t*>(a.ckpt_lp) + t + (size_t)k * Tq::RPP * N);
+                else
+                    v[k] = ld_stream8(reinterpret_cast<const uint16_t*>(a.ckpt_lp) + t + (size_t)k * Tq::RPP * N);
+            }
+        }
+        if constexpr (LP == kLpFP8) sc = a.lp_scale[(bH + h0 + hl) * P + min(pq, P - 1)];
     };
     // fold rows of head hl: x_s[p] for s < nf, as 4-element chunks
     Raw4 xf[kFoldXPerThread];
@@ -241,7 +255,8 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
 
     float4 va[R], vb[R];
     uint4 qa[RQ], qb[RQ];
-    if (use_lp) issue_tile_lp(0, qa);
+    float sqa = 0.f, sqb = 0.f;
+    if (use_lp) issue_tile_lp(0, qa, sqa);
     else issue_tile(0, va);
     if (fold && !idle) issue_foldx(0);
 
@@ -441,25 +456,39 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
         for (int k = 0; k < R; ++k) va[k] = vb[k];
     };
 
-    // outputs of head hl from a bf16-copy tile: same arithmetic as `outputs`, in the
-    // 8-elements-per-lane mapping
-    auto outputs_lp = [&](int hl, const uint4 (&v)[RQ]) {
-        if constexpr (MODE != kFold) {
+    // outputs of head hl from a low-precision tile: same arithmetic as `outputs`, in the
+    // EPL-elements-per-lane mapping.  fp8 tiles decode to 2^-8 times the code values; the
+    // row scale (times 2^8) multiplies the reduced row.
+    auto lp_dot = [&](const uint4& v, int j) -> float {
+        const float* c = sC + j * N + EPL * colq;
+        const float4 C0 = *reinterpret_cast<const float4*>(c);
+        const float4 C1 = *reinterpret_cast<const float4*>(c + 4);
+        if constexpr (LP == kLpBF16) {
+            return dot4(bf16x4_to_f32x4(make_uint2(v.x, v.y)), C0) + dot4(bf16x4_to_f32x4(make_uint2(v.z, v.w)), C1);
+        } else if constexpr (LP == kLpF16) {
+            const float2 e0 = f16x2_bits_to_f32(v.x), e1 = f16x2_bits_to_f32(v.y);
+            const float2 e2 = f16x2_bits_to_f32(v.z), e3 = f16x2_bits_to_f32(v.w);
+            return dot4(make_float4(e0.x, e0.y, e1.x, e1.y), C0) + dot4(make_float4(e2.x, e2.y, e3.x, e3.y), C1);
+        } else {
+            const float4 C2 = *reinterpret_cast<const float4*>(c + 8);
+            const float4 C3 = *reinterpret_cast<const float4*>(c + 12);
+            return dot4(e4m3x4_to_f32x4_scaled(v.x), C0) + dot4(e4m3x4_to_f32x4_scaled(v.y), C1) +
+                   dot4(e4m3x4_to_f32x4_scaled(v.z), C2) + dot4(e4m3x4_to_f32x4_scaled(v.w), C3);
+        }
+    };
+    auto outputs_lp = [&](int hl, const uint4 (&v)[RQ], float sc) {
+        if constexpr (MODE != kFold && LOWP) {
             constexpr int LQ = Tq::LPR;
-            constexpr int TBQ = (MODE == kSpec) ? LQ / RQ : 1;
             const int h = h0 + hl;
             const int qq = tid % LQ;
+            const float rs = (LP == kLpFP8) ? sc * 256.0f : 1.0f;
             for (int j0 = 0; j0 < T; j0 += TBQ) {
                 float acc[RQ * TBQ];
 #pragma unroll
                 for (int jj = 0; jj < TBQ; ++jj) {
                     const int j = min(j0 + jj, T - 1);
-                    const float4 C0 = *reinterpret_cast<const float4*>(sC + j * N + 8 * colq);
-                    const float4 C1 = *reinterpret_cast<const float4*>(sC + j * N + 8 * colq + 4);
 #pragma unroll
-                    for (int k = 0; k < RQ; ++k)
-                        acc[jj * RQ + k] = dot4(bf16x4_to_f32x4(make_uint2(v[k].x, v[k].y)), C0) +
-                                           dot4(bf16x4_to_f32x4(make_uint2(v[k].z, v[k].w)), C1);
+                    for (int k = 0; k < RQ; ++k) acc[jj * RQ + k] = lp_dot(v[k], j);
                 }
                 const float r = row_reduce<RQ * TBQ, LQ>(acc, lane);
                 const int vi = qq / (LQ / (RQ * TBQ));
@@ -467,7 +496,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 const int p = rowq0 + (vi % RQ) * Tq::RPP;
                 if ((qq % (LQ / (RQ * TBQ))) == 0 && j < T && (!Tq::MASK || p < P)) {
                     const int o = (hl * T1 + j) * P + p;
-                    a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
+                    a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * (rs * r) + sY[o], io::ld(sZ, o));
                 }
             }
         }
@@ -476,12 +505,13 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     if (!fold && use_lp) {
         // tile hl+1 is loaded while head hl is reduced
         for (int hl = 0; hl + 1 < nh; ++hl) {
-            issue_tile_lp(hl + 1, qb);
-            outputs_lp(hl, qa);
+            issue_tile_lp(hl + 1, qb, sqb);
+            outputs_lp(hl, qa, sqa);
 #pragma unroll
             for (int k = 0; k < RQ; ++k) qa[k] = qb[k];
+            sqa = sqb;
         }
-        outputs_lp(nh - 1, qa);
+        outputs_lp(nh - 1, qa, sqa);
     } else if (!fold) {
         // tile hl+1 is loaded while head hl is reduced
         for (int hl = 0; hl + 1 < nh; ++hl) {
@@ -525,10 +555,29 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
             const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
 #pragma unroll
             for (int k = 0; k < R; ++k) {
+                // fp8 copy: the row's largest magnitude over its LPR lanes (every lane
+                // takes part; rows past P are never stored)
+                float amax = 0.f;
+                if constexpr (LP == kLpFP8) {
+                    if (store_lp) {
+                        amax = fmaxf(fmaxf(fabsf(va[k].x), fabsf(va[k].y)), fmaxf(fabsf(va[k].z), fabsf(va[k].w)));
+                        amax = group_allmax<LPR>(amax, lane);
+                    }
+                }
                 if (!MASK || row0 + k * RPP < P) {
                     const size_t off = t + (size_t)k * RPP * N;
                     if (!keep_ckpt) st_stream(a.ckpt + off, va[k]);
-                    if (store_lp) st_stream(a.ckpt_lp + off, f32x4_to_bf16x4(va[k]));
+                    if (store_lp) {
+                        if constexpr (LP == kLpBF16) {
+                            st_stream(reinterpret_cast<uint16_t*>(a.ckpt_lp) + off, f32x4_to_bf16x4(va[k]));
+                        } else if constexpr (LP == kLpF16) {
+                            st_stream(reinterpret_cast<uint16_t*>(a.ckpt_lp) + off, f32x4_to_f16x4(va[k]));
+                        } else if constexpr (LP == kLpFP8) {
+                            const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+                            st_stream(reinterpret_cast<uint8_t*>(a.ckpt_lp) + off, f32x4_to_e4m3x4(va[k], inv));
+                            if (col4 == 0) a.lp_scale[(bH + h0 + hl) * P + row0 + k * RPP] = amax / 448.0f;
+                        }
+                    }
                 }
             }
             outputs(hl, va);

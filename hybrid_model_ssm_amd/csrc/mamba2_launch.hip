@@ -33,25 +33,20 @@ size_t mamba2_replay_smem_bytes(int P, int N, int hpg, int L, int n_pos, int io_
 
 size_t mamba2_max_smem_bytes() { return 64 * 1024; }
 
-static const void* find_replay(int P, int N, int io, bool lowp, int mode) {
-    if (io == kIoBF16) {
-        if (mode == kDecode) return replay_kernel_ptr_io1_mode0(P, N, lowp);
-        if (mode == kFold) return replay_kernel_ptr_io1_mode1(P, N, lowp);
-        if (mode == kSpec) return replay_kernel_ptr_io1_mode2(P, N, lowp);
-        return replay_kernel_ptr_io1_mode3(P, N, lowp);
-    }
-    if (mode == kDecode) return replay_kernel_ptr_io0_mode0(P, N, lowp);
-    if (mode == kFold) return replay_kernel_ptr_io0_mode1(P, N, lowp);
-    if (mode == kSpec) return replay_kernel_ptr_io0_mode2(P, N, lowp);
-    return replay_kernel_ptr_io0_mode3(P, N, lowp);
+static const void* find_replay(int P, int N, int io, int lp, int mode) {
+#define RSSM_PICK(IO, MODE, LP) \
+    if (io == IO && mode == MODE && lp == LP) return RSSM_REPLAY_PTR_NAME(IO, MODE, LP)(P, N);
+    RSSM_REPLAY_SLICES(RSSM_PICK)
+#undef RSSM_PICK
+    return nullptr;
 }
 
 static const void* find_conv(int P, int N, int io, bool snap) {
     return io == kIoBF16 ? conv_kernel_ptr_io1(P, N, snap) : conv_kernel_ptr_io0(P, N, snap);
 }
 
-hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int mode, hipStream_t stream) {
-    const void* fn = find_replay(a.headdim, a.dstate, io, a.ckpt_lp != nullptr, mode);
+hipError_t launch_mamba2_replay(const Mamba2Args& a, int io, int lp, int mode, hipStream_t stream) {
+    const void* fn = find_replay(a.headdim, a.dstate, io, a.ckpt_lp != nullptr ? lp : 0, mode);
     if (!fn) return hipErrorInvalidValue;
     Mamba2Args args = a;
     chunking(a.nheads / a.ngroups, &args.nchunk, &args.heads_per_chunk);

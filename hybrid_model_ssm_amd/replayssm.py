@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("REPLAYSSM_LIB") or os.path.join(_HERE, "libreplayssm.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
-F32, BF16 = 0, 1
+F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 DEVERR_CURSOR = 1
 MAX_BUFFER_LEN = 64
 
@@ -55,7 +55,8 @@ class Mamba2DescC(ctypes.Structure):
 
 class Mamba2StateC(ctypes.Structure):
     _fields_ = [("ckpt", ctypes.c_void_p), ("ckpt_lp", ctypes.c_void_p), ("rec_x", ctypes.c_void_p),
-                ("rec_B", ctypes.c_void_p), ("rec_dt", ctypes.c_void_p)]
+                ("rec_B", ctypes.c_void_p), ("rec_dt", ctypes.c_void_p), ("lp_dtype", ctypes.c_int32),
+                ("lp_scale", ctypes.c_void_p)]
 
 
 class GdnDescC(ctypes.Structure):
@@ -179,26 +180,41 @@ class Mamba2State:
     rec_B: torch.Tensor
     rec_dt: torch.Tensor
     ckpt_lp: torch.Tensor | None = None
+    lp_scale: torch.Tensor | None = None      # [B,H,P] f32 row scales of an fp8 copy
 
     @staticmethod
     def allocate(desc: Mamba2Desc, device="cuda", lowp=False, ckpt=None):
+        """``lowp``: False (no read copy), True or "bf16", "f16", or "fp8" (e4m3 codes
+        as uint8 with f32 row scales)."""
         B, H, P, N, G, L = desc.batch, desc.nheads, desc.headdim, desc.dstate, desc.ngroups, desc.buffer_len
         io = desc.torch_io
         if ckpt is None:
             ckpt = torch.zeros(B, H, P, N, dtype=torch.float32, device=device)
+        kind = "bf16" if lowp is True else (lowp or None)
+        if kind not in (None, "bf16", "f16", "fp8"):
+            raise ValueError(f"unknown read copy {lowp!r}")
+        lp_t = {"bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.uint8}.get(kind)
         return Mamba2State(
             ckpt=ckpt,
             rec_x=torch.zeros(B, H, L, P, dtype=io, device=device),
             rec_B=torch.zeros(B, G, L, N, dtype=io, device=device),
             rec_dt=torch.zeros(B, H, L, dtype=torch.float32, device=device),
-            ckpt_lp=torch.zeros(B, H, P, N, dtype=torch.bfloat16, device=device) if lowp else None,
+            ckpt_lp=torch.zeros(B, H, P, N, dtype=lp_t, device=device) if kind else None,
+            lp_scale=torch.zeros(B, H, P, dtype=torch.float32, device=device) if kind == "fp8" else None,
         )
+
+    @property
+    def lp_dtype(self):
+        if self.ckpt_lp is None:
+            return F32
+        return {torch.bfloat16: BF16, torch.float16: F16, torch.uint8: FP8_E4M3}[self.ckpt_lp.dtype]
 
     def c(self):
         return Mamba2StateC(_ptr(self.ckpt, torch.float32, "ckpt"),
-                            _ptr(self.ckpt_lp, torch.bfloat16, "ckpt_lp"),
+                            _ptr(self.ckpt_lp, None, "ckpt_lp"),
                             _ptr(self.rec_x, None, "rec_x"), _ptr(self.rec_B, None, "rec_B"),
-                            _ptr(self.rec_dt, torch.float32, "rec_dt"))
+                            _ptr(self.rec_dt, torch.float32, "rec_dt"), self.lp_dtype,
+                            _ptr(self.lp_scale, torch.float32, "lp_scale"))
 
 
 @dataclasses.dataclass

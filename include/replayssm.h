@@ -8,9 +8,10 @@
  * the checkpoint and the buffer without storing a state; when the buffer of L
  * records fills, the flush step folds the records into the checkpoint and stores it
  * once.  Speculative verification appends draft records and is output-only; rollback
- * moves a cursor ("ReplaySSM" README, benefit "Cheap rollback").  An optional bf16
- * read copy of the checkpoint serves non-flush reads while the fp32 checkpoint
- * carries the recurrence (same README, benefit "Separate state precisions").  The
+ * moves a cursor ("ReplaySSM" README, benefit "Cheap rollback").  An optional
+ * low-precision read copy of the checkpoint (bf16, fp16 or fp8) serves non-flush reads
+ * while the fp32 checkpoint carries the recurrence (same README, benefit "Separate
+ * state precisions").  The
  * entry points follow the kernels listed in "ReplaySSM (a vLLM research fork)",
  * section "Core implementation files".
  *
@@ -23,7 +24,7 @@
  *   and returns.  Buffers must stay alive until that stream work has finished.
  * - Arrays are dense and row-major with the last dimension contiguous, in the
  *   shapes written next to each argument ([batch, nheads, headdim] and so on).
- * - Alignment: the checkpoint and its bf16 copy must be 16-byte aligned; every
+ * - Alignment: the checkpoint and its read copy must be 16-byte aligned; every
  *   other array must be aligned to its element size.
  * - Errors: every entry point validates its arguments on the host before it touches
  *   the GPU.  On REPLAYSSM_ERR_INVALID_ARGUMENT or REPLAYSSM_ERR_UNSUPPORTED nothing
@@ -58,7 +59,9 @@ typedef enum {
 
 typedef enum {
     REPLAYSSM_F32 = 0,
-    REPLAYSSM_BF16 = 1
+    REPLAYSSM_BF16 = 1,
+    REPLAYSSM_F16 = 2,      /* read copies only */
+    REPLAYSSM_FP8_E4M3 = 3  /* read copies only: OCP 8-bit float with a scale per row */
 } replayssm_dtype;
 
 enum { REPLAYSSM_DEVERR_CURSOR = 1 };
@@ -100,12 +103,22 @@ typedef struct {
  * decode uses the slots circularly from `head`.
  *
  *   ckpt     f32  [batch, nheads, headdim, dstate]   fp32 checkpoint (required)
- *   ckpt_lp  bf16 [batch, nheads, headdim, dstate]   optional read copy, or NULL.
- *            When set, non-flush steps read it instead of ckpt; every flush reads
- *            ckpt, writes ckpt and refreshes ckpt_lp (round to nearest even).
+ *   ckpt_lp  lp   [batch, nheads, headdim, dstate]   optional read copy, or NULL.
+ *            When set, non-flush steps of the output-only route and of speculative
+ *            verification read it instead of ckpt; every flush reads ckpt, writes
+ *            ckpt and refreshes ckpt_lp ("ReplaySSM" README, benefit "Separate state
+ *            precisions": rounding of the copy never enters the recurrence).
  *   rec_x    io   [batch, nheads, buffer_len, headdim]   x records (exact copies)
  *   rec_B    io   [batch, ngroups, buffer_len, dstate]   B records (exact copies)
  *   rec_dt   f32  [batch, nheads, buffer_len]            dt after softplus
+ *   lp_dtype dtype of ckpt_lp (ignored when ckpt_lp is NULL):
+ *            REPLAYSSM_BF16, REPLAYSSM_F16  round to nearest even from ckpt;
+ *            REPLAYSSM_FP8_E4M3  OCP e4m3 (bias 7, 3 mantissa bits, largest 448, no
+ *            infinities) with one scale per row: lp_scale[b,h,p] = amax / 448 where
+ *            amax = max_n |ckpt[b,h,p,n]|, code = e4m3(ckpt * (448 / amax)) rounded
+ *            to nearest even; a zero row has scale 0 and zero codes.  The value read
+ *            is code * lp_scale.  dstate must be a multiple of 16.
+ *   lp_scale f32  [batch, nheads, headdim]   row scales of an fp8 copy (else NULL)
  */
 typedef struct {
     float* ckpt;
@@ -113,6 +126,8 @@ typedef struct {
     void* rec_x;
     void* rec_B;
     float* rec_dt;
+    replayssm_dtype lp_dtype;
+    float* lp_scale;
 } replayssm_mamba2_state;
 
 /*

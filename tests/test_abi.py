@@ -118,6 +118,18 @@ def test_mamba2_decode_rejects_bad_pointers(L):
     assert decode(L, err=fake(16) + 2, cout=fake(5)) == INV
 
 
+def test_mamba2_read_copy_kinds(L):
+    ok = dict(cout=fake(6))
+    # the read copy's dtype must name a read-copy format; fp8 needs its row scales
+    assert decode(L, state=m2state(ckpt_lp=fake(20), lp_dtype=rs.F32), **ok) == INV
+    assert decode(L, state=m2state(ckpt_lp=fake(20), lp_dtype=9), **ok) == INV
+    assert decode(L, state=m2state(ckpt_lp=fake(20), lp_dtype=rs.FP8_E4M3, lp_scale=None), **ok) == INV
+    assert decode(L, state=m2state(ckpt_lp=fake(20), lp_dtype=rs.FP8_E4M3, lp_scale=fake(21) + 2), **ok) == INV
+    # without a read copy its dtype and scales are ignored
+    assert decode(L, state=m2state(lp_dtype=9), x=None, **ok) == INV     # still rejected for x only
+    assert rs.Mamba2StateC.lp_dtype.offset == 40 and rs.Mamba2StateC.lp_scale.offset == 48
+
+
 def test_mamba2_window_limit_is_unsupported(L):
     # headdim 128 with L=64: one head's fold rows (headdim * L elements) exceed what the
     # replay kernel stages per head

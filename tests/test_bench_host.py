@@ -29,6 +29,19 @@ def test_mamba2_byte_model_headline():
     assert state_only == 1088
 
 
+def test_read_copy_byte_models():
+    # non-flush steps read 2 bytes per element (bf16, fp16) or 1 plus a 4-byte row scale (fp8)
+    f32 = bench.mamba2_replay_bytes(1, 1, 64, 128, 1, 16, 2, 3)
+    for kind, per_head in (("bf16", 2 * 64 * 128), ("f16", 2 * 64 * 128), ("fp8", 64 * 128 + 4 * 64)):
+        got = bench.mamba2_replay_bytes(1, 1, 64, 128, 1, 16, 2, 3, kind)
+        assert f32 - got == 4 * 64 * 128 - per_head
+        flush = bench.mamba2_replay_bytes(1, 1, 64, 128, 1, 16, 2, 15, kind)
+        assert flush - bench.mamba2_replay_bytes(1, 1, 64, 128, 1, 16, 2, 15) == per_head
+    avg = _window_avg(lambda c, L: bench.mamba2_replay_bytes(256, 128, 64, 128, 8, L, 2, c, "fp8"), 16)
+    # codes 256 MiB + row scales 8 MiB per read; the flush writes fp32 and the copy
+    assert avg == pytest.approx(15 / 16 * (256 + 8) + (2048 + 264) / 16 + 17.06 + 39.0, abs=0.1)
+
+
 def test_mamba2_byte_model_h64_and_gdn():
     assert _window_avg(lambda c, L: bench.mamba2_replay_bytes(256, 64, 64, 128, 8, L, 2, c), 16) == \
         pytest.approx(574.65, abs=0.01)
