@@ -306,11 +306,11 @@ def time_spec(torch, rs, synth, rounds, warmup, baseline=False, lowp=False):
         def launch(r):
             p = pool[r % pool_n]
             _check(Lb.replayssm_mamba2_spec_verify(ctypes.byref(d), ctypes.byref(s_c), head.data_ptr(), com.data_ptr(),
-                                                   T, *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
+                                                   T, None, *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
                                                    bias.data_ptr(), A.data_ptr(), D.data_ptr(), out.data_ptr(),
                                                    flushed.data_ptr(), err.data_ptr(), stream), "spec_verify")
             _check(Lb.replayssm_commit(B, L, T, head.data_ptr(), com.data_ptr(), flushed.data_ptr(),
-                                       keep_dev[r % pool_n].data_ptr(), err.data_ptr(), stream), "commit")
+                                       keep_dev[r % pool_n].data_ptr(), None, err.data_ptr(), stream), "commit")
         keep_state = [state, s_c]
     for r in range(warmup):
         launch(r)
@@ -446,10 +446,10 @@ def time_gdn_spec(torch, rs, synth, rounds, warmup, baseline=False):
         def launch(r):
             p = pool[r % pool_n]
             _check(Lb.replayssm_gdn_spec_verify(ctypes.byref(d), ctypes.byref(s_c), head.data_ptr(), com.data_ptr(), T,
-                                                *(p[k].data_ptr() for k in keys), out.data_ptr(), flushed.data_ptr(),
+                                                None, *(p[k].data_ptr() for k in keys), out.data_ptr(), flushed.data_ptr(),
                                                 err.data_ptr(), stream), "gdn_spec_verify")
             _check(Lb.replayssm_commit(B, L, T, head.data_ptr(), com.data_ptr(), flushed.data_ptr(),
-                                       keep_dev[r % pool_n].data_ptr(), err.data_ptr(), stream), "commit")
+                                       keep_dev[r % pool_n].data_ptr(), None, err.data_ptr(), stream), "commit")
         keep_state = [state, s_c]
     for r in range(warmup):
         launch(r)

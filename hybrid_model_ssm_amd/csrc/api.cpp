@@ -38,6 +38,10 @@ replayssm_status check_mamba2_state(const replayssm_mamba2_desc* d, const replay
     REQ(aligned(s->ckpt, 16) && aligned(s->rec_x, 16) && aligned(s->rec_B, 16) && aligned(s->rec_dt, 4));
     REQ(s->ckpt_lp == nullptr || aligned(s->ckpt_lp, 16));
     REQ(s->ckpt_lp != (void*)s->ckpt);
+    if (s->slot != nullptr) {
+        REQ(aligned(s->slot, 4) && s->num_slots >= 1);
+        REQ((int64_t)s->num_slots * d->nheads <= INT_MAX / REPLAYSSM_MAX_BUFFER_LEN);
+    }
     if (s->ckpt_lp != nullptr) {
         REQ(s->lp_dtype == REPLAYSSM_BF16 || s->lp_dtype == REPLAYSSM_F16 || s->lp_dtype == REPLAYSSM_FP8_E4M3);
         if (s->lp_dtype == REPLAYSSM_FP8_E4M3) {
@@ -77,6 +81,8 @@ rssm::Mamba2Args mamba2_args(const replayssm_mamba2_desc* d, const replayssm_mam
     a.ckpt = s->ckpt;
     a.ckpt_lp = s->ckpt_lp;
     a.lp_scale = s->lp_scale;
+    a.slot = s->slot;
+    a.num_slots = s->num_slots;
     a.rec_x = s->rec_x;
     a.rec_B = s->rec_B;
     a.rec_dt = s->rec_dt;
@@ -102,10 +108,14 @@ replayssm_status check_gdn_desc(const replayssm_gdn_desc* d, bool need_L) {
     return REPLAYSSM_OK;
 }
 
-replayssm_status check_gdn_state(const replayssm_gdn_state* s) {
+replayssm_status check_gdn_state(const replayssm_gdn_desc* d, const replayssm_gdn_state* s) {
     REQ(s && s->ckpt && s->rec_k && s->rec_v && s->rec_alpha && s->rec_beta);
     REQ(aligned(s->ckpt, 16) && aligned(s->rec_k, 16) && aligned(s->rec_v, 16) &&
         aligned(s->rec_alpha, 4) && aligned(s->rec_beta, 4));
+    if (s->slot != nullptr) {
+        REQ(aligned(s->slot, 4) && s->num_slots >= 1);
+        REQ((int64_t)s->num_slots * d->num_v_heads * 2 <= INT_MAX / REPLAYSSM_MAX_BUFFER_LEN);
+    }
     return REPLAYSSM_OK;
 }
 
@@ -128,6 +138,7 @@ rssm::GdnArgs gdn_args(const replayssm_gdn_desc* d, const replayssm_gdn_state* s
     if (s) {
         a.ckpt = s->ckpt; a.rec_k = s->rec_k; a.rec_v = s->rec_v;
         a.rec_alpha = s->rec_alpha; a.rec_beta = s->rec_beta;
+        a.slot = s->slot; a.num_slots = s->num_slots;
     }
     a.batch = d->batch;
     a.hv = d->num_v_heads;
@@ -178,7 +189,7 @@ const char* replayssm_status_string(replayssm_status status) {
     return "unknown status";
 }
 
-int32_t replayssm_version(void) { return 100; }
+int32_t replayssm_version(void) { return 200; }
 
 replayssm_status replayssm_mamba2_decode(const replayssm_mamba2_desc* desc,
                                          const replayssm_mamba2_state* state,
@@ -226,7 +237,8 @@ replayssm_status replayssm_mamba2_flush(const replayssm_mamba2_desc* desc,
 replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
                                               const replayssm_mamba2_state* state,
                                               const int32_t* head, const int32_t* committed,
-                                              int32_t n_pos, const void* x, const void* z,
+                                              int32_t n_pos, const int32_t* n_pos_seq, const void* x,
+                                              const void* z,
                                               const void* B, const void* C, const void* dt_raw,
                                               const float* dt_bias, const float* A, const float* D,
                                               float* out, int32_t* flushed, int32_t* err_flags,
@@ -240,11 +252,13 @@ replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
     REQ(head && committed && flushed && head != committed);
     REQ((const int32_t*)flushed != head && (const int32_t*)flushed != committed);
     REQ(aligned(head, 4) && aligned(committed, 4) && aligned(flushed, 4) && aligned(err_flags, 4));
+    REQ(aligned(n_pos_seq, 4));
     if (!replay_fits(desc, n_pos)) return REPLAYSSM_ERR_UNSUPPORTED;
     rssm::Mamba2Args a = mamba2_args(desc, state);
     a.cursor_in = head;
     a.committed = committed;
     a.flushed = flushed;
+    a.n_pos_seq = n_pos_seq;
     a.x = x; a.z = z; a.B = B; a.C = C; a.dt_raw = dt_raw;
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.out = out; a.err_flags = err_flags;
     a.n_pos = n_pos;
@@ -253,14 +267,14 @@ replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
 
 replayssm_status replayssm_commit(int32_t batch, int32_t buffer_len, int32_t n_pos, int32_t* head,
                                   int32_t* committed, const int32_t* flushed, const int32_t* n_keep,
-                                  int32_t* err_flags, hipStream_t stream) {
+                                  const int32_t* n_pos_seq, int32_t* err_flags, hipStream_t stream) {
     REQ(batch >= 1 && buffer_len >= 1 && buffer_len <= REPLAYSSM_MAX_BUFFER_LEN);
     REQ(n_pos >= 1 && n_pos <= buffer_len);
     REQ(head && committed && flushed && n_keep && head != committed);
     REQ(aligned(head, 4) && aligned(committed, 4) && aligned(flushed, 4) && aligned(n_keep, 4) &&
-        aligned(err_flags, 4));
+        aligned(err_flags, 4) && aligned(n_pos_seq, 4));
     return hip_status(rssm::launch_commit(batch, buffer_len, n_pos, head, committed, flushed, n_keep,
-                                          err_flags, stream));
+                                          n_pos_seq, err_flags, stream));
 }
 
 replayssm_status replayssm_reset_cursors(int32_t batch, int32_t* head, int32_t* cursor,
@@ -321,7 +335,7 @@ replayssm_status replayssm_gdn_decode(const replayssm_gdn_desc* desc, const repl
                                       hipStream_t stream) {
     replayssm_status st = check_gdn_desc(desc, true);
     if (st != REPLAYSSM_OK) return st;
-    if ((st = check_gdn_state(state)) != REPLAYSSM_OK) return st;
+    if ((st = check_gdn_state(desc, state)) != REPLAYSSM_OK) return st;
     if ((st = check_gdn_inputs(q, k, v, alpha, beta, out)) != REPLAYSSM_OK) return st;
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
@@ -337,7 +351,7 @@ replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const repla
                                      hipStream_t stream) {
     replayssm_status st = check_gdn_desc(desc, true);
     if (st != REPLAYSSM_OK) return st;
-    if ((st = check_gdn_state(state)) != REPLAYSSM_OK) return st;
+    if ((st = check_gdn_state(desc, state)) != REPLAYSSM_OK) return st;
     REQ(cursor_in && cursor_out && cursor_in != cursor_out);
     REQ(aligned(cursor_in, 4) && aligned(cursor_out, 4) && aligned(err_flags, 4));
     if (!gdn_fits(desc, 1, 0)) return REPLAYSSM_ERR_UNSUPPORTED;
@@ -348,23 +362,25 @@ replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const repla
 
 replayssm_status replayssm_gdn_spec_verify(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
                                            const int32_t* head, const int32_t* committed, int32_t n_pos,
-                                           const void* q, const void* k, const void* v,
-                                           const float* alpha, const float* beta, float* out,
+                                           const int32_t* n_pos_seq, const void* q, const void* k,
+                                           const void* v, const float* alpha, const float* beta, float* out,
                                            int32_t* flushed, int32_t* err_flags, hipStream_t stream) {
     replayssm_status st = check_gdn_desc(desc, true);
     if (st != REPLAYSSM_OK) return st;
-    if ((st = check_gdn_state(state)) != REPLAYSSM_OK) return st;
+    if ((st = check_gdn_state(desc, state)) != REPLAYSSM_OK) return st;
     if ((st = check_gdn_inputs(q, k, v, alpha, beta, out)) != REPLAYSSM_OK) return st;
     REQ(n_pos >= 1 && n_pos <= desc->buffer_len);
     REQ((int64_t)desc->batch * n_pos * desc->num_v_heads <= INT_MAX / 2);
     REQ(head && committed && flushed && head != committed);
     REQ((const int32_t*)flushed != head && (const int32_t*)flushed != committed);
     REQ(aligned(head, 4) && aligned(committed, 4) && aligned(flushed, 4) && aligned(err_flags, 4));
+    REQ(aligned(n_pos_seq, 4));
     if (!gdn_fits(desc, 2, n_pos)) return REPLAYSSM_ERR_UNSUPPORTED;
     rssm::GdnArgs a = gdn_args(desc, state);
     a.cursor_in = head;
     a.committed = committed;
     a.flushed = flushed;
+    a.n_pos_seq = n_pos_seq;
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out; a.err_flags = err_flags;
     a.n_pos = n_pos;
     return hip_status(rssm::launch_gdn_replay(a, desc->io_dtype, 2, stream));

@@ -7,20 +7,24 @@
 
 namespace rssm {
 
+// A sequence with no positions this round (n_pos_seq[b] == 0: a pad row) is left as
+// it is; otherwise 1 <= n_keep <= its positions.
 __global__ void __launch_bounds__(256) commit_kernel(int32_t batch, int32_t L, int32_t n_pos,
                                                      int32_t* head, int32_t* committed,
                                                      const int32_t* flushed, const int32_t* n_keep,
-                                                     int32_t* err_flags) {
+                                                     const int32_t* n_pos_seq, int32_t* err_flags) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= batch) return;
+    const int tb = n_pos_seq ? n_pos_seq[b] : n_pos;
+    if (tb == 0) return;
     int hd = head[b], cm = committed[b];
     const int nk = n_keep[b];
     if (flushed[b]) {
         hd = (hd + cm) % L;
         cm = 0;
     }
-    if (hd < 0 || hd >= L || cm < 0 || nk < 1 || nk > n_pos || cm + nk > L) {
-        if (err_flags) atomicOr(err_flags, 1);
+    if (hd < 0 || hd >= L || cm < 0 || tb < 0 || tb > n_pos || nk < 1 || nk > tb || cm + nk > L) {
+        if (err_flags) atomicOr(err_flags, kDevErrCursor);
         return;
     }
     head[b] = hd;
@@ -38,10 +42,11 @@ __global__ void __launch_bounds__(256) reset_kernel(int32_t batch, int32_t* head
 }
 
 hipError_t launch_commit(int32_t batch, int32_t L, int32_t n_pos, int32_t* head, int32_t* committed,
-                         const int32_t* flushed, const int32_t* n_keep, int32_t* err_flags,
-                         hipStream_t stream) {
+                         const int32_t* flushed, const int32_t* n_keep, const int32_t* n_pos_seq,
+                         int32_t* err_flags, hipStream_t stream) {
     const unsigned blocks = (unsigned)((batch + 255) / 256);
-    void* kargs[] = {&batch, &L, &n_pos, &head, &committed, (void*)&flushed, (void*)&n_keep, &err_flags};
+    void* kargs[] = {&batch, &L, &n_pos, &head, &committed, (void*)&flushed, (void*)&n_keep,
+                     (void*)&n_pos_seq, &err_flags};
     return hipLaunchKernel((const void*)&commit_kernel, dim3(blocks), dim3(256), kargs, 0, stream);
 }
 

@@ -7,6 +7,9 @@
 namespace rssm {
 
 constexpr int kWave = 64;
+// bits ORed into the caller's err_flags word
+constexpr int kDevErrCursor = 1;
+constexpr int kDevErrSlot = 2;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
 
 // ---------------------------------------------------------------------------------------

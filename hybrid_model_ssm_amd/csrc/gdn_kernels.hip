@@ -100,34 +100,46 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     const int hv0 = hk * rv + chunk * a.vheads_per_chunk;
     const int nv = min(a.vheads_per_chunk, rv - chunk * a.vheads_per_chunk);
     const bool lead = (hk == 0 && chunk == 0);
+    // T: position stride of this call's inputs; Tb: positions of this sequence
     const int T = (MODE == kGdnSpec) ? a.n_pos : (MODE == kGdnDecode ? 1 : 0);
 
-    // ---- cursors -------------------------------------------------------------------
+    // ---- state row, positions and cursors of this sequence ------------------------------
+    // A pad row (state slot -1, or no positions) is skipped; a slot or position count
+    // out of range, or a bad cursor, is flagged and skipped.  Skipped rows keep their
+    // cursors (cursor_out = cursor_in) and report no flush.
+    const int sb = a.slot ? a.slot[b] : b;
+    const int Tb = (MODE == kGdnSpec && a.n_pos_seq) ? a.n_pos_seq[b] : T;
     int c = 0, hd = 0, cm = 0;
-    bool bad;
+    int err = 0;
+    if (sb < -1 || sb >= (a.slot ? a.num_slots : a.batch)) err |= kDevErrSlot;
+    if (Tb < 0 || Tb > T) err |= kDevErrCursor;
     if constexpr (MODE == kGdnSpec) {
         hd = a.cursor_in[b];
         cm = a.committed[b];
-        bad = hd < 0 || hd >= L || cm < 0 || cm > L;
+        if (hd < 0 || hd >= L || cm < 0 || cm > L) err |= kDevErrCursor;
     } else {
         c = a.cursor_in[b];
-        bad = c < 0 || c >= L;
+        if (c < 0 || c >= L) err |= kDevErrCursor;
     }
-    if (bad) {
+    if (err || sb < 0 || (MODE == kGdnSpec && Tb == 0)) {
         if (tid == 0) {
-            if (a.err_flags) atomicOr(a.err_flags, 1);
-            if (lead && MODE != kGdnSpec) a.cursor_out[b] = c;
+            if (err && a.err_flags) atomicOr(a.err_flags, err);
+            if (lead) {
+                if (MODE == kGdnSpec) a.flushed[b] = 0;
+                else a.cursor_out[b] = c;
+            }
         }
         return;
     }
     const int nstored = (MODE == kGdnSpec) ? cm : c;   // window rows taken from the ring
-    const int nrec = nstored + T;                       // window rows
+    const int nrec = nstored + Tb;                      // window rows
     const bool fold = (MODE == kGdnFold) || (MODE == kGdnDecode && c + 1 == L) ||
-                      (MODE == kGdnSpec && cm + T > L);
+                      (MODE == kGdnSpec && cm + Tb > L);
     const int nf = (MODE == kGdnSpec) ? cm : nrec;      // the fold covers rows [0, nf)
     const int st = fold ? nf : 0;                       // first row of every chain
     const bool idle = (MODE == kGdnFold) && c == 0;
-    const size_t bHV = (size_t)b * HV;
+    const size_t bHV = (size_t)b * HV;    // inputs and outputs: batch row
+    const size_t sHV = (size_t)sb * HV;   // checkpoint and records: state row
 
     const GdnSmem lay(DK, DV, L, T, MODE, a.vheads_per_chunk, (int)sizeof(IO));
     const int NR = lay.NR, T1 = lay.T1;
@@ -144,7 +156,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     const int col4 = tid % LPR;
     auto tile_base = [&](int u) -> size_t {   // unit u = (value head u / NTILE, tile u % NTILE)
         const int vl = u / NTILE, tl = u % NTILE;
-        return ((bHV + hv0 + vl) * DV + tl * DVT + row0) * (size_t)DK + 4 * col4;
+        return ((sHV + hv0 + vl) * DV + tl * DVT + row0) * (size_t)DK + 4 * col4;
     };
     auto issue_tile = [&](int u, float4 (&v)[R]) {
         const size_t t = tile_base(u);
@@ -170,7 +182,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     auto pos_h = [&](int vl, int j) -> size_t {   // alpha/beta index of value head vl, position j
         return (MODE == kGdnSpec) ? (size_t)(b * T + j) * HV + hv0 + vl : bHV + hv0 + vl;
     };
-    const IO* recK = reinterpret_cast<const IO*>(a.rec_k) + ((size_t)b * HK + hk) * L * DK;
+    const IO* recK = reinterpret_cast<const IO*>(a.rec_k) + ((size_t)sb * HK + hk) * L * DK;
     const IO* kin = reinterpret_cast<const IO*>(a.k);
     const IO* qin = reinterpret_cast<const IO*>(a.q);
     const IO* vin = reinterpret_cast<const IO*>(a.v);
@@ -185,19 +197,19 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         const int i4 = task % DV4;
         const int vs = task / DV4;
         const int vl = vs / nrec, s = vs - vl * nrec;
-        const size_t hv = bHV + hv0 + vl;
+        const size_t hv = sHV + hv0 + vl;
         const Raw4 r = (s < nstored) ? io::ldraw4(recV, (hv * L + slot_of(s)) * DV + 4 * i4)
                                      : io::ldraw4(vin, pos_h(vl, s - nstored) * DV + 4 * i4);
         *reinterpret_cast<Raw4*>(sV + (vl * NR + s) * DV + 4 * i4) = r;
     }
     for (int task = tid; task < nv * nrec; task += kGdnThreads) {
         const int vl = task / nrec, s = task - vl * nrec;
-        const size_t hv = bHV + hv0 + vl;
+        const size_t hv = sHV + hv0 + vl;
         const bool rec = s < nstored;
         sAl[vl * NR + s] = rec ? a.rec_alpha[hv * L + slot_of(s)] : a.alpha[pos_h(vl, s - nstored)];
         sBe[vl * NR + s] = rec ? a.rec_beta[hv * L + slot_of(s)] : a.beta[pos_h(vl, s - nstored)];
     }
-    for (int task = tid; task < T * DK4; task += kGdnThreads) {
+    for (int task = tid; task < Tb * DK4; task += kGdnThreads) {
         const int j = task / DK4, j4 = task % DK4;
         *reinterpret_cast<float4*>(sQ + j * DK + 4 * j4) = io::cvt4(io::ldraw4(qin, pos_qk(j) + 4 * j4));
     }
@@ -212,20 +224,20 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     // ---- carry each position's q back through its window --------------------------------
     // Position j's chain covers rows nstored + j down to st.  A wave runs TC chains of
     // one value head in lockstep over the rows (they share k_s, alpha_s and beta_s).
-    if (T > 0) {
-        const int ngrp = (T + TC - 1) / TC;
+    if (Tb > 0) {
+        const int ngrp = (Tb + TC - 1) / TC;
         for (int task = wave; task < nv * ngrp; task += NWAVE) {
             const int vl = task / ngrp, j0 = (task - vl * ngrp) * TC;
             float u[TC][UPL];
 #pragma unroll
             for (int cc = 0; cc < TC; ++cc) {
-                const int j = min(j0 + cc, T - 1);
+                const int j = min(j0 + cc, Tb - 1);
 #pragma unroll
                 for (int m = 0; m < UPL; ++m) u[cc][m] = sQ[j * DK + lane + m * kWave];
             }
             const float* al = sAl + vl * NR;
             const float* be = sBe + vl * NR;
-            const int jtop = min(j0 + TC, T) - 1;
+            const int jtop = min(j0 + TC, Tb) - 1;
             for (int s = nstored + jtop; s >= st; --s) {
                 float kap[TC];
 #pragma unroll
@@ -239,10 +251,10 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 const float as = al[s], bs = be[s];
 #pragma unroll
                 for (int cc = 0; cc < TC; ++cc) {
-                    const int j = min(j0 + cc, T - 1);
+                    const int j = min(j0 + cc, Tb - 1);
                     const bool on = s <= nstored + j;     // row s lies in position j's window
                     const float bk = on ? bs * kap[cc] : 0.f;
-                    if (lane == 0 && j0 + cc < T) sCoef[(vl * T1 + j) * NR + s] = bk;
+                    if (lane == 0 && j0 + cc < Tb) sCoef[(vl * T1 + j) * NR + s] = bk;
                     if (on) {
 #pragma unroll
                         for (int m = 0; m < UPL; ++m) u[cc][m] = as * (u[cc][m] - bk * sK[s * DK + lane + m * kWave]);
@@ -251,7 +263,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
             }
 #pragma unroll
             for (int cc = 0; cc < TC; ++cc) {
-                if (j0 + cc < T) {
+                if (j0 + cc < Tb) {
 #pragma unroll
                     for (int m = 0; m < UPL; ++m) sU[(vl * T1 + j0 + cc) * DK + lane + m * kWave] = u[cc][m];
                 }
@@ -259,9 +271,9 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         }
         __syncthreads();
         // ---- record terms sum_s beta_s kappa_s v_s[i] of every (value head, position) --
-        for (int task = tid; task < nv * T * DV; task += kGdnThreads) {
+        for (int task = tid; task < nv * Tb * DV; task += kGdnThreads) {
             const int i = task % DV, vj = task / DV;
-            const int vl = vj / T, j = vj - vl * T;
+            const int vl = vj / Tb, j = vj - vl * Tb;
             float acc = 0.f;
             for (int s = st; s <= nstored + j; ++s)
                 acc += sCoef[(vl * T1 + j) * NR + s] * io::ld(sV, (vl * NR + s) * DV + i);
@@ -288,11 +300,11 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 a.out[out_index(vl, 0, i)] = scale * (r + sAcc[vl * DV + i]);
             }
         } else if constexpr (MODE == kGdnSpec) {
-            for (int j0 = 0; j0 < T; j0 += TB) {
+            for (int j0 = 0; j0 < Tb; j0 += TB) {
                 float acc[R * TB];
 #pragma unroll
                 for (int jj = 0; jj < TB; ++jj) {
-                    const int j = min(j0 + jj, T - 1);
+                    const int j = min(j0 + jj, Tb - 1);
                     const float4 Uv = *reinterpret_cast<const float4*>(sU + (vl * T1 + j) * DK + 4 * col4);
 #pragma unroll
                     for (int k = 0; k < R; ++k) acc[jj * R + k] = dot4(v[k], Uv);
@@ -301,7 +313,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 const int vi = q / (LPR / (R * TB));          // value index this lane holds
                 const int j = j0 + vi / R;
                 const int i = tl * DVT + row0 + (vi % R) * RPP;
-                if ((q % (LPR / (R * TB))) == 0 && j < T)
+                if ((q % (LPR / (R * TB))) == 0 && j < Tb)
                     a.out[out_index(vl, j, i)] = scale * (r + sAcc[(vl * T1 + j) * DV + i]);
             }
         }
@@ -359,18 +371,18 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         if (!fold) {
             for (int task = tid; task < nv * DV4; task += kGdnThreads) {
                 const int vl = task / DV4, i4 = task % DV4;
-                const size_t hv = bHV + hv0 + vl;
-                io::straw4(reinterpret_cast<IO*>(a.rec_v), (hv * L + c) * DV + 4 * i4,
-                           io::ldraw4(vin, hv * DV + 4 * i4));
+                const size_t sv = sHV + hv0 + vl, iv = bHV + hv0 + vl;
+                io::straw4(reinterpret_cast<IO*>(a.rec_v), (sv * L + c) * DV + 4 * i4,
+                           io::ldraw4(vin, iv * DV + 4 * i4));
             }
             for (int vl = tid; vl < nv; vl += kGdnThreads) {
-                const size_t hv = bHV + hv0 + vl;
-                a.rec_alpha[hv * L + c] = a.alpha[hv];
-                a.rec_beta[hv * L + c] = a.beta[hv];
+                const size_t sv = sHV + hv0 + vl, iv = bHV + hv0 + vl;
+                a.rec_alpha[sv * L + c] = a.alpha[iv];
+                a.rec_beta[sv * L + c] = a.beta[iv];
             }
             if (chunk == 0) {
                 for (int j4 = tid; j4 < DK4; j4 += kGdnThreads)
-                    io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)b * HK + hk) * L + c) * DK + 4 * j4,
+                    io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)sb * HK + hk) * L + c) * DK + 4 * j4,
                                io::ldraw4(kin, pos_qk(0) + 4 * j4));
             }
         }
@@ -378,25 +390,25 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         // Every ring row this workgroup reads was staged before the first barrier, so
         // position slots may replace committed ones here (rounds that fold).
         const int slot0 = hd + cm;
-        for (int task = tid; task < nv * T * DV4; task += kGdnThreads) {
+        for (int task = tid; task < nv * Tb * DV4; task += kGdnThreads) {
             const int i4 = task % DV4, vj = task / DV4;
-            const int vl = vj / T, j = vj - vl * T;
-            const size_t hv = bHV + hv0 + vl;
+            const int vl = vj / Tb, j = vj - vl * Tb;
+            const size_t hv = sHV + hv0 + vl;
             io::straw4(reinterpret_cast<IO*>(a.rec_v), (hv * L + (slot0 + j) % L) * DV + 4 * i4,
                        *reinterpret_cast<const Raw4*>(sV + (vl * NR + nstored + j) * DV + 4 * i4));
         }
-        for (int task = tid; task < nv * T; task += kGdnThreads) {
-            const int vl = task / T, j = task - vl * T;
-            const size_t hv = bHV + hv0 + vl;
+        for (int task = tid; task < nv * Tb; task += kGdnThreads) {
+            const int vl = task / Tb, j = task - vl * Tb;
+            const size_t hv = sHV + hv0 + vl;
             a.rec_alpha[hv * L + (slot0 + j) % L] = sAl[vl * NR + nstored + j];
             a.rec_beta[hv * L + (slot0 + j) % L] = sBe[vl * NR + nstored + j];
         }
         // the q/k head's k records: with several workgroups per q/k head the host
         // appends them in a separate launch
         if (nchunk == 1) {
-            for (int task = tid; task < T * DK4; task += kGdnThreads) {
+            for (int task = tid; task < Tb * DK4; task += kGdnThreads) {
                 const int j = task / DK4, j4 = task % DK4;
-                io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)b * HK + hk) * L + (slot0 + j) % L) * DK + 4 * j4,
+                io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)sb * HK + hk) * L + (slot0 + j) % L) * DK + 4 * j4,
                            io::ldraw4(kin, pos_qk(j) + 4 * j4));
             }
         }
@@ -426,10 +438,13 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_spec_append_k_kernel(GdnArgs 
         r /= HK;
         const int j = (int)(r % T);
         const int b = (int)(r / T);
+        const int sb = a.slot ? a.slot[b] : b;
+        const int Tb = a.n_pos_seq ? a.n_pos_seq[b] : T;
         const int hd = a.cursor_in[b], cm = a.committed[b];
         if (hd < 0 || hd >= L || cm < 0 || cm > L) continue;
+        if (sb < 0 || sb >= (a.slot ? a.num_slots : a.batch) || Tb < 0 || Tb > T || j >= Tb) continue;
         const int slot = (hd + cm + j) % L;
-        io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)b * HK + hk) * L + slot) * DK + 4 * j4,
+        io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)sb * HK + hk) * L + slot) * DK + 4 * j4,
                    io::ldraw4(reinterpret_cast<const IO*>(a.k), (((size_t)b * T + j) * HK + hk) * DK + 4 * j4));
     }
 }

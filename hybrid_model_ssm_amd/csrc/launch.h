@@ -32,6 +32,9 @@ struct Mamba2Args {
     int32_t batch, nheads, headdim, dstate, ngroups, L, dt_softplus, n_pos;
     int32_t nchunk;       // workgroups per (sequence, group)
     int32_t heads_per_chunk;
+    const int32_t* slot;       // state row of each batch row (-1: pad), or null (identity)
+    int32_t num_slots;         // rows of the state arrays when slot is set
+    const int32_t* n_pos_seq;  // speculative: positions of each sequence, or null (n_pos)
 };
 
 // Conventional read-update-write step (and the per-position snapshot baseline).
@@ -71,6 +74,9 @@ struct GdnArgs {
     float scale;
     int32_t nchunk;            // workgroups per (sequence, q/k head)
     int32_t vheads_per_chunk;
+    const int32_t* slot;       // state row of each batch row (-1: pad), or null (identity)
+    int32_t num_slots;
+    const int32_t* n_pos_seq;  // speculative: positions of each sequence, or null (n_pos)
 };
 
 bool mamba2_shape_supported(int headdim, int dstate);
@@ -88,7 +94,7 @@ hipError_t launch_mamba2_conventional(const Mamba2ConvArgs& a, int io, bool snap
 
 hipError_t launch_commit(int32_t batch, int32_t L, int32_t n_pos, int32_t* head,
                          int32_t* committed, const int32_t* flushed, const int32_t* n_keep,
-                         int32_t* err_flags, hipStream_t stream);
+                         const int32_t* n_pos_seq, int32_t* err_flags, hipStream_t stream);
 hipError_t launch_reset(int32_t batch, int32_t* head, int32_t* cursor, const int32_t* seq_idx,
                         int32_t n_seq, hipStream_t stream);
 

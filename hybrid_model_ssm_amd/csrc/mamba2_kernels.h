@@ -122,32 +122,43 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     const int h0 = g * hpg + chunk * a.heads_per_chunk;
     const int nh = min(a.heads_per_chunk, hpg - chunk * a.heads_per_chunk);
     const bool lead = (g == 0 && chunk == 0);  // writes the per-sequence cursor outputs
+    // T: position stride of this call's inputs; Tb: positions of this sequence
     const int T = (MODE == kSpec) ? a.n_pos : (MODE == kFold ? 0 : 1);
 
-    // ---- cursors -------------------------------------------------------------------
+    // ---- state row, positions and cursors of this sequence ------------------------------
+    // A pad row (state slot -1, or no positions) is skipped; a slot or position count
+    // out of range, or a bad cursor, is flagged and skipped.  Skipped rows keep their
+    // cursors (cursor_out = cursor_in) and report no flush.
+    const int sb = a.slot ? a.slot[b] : b;
+    const int Tb = (MODE == kSpec && a.n_pos_seq) ? a.n_pos_seq[b] : T;
     int c = 0, hd = 0, cm = 0;
-    bool bad;
+    int err = 0;
+    if (sb < -1 || sb >= (a.slot ? a.num_slots : a.batch)) err |= kDevErrSlot;
+    if (Tb < 0 || Tb > T) err |= kDevErrCursor;
     if constexpr (MODE == kSpec) {
         hd = a.cursor_in[b];
         cm = a.committed[b];
-        bad = hd < 0 || hd >= L || cm < 0 || cm > L;
+        if (hd < 0 || hd >= L || cm < 0 || cm > L) err |= kDevErrCursor;
     } else {
         c = a.cursor_in[b];
-        bad = c < 0 || c >= L;
+        if (c < 0 || c >= L) err |= kDevErrCursor;
     }
-    if (bad) {
+    if (err || sb < 0 || (MODE == kSpec && Tb == 0)) {
         if (tid == 0) {
-            if (a.err_flags) atomicOr(a.err_flags, 1);
-            if (lead && MODE != kSpec) a.cursor_out[b] = c;
+            if (err && a.err_flags) atomicOr(a.err_flags, err);
+            if (lead) {
+                if (MODE == kSpec) a.flushed[b] = 0;
+                else a.cursor_out[b] = c;
+            }
         }
         return;
     }
     const int nstored = (MODE == kSpec) ? cm : c;   // window rows taken from the ring
-    const int nrec = nstored + T;                    // window rows
+    const int nrec = nstored + Tb;                   // window rows
     // flush: the checkpoint is rewritten; fold: the window is applied to the tile in
     // registers (every step of the state-and-output route)
     const bool flush = (MODE == kFold) || ((MODE == kDecode || MODE == kDecodeSO) && c + 1 == L) ||
-                       (MODE == kSpec && cm + T > L);
+                       (MODE == kSpec && cm + Tb > L);
     const bool fold = flush || MODE == kDecodeSO;
     const int nf = (MODE == kSpec) ? cm : nrec;      // the fold covers rows [0, nf)
     const int st = fold ? nf : 0;                    // first row of every output window
@@ -181,8 +192,9 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     const IO* Cin = reinterpret_cast<const IO*>(a.C);
     const IO* dtin = reinterpret_cast<const IO*>(a.dt_raw);
     const IO* recX = reinterpret_cast<const IO*>(a.rec_x);
-    const IO* recB = reinterpret_cast<const IO*>(a.rec_B) + (size_t)(b * G + g) * L * N;
-    const size_t bH = (size_t)b * H;
+    const IO* recB = reinterpret_cast<const IO*>(a.rec_B) + (size_t)(sb * G + g) * L * N;
+    const size_t bH = (size_t)b * H;    // inputs and outputs: batch row
+    const size_t sH = (size_t)sb * H;   // checkpoint, copy and records: state row
 
     auto slot_of = [&](int s) {
         if constexpr (MODE == kSpec) {
@@ -194,7 +206,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     };
     // row s of head h's x window: a ring record or one of this call's positions
     auto xrow = [&](int h, int s) -> const IO* {
-        if (s < nstored) return recX + ((bH + h) * L + slot_of(s)) * P;
+        if (s < nstored) return recX + ((sH + h) * L + slot_of(s)) * P;
         const int j = s - nstored;
         return xin + ((MODE == kSpec) ? ((size_t)(b * T + j) * H + h) * P : (bH + h) * P);
     };
@@ -211,7 +223,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     // ---- checkpoint tile loads (head hl into v / vl) -------------------------------------
     auto issue_tile = [&](int hl, float4 (&v)[R]) {
         if (!idle) {
-            const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
+            const size_t t = (sH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
 #pragma unroll
             for (int k = 0; k < R; ++k)
                 if (!MASK || row0 + k * RPP < P) v[k] = ld_stream(a.ckpt + t + (size_t)k * RPP * N);
@@ -228,7 +240,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     // the row this lane writes after the transpose-reduce (fixed for the whole call)
     const int pq = rowq0 + ((colq / (Tq::LPR / (RQ * TBQ))) % RQ) * Tq::RPP;
     auto issue_tile_lp = [&](int hl, uint4 (&v)[RQ], float& sc) {
-        const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)rowq0 * N + EPL * colq;
+        const size_t t = (sH + h0 + hl) * (size_t)(P * N) + (size_t)rowq0 * N + EPL * colq;
 #pragma unroll
         for (int k = 0; k < RQ; ++k) {
             if (!Tq::MASK || rowq0 + k * Tq::RPP < P) {
@@ -238,7 +250,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                     v[k] = ld_stream8(reinterpret_cast<const uint16_t*>(a.ckpt_lp) + t + (size_t)k * Tq::RPP * N);
             }
         }
-        if constexpr (LP == kLpFP8) sc = a.lp_scale[(bH + h0 + hl) * P + min(pq, P - 1)];
+        if constexpr (LP == kLpFP8) sc = a.lp_scale[(sH + h0 + hl) * P + min(pq, P - 1)];
     };
     // fold rows of head hl: x_s[p] for s < nf, as 4-element chunks
     Raw4 xf[kFoldXPerThread];
@@ -264,14 +276,14 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     // (autoregressive decode only: in speculative mode they would stay live across the
     // head loop and cost occupancy)
     constexpr int kAppendPerThread = (MODE == kDecode) ? 2 : 0;
-    const int napp = (MODE == kFold || (MODE != kSpec && flush)) ? 0 : nh * T * P4;
+    const int napp = (MODE == kFold || (MODE != kSpec && flush)) ? 0 : nh * Tb * P4;
     Raw4 app[kAppendPerThread > 0 ? kAppendPerThread : 1];
 #pragma unroll
     for (int i = 0; i < kAppendPerThread; ++i) {
         const int task = tid + i * kThreads;
         if (task < napp) {
             const int p4 = task % P4, hj = task / P4;
-            const int hl = hj / T, j = hj - hl * T;
+            const int hl = hj / Tb, j = hj - hl * Tb;
             app[i] = io::ldraw4(xin, pos_x(h0 + hl, j) + 4 * p4);
         }
     }
@@ -283,7 +295,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                                      : io::ldraw4(Bin, pos_g(s - nstored) + 4 * n4);
         *reinterpret_cast<Raw4*>(sB + s * N + 4 * n4) = r;
     }
-    for (int task = tid; task < T * N4; task += kThreads) {
+    for (int task = tid; task < Tb * N4; task += kThreads) {
         const int j = task / N4, n4 = task % N4;
         *reinterpret_cast<float4*>(sC + j * N + 4 * n4) = io::cvt4(io::ldraw4(Cin, pos_g(j) + 4 * n4));
     }
@@ -292,7 +304,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
         const int h = h0 + hl;
         float dt;
         if (s < nstored) {
-            dt = a.rec_dt[(bH + h) * L + slot_of(s)];
+            dt = a.rec_dt[(sH + h) * L + slot_of(s)];
         } else {
             dt = io::ld(dtin, pos_h(h, s - nstored)) + a.dt_bias[h];
             if (a.dt_softplus) dt = softplus_f32(dt);
@@ -307,10 +319,10 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
 
     if constexpr (MODE != kFold) {
         // ---- prologue 2: beta[j][s] = B_s . C_j, 16 lanes a pair -----------------------
-        for (int base = 0; base < T * nrec; base += kThreads / 16) {
+        for (int base = 0; base < Tb * nrec; base += kThreads / 16) {
             const int pr = base + tid / 16;
             const int part = tid & 15;
-            if (pr < T * nrec) {
+            if (pr < Tb * nrec) {
                 const int j = pr / nrec, s = pr - j * nrec;
                 float beta = 0.f;
                 for (int n = part; n < N; n += 16) beta += io::ld(sB, s * N + n) * sC[j * N + n];
@@ -322,8 +334,8 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
     }
 
     // ---- prologue 3: per-head coefficients (log-space decay sums, newest row first) -------
-    for (int pr = tid; pr < nh * T; pr += kThreads) {
-        const int hl = pr / T, j = pr - hl * T;
+    for (int pr = tid; pr < nh * Tb; pr += kThreads) {
+        const int hl = pr / Tb, j = pr - hl * Tb;
         const int e = nstored + j;          // position j's own row
         const float Ah = sA[hl];
         float lam = 0.f;
@@ -354,13 +366,13 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
         // One task per (head, 4 columns, up to kPosBatch positions): each window row is
         // loaded once and feeds every position whose window holds it.
         constexpr int kPosBatch = 4;
-        const int njb = (T + kPosBatch - 1) / kPosBatch;
+        const int njb = (Tb + kPosBatch - 1) / kPosBatch;
         for (int task = tid; task < nh * njb * P4; task += kThreads) {
             const int p4 = task % P4;
             const int hb = task / P4;
             const int hl = hb / njb, j0 = (hb - hl * njb) * kPosBatch;
             const int h = h0 + hl;
-            const int jn = min(kPosBatch, T - j0);
+            const int jn = min(kPosBatch, Tb - j0);
             const int elast = nstored + j0 + jn - 1;        // last row any of these windows uses
             const float Dh = sD[hl];
             float4 y[kPosBatch];
@@ -431,11 +443,11 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
             }
         } else if constexpr (MODE == kSpec) {
             const int h = h0 + hl;
-            for (int j0 = 0; j0 < T; j0 += TB) {
+            for (int j0 = 0; j0 < Tb; j0 += TB) {
                 float acc[R * TB];
 #pragma unroll
                 for (int jj = 0; jj < TB; ++jj) {
-                    const int j = min(j0 + jj, T - 1);
+                    const int j = min(j0 + jj, Tb - 1);
                     const float4 Cv = *reinterpret_cast<const float4*>(sC + j * N + 4 * col4);
 #pragma unroll
                     for (int k = 0; k < R; ++k) acc[jj * R + k] = dot4(v[k], Cv);
@@ -444,7 +456,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 const int vi = q / (LPR / (R * TB));          // value index this lane holds
                 const int j = j0 + vi / R;
                 const int p = row0 + (vi % R) * RPP;
-                if ((q % (LPR / (R * TB))) == 0 && j < T && (!MASK || p < P)) {
+                if ((q % (LPR / (R * TB))) == 0 && j < Tb && (!MASK || p < P)) {
                     const int o = (hl * T1 + j) * P + p;
                     a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
                 }
@@ -482,11 +494,11 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
             const int h = h0 + hl;
             const int qq = tid % LQ;
             const float rs = (LP == kLpFP8) ? sc * 256.0f : 1.0f;
-            for (int j0 = 0; j0 < T; j0 += TBQ) {
+            for (int j0 = 0; j0 < Tb; j0 += TBQ) {
                 float acc[RQ * TBQ];
 #pragma unroll
                 for (int jj = 0; jj < TBQ; ++jj) {
-                    const int j = min(j0 + jj, T - 1);
+                    const int j = min(j0 + jj, Tb - 1);
 #pragma unroll
                     for (int k = 0; k < RQ; ++k) acc[jj * RQ + k] = lp_dot(v[k], j);
                 }
@@ -494,7 +506,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 const int vi = qq / (LQ / (RQ * TBQ));
                 const int j = j0 + vi / RQ;
                 const int p = rowq0 + (vi % RQ) * Tq::RPP;
-                if ((qq % (LQ / (RQ * TBQ))) == 0 && j < T && (!Tq::MASK || p < P)) {
+                if ((qq % (LQ / (RQ * TBQ))) == 0 && j < Tb && (!Tq::MASK || p < P)) {
                     const int o = (hl * T1 + j) * P + p;
                     a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * (rs * r) + sY[o], io::ld(sZ, o));
                 }
@@ -552,7 +564,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                     }
                 }
             }
-            const size_t t = (bH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
+            const size_t t = (sH + h0 + hl) * (size_t)(P * N) + (size_t)row0 * N + 4 * col4;
 #pragma unroll
             for (int k = 0; k < R; ++k) {
                 // fp8 copy: the row's largest magnitude over its LPR lanes (every lane
@@ -575,7 +587,7 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                         } else if constexpr (LP == kLpFP8) {
                             const float inv = amax > 0.f ? 448.0f / amax : 0.f;
                             st_stream(reinterpret_cast<uint8_t*>(a.ckpt_lp) + off, f32x4_to_e4m3x4(va[k], inv));
-                            if (col4 == 0) a.lp_scale[(bH + h0 + hl) * P + row0 + k * RPP] = amax / 448.0f;
+                            if (col4 == 0) a.lp_scale[(sH + h0 + hl) * P + row0 + k * RPP] = amax / 448.0f;
                         }
                     }
                 }
@@ -604,28 +616,28 @@ __global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
                 const int task = tid + i * kThreads;
                 if (task < napp) {
                     const int p4 = task % P4, hj = task / P4;
-                    const int hl = hj / T, j = hj - hl * T;
+                    const int hl = hj / Tb, j = hj - hl * Tb;
                     const int slot = (slot0 + j) % L;
-                    io::straw4(reinterpret_cast<IO*>(a.rec_x), ((bH + h0 + hl) * L + slot) * P + 4 * p4, app[i]);
+                    io::straw4(reinterpret_cast<IO*>(a.rec_x), ((sH + h0 + hl) * L + slot) * P + 4 * p4, app[i]);
                 }
             }
             for (int task = tid + kAppendPerThread * kThreads; task < napp; task += kThreads) {
                 const int p4 = task % P4, hj = task / P4;
-                const int hl = hj / T, j = hj - hl * T;
+                const int hl = hj / Tb, j = hj - hl * Tb;
                 const int slot = (slot0 + j) % L;
-                io::straw4(reinterpret_cast<IO*>(a.rec_x), ((bH + h0 + hl) * L + slot) * P + 4 * p4,
+                io::straw4(reinterpret_cast<IO*>(a.rec_x), ((sH + h0 + hl) * L + slot) * P + 4 * p4,
                            io::ldraw4(xin, pos_x(h0 + hl, j) + 4 * p4));
             }
-            for (int task = tid; task < nh * T; task += kThreads) {
-                const int hl = task / T, j = task - hl * T;
-                a.rec_dt[(bH + h0 + hl) * L + (slot0 + j) % L] = sdt[hl * NR + nstored + j];
+            for (int task = tid; task < nh * Tb; task += kThreads) {
+                const int hl = task / Tb, j = task - hl * Tb;
+                a.rec_dt[(sH + h0 + hl) * L + (slot0 + j) % L] = sdt[hl * NR + nstored + j];
             }
             // the group's B records: with several workgroups per group the host appends
             // them in a separate launch (speculative rounds only)
             if (nchunk == 1 || (MODE != kSpec && chunk == 0)) {
-                for (int task = tid; task < T * N4; task += kThreads) {
+                for (int task = tid; task < Tb * N4; task += kThreads) {
                     const int j = task / N4, n4 = task % N4;
-                    io::straw4(reinterpret_cast<IO*>(a.rec_B), ((size_t)(b * G + g) * L + (slot0 + j) % L) * N + 4 * n4,
+                    io::straw4(reinterpret_cast<IO*>(a.rec_B), ((size_t)(sb * G + g) * L + (slot0 + j) % L) * N + 4 * n4,
                                *reinterpret_cast<const Raw4*>(sB + (nstored + j) * N + 4 * n4));
                 }
             }
@@ -654,10 +666,13 @@ __global__ void __launch_bounds__(kThreads) mamba2_spec_append_B_kernel(Mamba2Ar
         r /= G;
         const int j = (int)(r % T);
         const int b = (int)(r / T);
+        const int sb = a.slot ? a.slot[b] : b;
+        const int Tb = a.n_pos_seq ? a.n_pos_seq[b] : T;
         const int hd = a.cursor_in[b], cm = a.committed[b];
         if (hd < 0 || hd >= L || cm < 0 || cm > L) continue;
+        if (sb < 0 || sb >= (a.slot ? a.num_slots : a.batch) || Tb < 0 || Tb > T || j >= Tb) continue;
         const int slot = (hd + cm + j) % L;
-        reinterpret_cast<IO*>(a.rec_B)[((size_t)(b * G + g) * L + slot) * N + n] =
+        reinterpret_cast<IO*>(a.rec_B)[((size_t)(sb * G + g) * L + slot) * N + n] =
             reinterpret_cast<const IO*>(a.B)[i];
     }
 }

@@ -24,7 +24,7 @@ LIB_PATH = os.environ.get("REPLAYSSM_LIB") or os.path.join(_HERE, "libreplayssm.
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
-DEVERR_CURSOR = 1
+DEVERR_CURSOR, DEVERR_SLOT = 1, 2
 MAX_BUFFER_LEN = 64
 
 EXPORTED = (
@@ -56,7 +56,7 @@ class Mamba2DescC(ctypes.Structure):
 class Mamba2StateC(ctypes.Structure):
     _fields_ = [("ckpt", ctypes.c_void_p), ("ckpt_lp", ctypes.c_void_p), ("rec_x", ctypes.c_void_p),
                 ("rec_B", ctypes.c_void_p), ("rec_dt", ctypes.c_void_p), ("lp_dtype", ctypes.c_int32),
-                ("lp_scale", ctypes.c_void_p)]
+                ("lp_scale", ctypes.c_void_p), ("slot", ctypes.c_void_p), ("num_slots", ctypes.c_int32)]
 
 
 class GdnDescC(ctypes.Structure):
@@ -67,7 +67,8 @@ class GdnDescC(ctypes.Structure):
 
 class GdnStateC(ctypes.Structure):
     _fields_ = [("ckpt", ctypes.c_void_p), ("rec_k", ctypes.c_void_p), ("rec_v", ctypes.c_void_p),
-                ("rec_alpha", ctypes.c_void_p), ("rec_beta", ctypes.c_void_p)]
+                ("rec_alpha", ctypes.c_void_p), ("rec_beta", ctypes.c_void_p), ("slot", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int32)]
 
 
 _lib = None
@@ -94,14 +95,14 @@ def lib():
         "replayssm_mamba2_decode": [D, S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_mamba2_decode_state_and_output": [D, S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_mamba2_flush": [D, S, _P, _P, _P, _P, _P],
-        "replayssm_mamba2_spec_verify": [D, S, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
-        "replayssm_commit": [_I, _I, _I, _P, _P, _P, _P, _P, _P],
+        "replayssm_mamba2_spec_verify": [D, S, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "replayssm_commit": [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_reset_cursors": [_I, _P, _P, _P, _I, _P],
         "replayssm_selective_state_update": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_mamba2_spec_baseline": [D, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_decode": [GD, GS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_flush": [GD, GS, _P, _P, _P, _P],
-        "replayssm_gdn_spec_verify": [GD, GS, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "replayssm_gdn_spec_verify": [GD, GS, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_conventional_decode": [GD, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_spec_baseline": [GD, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P],
     }
@@ -181,12 +182,15 @@ class Mamba2State:
     rec_dt: torch.Tensor
     ckpt_lp: torch.Tensor | None = None
     lp_scale: torch.Tensor | None = None      # [B,H,P] f32 row scales of an fp8 copy
+    slot: torch.Tensor | None = None          # [batch] int32 state row of each batch row (-1: pad)
 
     @staticmethod
-    def allocate(desc: Mamba2Desc, device="cuda", lowp=False, ckpt=None):
+    def allocate(desc: Mamba2Desc, device="cuda", lowp=False, ckpt=None, num_slots=None):
         """``lowp``: False (no read copy), True or "bf16", "f16", or "fp8" (e4m3 codes
-        as uint8 with f32 row scales)."""
-        B, H, P, N, G, L = desc.batch, desc.nheads, desc.headdim, desc.dstate, desc.ngroups, desc.buffer_len
+        as uint8 with f32 row scales).  ``num_slots``: rows of a state pool addressed
+        through ``slot`` (default: one row per batch row)."""
+        H, P, N, G, L = desc.nheads, desc.headdim, desc.dstate, desc.ngroups, desc.buffer_len
+        B = desc.batch if num_slots is None else int(num_slots)
         io = desc.torch_io
         if ckpt is None:
             ckpt = torch.zeros(B, H, P, N, dtype=torch.float32, device=device)
@@ -214,7 +218,8 @@ class Mamba2State:
                             _ptr(self.ckpt_lp, None, "ckpt_lp"),
                             _ptr(self.rec_x, None, "rec_x"), _ptr(self.rec_B, None, "rec_B"),
                             _ptr(self.rec_dt, torch.float32, "rec_dt"), self.lp_dtype,
-                            _ptr(self.lp_scale, torch.float32, "lp_scale"))
+                            _ptr(self.lp_scale, torch.float32, "lp_scale"), _ptr(self.slot, torch.int32, "slot"),
+                            self.ckpt.shape[0])
 
 
 @dataclasses.dataclass
@@ -244,10 +249,12 @@ class GdnState:
     rec_v: torch.Tensor
     rec_alpha: torch.Tensor
     rec_beta: torch.Tensor
+    slot: torch.Tensor | None = None          # [batch] int32 state row of each batch row (-1: pad)
 
     @staticmethod
-    def allocate(desc: GdnDesc, device="cuda", ckpt=None):
-        B, HV, HK, dk, dv, L = desc.batch, desc.num_v_heads, desc.num_k_heads, desc.dk, desc.dv, desc.buffer_len
+    def allocate(desc: GdnDesc, device="cuda", ckpt=None, num_slots=None):
+        HV, HK, dk, dv, L = desc.num_v_heads, desc.num_k_heads, desc.dk, desc.dv, desc.buffer_len
+        B = desc.batch if num_slots is None else int(num_slots)
         io = desc.torch_io
         if ckpt is None:
             ckpt = torch.zeros(B, HV, dv, dk, dtype=torch.float32, device=device)
@@ -260,7 +267,8 @@ class GdnState:
     def c(self):
         return GdnStateC(_ptr(self.ckpt, torch.float32, "ckpt"), _ptr(self.rec_k, None, "rec_k"),
                          _ptr(self.rec_v, None, "rec_v"), _ptr(self.rec_alpha, torch.float32, "rec_alpha"),
-                         _ptr(self.rec_beta, torch.float32, "rec_beta"))
+                         _ptr(self.rec_beta, torch.float32, "rec_beta"), _ptr(self.slot, torch.int32, "slot"),
+                         self.ckpt.shape[0])
 
 
 # --------------------------------------------------------------------------------------
@@ -300,11 +308,12 @@ def mamba2_flush(desc, state, cursor_in, cursor_out, A, err_flags=None, stream=N
 
 
 def mamba2_spec_verify(desc, state, head, committed, n_pos, x, z, B, C, dt_raw, dt_bias, A, D, out,
-                       flushed, err_flags=None, stream=None):
+                       flushed, err_flags=None, stream=None, n_pos_seq=None):
     io = desc.torch_io
     st = lib().replayssm_mamba2_spec_verify(
         ctypes.byref(desc.c()), ctypes.byref(state.c()),
         _ptr(head, torch.int32, "head"), _ptr(committed, torch.int32, "committed"), int(n_pos),
+        _ptr(n_pos_seq, torch.int32, "n_pos_seq"),
         _ptr(x, io, "x"), _ptr(z, io, "z"), _ptr(B, io, "B"), _ptr(C, io, "C"), _ptr(dt_raw, io, "dt_raw"),
         _ptr(dt_bias, torch.float32, "dt_bias"), _ptr(A, torch.float32, "A"), _ptr(D, torch.float32, "D"),
         _ptr(out, torch.float32, "out"), _ptr(flushed, torch.int32, "flushed"),
@@ -312,10 +321,12 @@ def mamba2_spec_verify(desc, state, head, committed, n_pos, x, z, B, C, dt_raw, 
     _check(st, "replayssm_mamba2_spec_verify")
 
 
-def commit(batch, buffer_len, n_pos, head, committed, flushed, n_keep, err_flags=None, stream=None):
+def commit(batch, buffer_len, n_pos, head, committed, flushed, n_keep, err_flags=None, stream=None,
+           n_pos_seq=None):
     st = lib().replayssm_commit(int(batch), int(buffer_len), int(n_pos),
                                 _ptr(head, torch.int32, "head"), _ptr(committed, torch.int32, "committed"),
                                 _ptr(flushed, torch.int32, "flushed"), _ptr(n_keep, torch.int32, "n_keep"),
+                                _ptr(n_pos_seq, torch.int32, "n_pos_seq"),
                                 _ptr(err_flags, torch.int32, "err_flags"), _stream(stream))
     _check(st, "replayssm_commit")
 
@@ -370,11 +381,12 @@ def gdn_flush(desc, state, cursor_in, cursor_out, err_flags=None, stream=None):
 
 
 def gdn_spec_verify(desc, state, head, committed, n_pos, q, k, v, alpha, beta, out, flushed,
-                    err_flags=None, stream=None):
+                    err_flags=None, stream=None, n_pos_seq=None):
     io = desc.torch_io
     st = lib().replayssm_gdn_spec_verify(
         ctypes.byref(desc.c()), ctypes.byref(state.c()),
         _ptr(head, torch.int32, "head"), _ptr(committed, torch.int32, "committed"), int(n_pos),
+        _ptr(n_pos_seq, torch.int32, "n_pos_seq"),
         _ptr(q, io, "q"), _ptr(k, io, "k"), _ptr(v, io, "v"),
         _ptr(alpha, torch.float32, "alpha"), _ptr(beta, torch.float32, "beta"),
         _ptr(out, torch.float32, "out"), _ptr(flushed, torch.int32, "flushed"),

@@ -31,10 +31,17 @@
  *   is launched and nothing is written.  REPLAYSSM_ERR_HIP reports a launch failure
  *   (hipGetLastError) after the enqueue.
  * - Device-side errors: `err_flags` (may be NULL) points to one int32 word.  A
- *   kernel that meets a cursor outside its documented range ORs
- *   REPLAYSSM_DEVERR_CURSOR into it, skips that sequence (its outputs, records and
- *   checkpoint are left untouched) and copies the bad cursor to the output cursor
- *   unchanged.  The caller clears the word.
+ *   kernel that meets a cursor or position count outside its documented range ORs
+ *   REPLAYSSM_DEVERR_CURSOR into it (a state slot out of range: REPLAYSSM_DEVERR_SLOT),
+ *   skips that sequence (its outputs, records and checkpoint are left untouched,
+ *   flushed[b] = 0) and copies the cursor to the output cursor unchanged.  The
+ *   caller clears the word.
+ * - State slots (serving): a state struct may carry `slot`, a device array [batch]
+ *   mapping each batch row to a row of the state arrays, which then have num_slots
+ *   rows (a pool).  slot[b] == -1 marks a pad row: it is skipped like a bad one but
+ *   without an error.  Inputs, outputs and cursors stay indexed by batch row.  Two
+ *   batch rows must not name the same slot in one call.  slot == NULL is the
+ *   identity (the state arrays have batch rows).
  * - Reentrancy: functions are reentrant and thread-safe; calls on one stream are
  *   ordered by the stream.
  * - Determinism: reductions use no atomics; the same inputs give bit-identical
@@ -64,7 +71,7 @@ typedef enum {
     REPLAYSSM_FP8_E4M3 = 3  /* read copies only: OCP 8-bit float with a scale per row */
 } replayssm_dtype;
 
-enum { REPLAYSSM_DEVERR_CURSOR = 1 };
+enum { REPLAYSSM_DEVERR_CURSOR = 1, REPLAYSSM_DEVERR_SLOT = 2 };
 
 /* Largest buffer length (window L) the kernels accept. */
 #define REPLAYSSM_MAX_BUFFER_LEN 64
@@ -128,6 +135,8 @@ typedef struct {
     float* rec_dt;
     replayssm_dtype lp_dtype;
     float* lp_scale;
+    const int32_t* slot;   /* [batch] state row of each batch row, -1 = pad; or NULL */
+    int32_t num_slots;     /* rows of the state arrays when slot is set */
 } replayssm_mamba2_state;
 
 /*
@@ -217,11 +226,15 @@ replayssm_status replayssm_mamba2_flush(const replayssm_mamba2_desc* desc,
  *   x, z   io [batch, n_pos, nheads, headdim];  B, C io [batch, n_pos, ngroups, dstate];
  *   dt_raw io [batch, n_pos, nheads];  out f32 [batch, n_pos, nheads, headdim];
  *   flushed int32 [batch] written;  head, committed int32 [batch] read only.
+ *   n_pos_seq int32 [batch] or NULL: positions of each sequence this round
+ *   (0 <= n_pos_seq[b] <= n_pos; the fold rule uses it in place of n_pos).  Inputs
+ *   past a sequence's count are ignored and its outputs there are not written; a
+ *   sequence with 0 positions is a pad row (skipped, flushed[b] = 0).
  */
 replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
                                               const replayssm_mamba2_state* state,
                                               const int32_t* head, const int32_t* committed,
-                                              int32_t n_pos,
+                                              int32_t n_pos, const int32_t* n_pos_seq,
                                               const void* x, const void* z, const void* B,
                                               const void* C, const void* dt_raw,
                                               const float* dt_bias, const float* A,
@@ -231,15 +244,20 @@ replayssm_status replayssm_mamba2_spec_verify(const replayssm_mamba2_desc* desc,
 /*
  * Apply a verified round: for each b, if flushed[b] then head[b] = (head[b] +
  * committed[b]) % buffer_len and committed[b] = 0; then committed[b] += n_keep[b].
- * n_keep[b] (1 <= n_keep <= n_pos) is the kept prefix (last accepted token plus the
- * accepted drafts).  Rejected records are dropped by not counting them; no state
- * is touched.  A sequence whose n_keep is out of range or whose result would exceed
- * buffer_len is left unchanged and REPLAYSSM_DEVERR_CURSOR is ORed into err_flags.
- *   head, committed int32 [batch] read-write;  flushed, n_keep int32 [batch].
+ * n_keep[b] (1 <= n_keep <= n_pos, or <= n_pos_seq[b] when given) is the kept prefix
+ * (last accepted token plus the accepted drafts).  Rejected records are dropped by
+ * not counting them; no state is touched.  A sequence with n_pos_seq[b] == 0 (a pad
+ * row) is left unchanged; rows that a state-slot map marks as pads should pass 0
+ * here too, since this call sees no slot map.  A sequence whose n_keep is out of range or whose result
+ * would exceed buffer_len is left unchanged and REPLAYSSM_DEVERR_CURSOR is ORed into
+ * err_flags.
+ *   head, committed int32 [batch] read-write;  flushed, n_keep int32 [batch];
+ *   n_pos_seq int32 [batch] or NULL, as passed to the verify call.
  */
 replayssm_status replayssm_commit(int32_t batch, int32_t buffer_len, int32_t n_pos,
                                   int32_t* head, int32_t* committed, const int32_t* flushed,
-                                  const int32_t* n_keep, int32_t* err_flags, hipStream_t stream);
+                                  const int32_t* n_keep, const int32_t* n_pos_seq, int32_t* err_flags,
+                                  hipStream_t stream);
 
 /*
  * Reset cursors for new sequences: head[b] = 0 (when head is not NULL) and
@@ -302,6 +320,7 @@ typedef struct {
  *   rec_v      io  [batch, num_v_heads, buffer_len, dv]
  *   rec_alpha  f32 [batch, num_v_heads, buffer_len]
  *   rec_beta   f32 [batch, num_v_heads, buffer_len]
+ *   slot, num_slots  state-slot map as for Mamba2 (NULL: identity)
  */
 typedef struct {
     float* ckpt;
@@ -309,6 +328,8 @@ typedef struct {
     void* rec_v;
     float* rec_alpha;
     float* rec_beta;
+    const int32_t* slot;
+    int32_t num_slots;
 } replayssm_gdn_state;
 
 /*
@@ -356,11 +377,13 @@ replayssm_status replayssm_gdn_flush(const replayssm_gdn_desc* desc, const repla
  *   out f32 [batch, n_pos, num_v_heads, dv];  flushed int32 [batch] written;
  *   head, committed int32 [batch] read only.  1 <= n_pos <= buffer_len; shapes
  *   whose staging exceeds one workgroup's LDS give REPLAYSSM_ERR_UNSUPPORTED.
+ *   n_pos_seq int32 [batch] or NULL: positions of each sequence, as for Mamba2.
  *   Invalid cursors: REPLAYSSM_DEVERR_CURSOR is ORed into err_flags and that
  *   sequence's outputs, records, checkpoint and flushed[b] are left untouched.
  */
 replayssm_status replayssm_gdn_spec_verify(const replayssm_gdn_desc* desc, const replayssm_gdn_state* state,
                                            const int32_t* head, const int32_t* committed, int32_t n_pos,
+                                           const int32_t* n_pos_seq,
                                            const void* q, const void* k, const void* v,
                                            const float* alpha, const float* beta, float* out,
                                            int32_t* flushed, int32_t* err_flags, hipStream_t stream);

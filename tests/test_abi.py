@@ -57,7 +57,7 @@ def test_status_strings_and_version(L):
     assert rs.status_string(2) == "unsupported shape"
     assert rs.status_string(3) == "HIP launch failure"
     assert rs.status_string(99) == "unknown status"
-    assert rs.version() == 100
+    assert rs.version() == 200
 
 
 # fake, 256-byte aligned device addresses (never dereferenced)
@@ -128,6 +128,15 @@ def test_mamba2_read_copy_kinds(L):
     # without a read copy its dtype and scales are ignored
     assert decode(L, state=m2state(lp_dtype=9), x=None, **ok) == INV     # still rejected for x only
     assert rs.Mamba2StateC.lp_dtype.offset == 40 and rs.Mamba2StateC.lp_scale.offset == 48
+    assert rs.Mamba2StateC.slot.offset == 56 and rs.Mamba2StateC.num_slots.offset == 64
+    assert rs.GdnStateC.slot.offset == 40 and rs.GdnStateC.num_slots.offset == 48
+
+
+def test_state_slot_validation(L):
+    ok = dict(cout=fake(6))
+    assert decode(L, state=m2state(slot=fake(22), num_slots=0), **ok) == INV
+    assert decode(L, state=m2state(slot=fake(22) + 2, num_slots=8), **ok) == INV
+    assert decode(L, state=m2state(slot=fake(22), num_slots=1 << 30), **ok) == INV
 
 
 def test_mamba2_window_limit_is_unsupported(L):
@@ -142,8 +151,8 @@ def test_mamba2_flush_and_spec_validation(L):
     assert L.replayssm_mamba2_flush(ctypes.byref(d), ctypes.byref(s), fake(5), fake(5), fake(13), None, None) == INV
     assert L.replayssm_mamba2_flush(ctypes.byref(d), ctypes.byref(s), fake(5), fake(6), None, None, None) == INV
 
-    def spec(n_pos, head=fake(5), com=fake(6), flushed=fake(17), x=fake(7)):
-        return L.replayssm_mamba2_spec_verify(ctypes.byref(d), ctypes.byref(s), head, com, n_pos, x, fake(8),
+    def spec(n_pos, head=fake(5), com=fake(6), flushed=fake(17), x=fake(7), nps=None):
+        return L.replayssm_mamba2_spec_verify(ctypes.byref(d), ctypes.byref(s), head, com, n_pos, nps, x, fake(8),
                                               fake(9), fake(10), fake(11), fake(12), fake(13), fake(14),
                                               fake(15), flushed, None, None)
     assert spec(0, x=None) == INV
@@ -151,16 +160,18 @@ def test_mamba2_flush_and_spec_validation(L):
     assert spec(4, head=fake(6), x=None) == INV
     assert spec(4, flushed=fake(5), x=None) == INV
     assert spec(0) == INV and spec(17) == INV and spec(4, head=fake(6)) == INV and spec(4, flushed=fake(6)) == INV
+    assert spec(4, nps=fake(18) + 2) == INV                                       # misaligned counts
 
 
 def test_cursor_call_validation(L):
     C = L.replayssm_commit
-    assert C(0, 16, 4, fake(1), fake(2), fake(3), fake(4), None, None) == INV
-    assert C(4, 0, 1, fake(1), fake(2), fake(3), fake(4), None, None) == INV
-    assert C(4, 16, 17, fake(1), fake(2), fake(3), fake(4), None, None) == INV
-    assert C(4, 16, 0, fake(1), fake(2), fake(3), fake(4), None, None) == INV
-    assert C(4, 16, 4, fake(1), fake(1), fake(3), fake(4), None, None) == INV
-    assert C(4, 16, 4, fake(1), fake(2), None, fake(4), None, None) == INV
+    assert C(0, 16, 4, fake(1), fake(2), fake(3), fake(4), None, None, None) == INV
+    assert C(4, 0, 1, fake(1), fake(2), fake(3), fake(4), None, None, None) == INV
+    assert C(4, 16, 17, fake(1), fake(2), fake(3), fake(4), None, None, None) == INV
+    assert C(4, 16, 0, fake(1), fake(2), fake(3), fake(4), None, None, None) == INV
+    assert C(4, 16, 4, fake(1), fake(1), fake(3), fake(4), None, None, None) == INV
+    assert C(4, 16, 4, fake(1), fake(2), None, fake(4), None, None, None) == INV
+    assert C(4, 16, 4, fake(1), fake(2), fake(3), fake(4), fake(5) + 1, None, None) == INV
     R = L.replayssm_reset_cursors
     assert R(0, fake(1), fake(2), None, 0, None) == INV
     assert R(4, fake(1), None, None, 0, None) == INV
@@ -202,7 +213,7 @@ def test_gdn_validation(L):
                                                fake(11), fake(12), fake(13), None) == INV
 
     def spec(desc, hd=fake(6), cm=fake(7), n_pos=4, fl=fake(14)):
-        return L.replayssm_gdn_spec_verify(ctypes.byref(desc), ctypes.byref(s), hd, cm, n_pos, fake(8), fake(9),
+        return L.replayssm_gdn_spec_verify(ctypes.byref(desc), ctypes.byref(s), hd, cm, n_pos, None, fake(8), fake(9),
                                            fake(10), fake(11), fake(12), fake(13), fl, None, None)
     assert spec(gdesc(), n_pos=0) == INV
     assert spec(gdesc(), n_pos=17) == INV                    # beyond buffer_len
