@@ -47,7 +47,7 @@ HEADLINE = "mamba2_h128"
 KERNEL_SOURCES = ["hybrid_model_ssm_amd/csrc/mamba2_kernels.h", "hybrid_model_ssm_amd/csrc/device_common.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_pmc.txt")
 STATS_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_kernel_stats.txt")
-REPLAY_KERNEL_TAG = "mamba2_replay_kernel<64, 128, unsigned short, false, 0>"
+REPLAY_KERNEL_TAG = "mamba2_replay_kernel<64, 128, unsigned short, 0, 0>"
 COPY_BYTES = 1 << 30
 MiB = float(1 << 20)
 
