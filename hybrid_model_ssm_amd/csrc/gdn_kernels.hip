@@ -29,6 +29,8 @@ constexpr int kGdnDecode = 0;
 constexpr int kGdnFold = 1;
 constexpr int kGdnSpec = 2;
 constexpr int kGdnMaxVHeads = 4;   // value heads per workgroup
+constexpr int kGdnFoldChunk = 16;  // records folded together in matrix form
+constexpr size_t kGdnMaxSmemBytes = 64 * 1024;
 
 template <int DK>
 struct GdnShape {
@@ -41,19 +43,31 @@ struct GdnShape {
 // LDS layout (4-byte words) of the replay kernel.  NR bounds the window rows (stored
 // records plus this call's positions), T1 the positions.
 struct GdnSmem {
-    int NR, T1, oK, oV, oAl, oBe, oQ, oU, oCoef, oAcc, total;
+    int NR, T1, oK, oV, oAl, oBe, oQ, oU, oCoef, oAcc;
+    int oKp, oCv, oNm, oPf, oGs, oDc, oCw, total;
     __host__ __device__ GdnSmem(int DK, int DV, int L, int T, int mode, int NV, int io_bytes) {
         NR = (mode == kGdnSpec) ? L + T : L;
         T1 = T > 1 ? T : 1;
-        oK = 0;                                    // [NR][DK]      k rows of the window
-        oV = oK + NR * DK;                         // [NV][NR][DV]  v rows (io dtype)
+        oK = 0;                                    // [NR][DK]      k rows of the window (io dtype)
+        oV = oK + (NR * DK * io_bytes + 3) / 4;    // [NV][NR][DV]  v rows (io dtype)
         oAl = oV + (NV * NR * DV * io_bytes + 3) / 4;   // [NV][NR]
         oBe = oAl + NV * NR;                       // [NV][NR]
         oQ = oBe + NV * NR;                        // [T1][DK]
         oU = oQ + T1 * DK;                         // [NV][T1][DK]  carried-back q
         oCoef = oU + NV * T1 * DK;                 // [NV][T1][NR]  beta_s kappa_s
         oAcc = oCoef + NV * T1 * NR;               // [NV][T1][DV]  sum_s beta_s kappa_s v_s
-        total = oAcc + NV * T1 * DV;
+        // fold in matrix form, one value head at a time (see the fold branch)
+        constexpr int CH = kGdnFoldChunk;
+        oKp = oAcc + NV * T1 * DV;                 // [L][DK]   K' rows of every chunk
+        oCv = oKp + L * DK;                        // [L][DV]   record part of the fold factors
+        oPf = oCv + L * DV;                        // [L]       decay products before each record
+        oGs = oPf + L;                             // [L]       decay products after each record
+        oDc = oGs + L;                             // [L/CH+1]  decay of each chunk
+        // [4][16][CH] fold factors of each wave's rows while tiles are folded; the same
+        // words hold the [CH][CH] coupling of one chunk's records while K' is formed
+        oCw = oDc + L / CH + 1;
+        oNm = oCw;
+        total = oCw + (kGdnThreads / 64) * 16 * CH;
     }
 };
 
@@ -143,7 +157,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
 
     const GdnSmem lay(DK, DV, L, T, MODE, a.vheads_per_chunk, (int)sizeof(IO));
     const int NR = lay.NR, T1 = lay.T1;
-    float* sK = smem + lay.oK;
+    IO* sK = reinterpret_cast<IO*>(smem + lay.oK);   // exact copies of the k rows
     IO* sV = reinterpret_cast<IO*>(smem + lay.oV);
     float* sAl = smem + lay.oAl;
     float* sBe = smem + lay.oBe;
@@ -191,7 +205,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         const int s = task / DK4, j4 = task % DK4;
         const Raw4 r = (s < nstored) ? io::ldraw4(recK, (size_t)slot_of(s) * DK + 4 * j4)
                                      : io::ldraw4(kin, pos_qk(s - nstored) + 4 * j4);
-        *reinterpret_cast<float4*>(sK + s * DK + 4 * j4) = io::cvt4(r);
+        *reinterpret_cast<Raw4*>(sK + s * DK + 4 * j4) = r;
     }
     for (int task = tid; task < nv * nrec * DV4; task += kGdnThreads) {
         const int i4 = task % DV4;
@@ -244,7 +258,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 for (int cc = 0; cc < TC; ++cc) {
                     kap[cc] = 0.f;
 #pragma unroll
-                    for (int m = 0; m < UPL; ++m) kap[cc] += sK[s * DK + lane + m * kWave] * u[cc][m];
+                    for (int m = 0; m < UPL; ++m) kap[cc] += io::ld(sK, s * DK + lane + m * kWave) * u[cc][m];
                 }
 #pragma unroll
                 for (int cc = 0; cc < TC; ++cc) kap[cc] = group_allreduce<kWave>(kap[cc], lane);
@@ -257,7 +271,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                     if (lane == 0 && j0 + cc < Tb) sCoef[(vl * T1 + j) * NR + s] = bk;
                     if (on) {
 #pragma unroll
-                        for (int m = 0; m < UPL; ++m) u[cc][m] = as * (u[cc][m] - bk * sK[s * DK + lane + m * kWave]);
+                        for (int m = 0; m < UPL; ++m) u[cc][m] = as * (u[cc][m] - bk * io::ld(sK, s * DK + lane + m * kWave));
                     }
                 }
             }
@@ -331,36 +345,144 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         }
         outputs(nunit - 1, va);
     } else if (!idle) {
-        // ---- fold rows [0, nf) into the checkpoint row by row, oldest first -------------
-        auto body = [&](int u) {
-            const int vl = u / NTILE, tl = u % NTILE;
+        // ---- fold rows [0, nf) into the checkpoint -----------------------------------------
+        // Matrix form over chunks of up to CH records (s = 0..nc-1 within a chunk, oldest
+        // first).  Each record updates every row r of the tile as
+        //     r <- a_s r + e_s k_s,   e_s = beta_s v_s[i] - a_s beta_s (r . k_s)
+        // with a_s = alpha_s, so after the chunk
+        //     r <- P r + sum_t c_t k_t,   c = Cv[i] - K' r0,
+        // where P is the chunk's decay, K' = G W D K and Cv = G W diag(beta) V for the
+        // unit lower triangular W = (I + Nm)^-1, Nm[s][t] = a_s beta_s (prod_{t<u<s} a_u)
+        // (k_t . k_s) for t < s, D = diag(a_s beta_s prod_{u<s} a_u), G = diag(prod_{u>t}
+        // a_u).  K' and Cv are formed once per value head by forward substitution, one
+        // column per thread; each tile then needs nc independent row dots (one batched
+        // transpose-reduce per 4 records) and a rank-nc update, instead of nc sequential
+        // row all-reduces.
+        constexpr int CH = kGdnFoldChunk;
+        constexpr int RGW = kWave / LPR;            // row groups of one wave
+        const int nch = (nf + CH - 1) / CH;
+        float* sKp = smem + lay.oKp;
+        float* sCv = smem + lay.oCv;
+        float* sNm = smem + lay.oNm;
+        float* sPf = smem + lay.oPf;
+        float* sGs = smem + lay.oGs;
+        float* sDc = smem + lay.oDc;
+        float* sCw = smem + lay.oCw + wave * (16 * CH);
+        const int rg = lane / LPR;
+        auto wave_sync = [&]() {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        auto prepare = [&](int vl) {               // K' and Cv of every chunk of value head vl
             const float* al = sAl + vl * NR;
             const float* be = sBe + vl * NR;
-            for (int s = 0; s < nf; ++s) {
-                const float4 Kv = *reinterpret_cast<const float4*>(sK + s * DK + 4 * col4);
-                float d[R];
+            for (int ch = 0; ch < nch; ++ch) {
+                const int s0 = ch * CH, nc = min(CH, nf - s0);
+                __syncthreads();                    // earlier readers of sNm, sKp, sCv are done
+                if (tid == 0) {
+                    float pf = 1.f;
+                    for (int x = 0; x < nc; ++x) {
+                        sPf[s0 + x] = pf;
+                        pf *= al[s0 + x];
+                    }
+                    sDc[ch] = pf;
+                    float gs = 1.f;
+                    for (int x = nc - 1; x >= 0; --x) {
+                        sGs[s0 + x] = gs;
+                        gs *= al[s0 + x];
+                    }
+                }
+                __syncthreads();
+                for (int pr = tid; pr < CH * CH; pr += kGdnThreads) {
+                    const int sr = pr / CH, tr = pr % CH;
+                    if (tr < sr && sr < nc) {
+                        float m = 0.f;
+                        for (int jj = 0; jj < DK4; ++jj) {
+                            const int j4 = (jj + pr) % DK4;     // rotated start: fewer bank conflicts
+                            m += dot4(io::ld4(sK, (s0 + sr) * DK + 4 * j4), io::ld4(sK, (s0 + tr) * DK + 4 * j4));
+                        }
+                        sNm[sr * CH + tr] = al[s0 + sr] * be[s0 + sr] * (sPf[s0 + sr] / sPf[s0 + tr + 1]) * m;
+                    }
+                }
+                __syncthreads();
+                if (tid < DK + DV) {
+                    float z[CH];
 #pragma unroll
-                for (int k = 0; k < R; ++k) d[k] = dot4(va[k], Kv);
-                row_allreduce<R, LPR>(d, lane);
-                const float as = al[s], bs = be[s];
+                    for (int x = 0; x < CH; ++x) {
+                        if (x < nc) {
+                            const int sx = s0 + x;
+                            float acc = (tid < DK) ? al[sx] * be[sx] * sPf[sx] * io::ld(sK, sx * DK + tid)
+                                                   : be[sx] * io::ld(sV, (vl * NR + sx) * DV + tid - DK);
 #pragma unroll
-                for (int k = 0; k < R; ++k) {
-                    const float bd = bs * d[k];
-                    const float bv = bs * io::ld(sV, (vl * NR + s) * DV + tl * DVT + row0 + k * RPP);
-                    va[k].x = as * (va[k].x - bd * Kv.x) + bv * Kv.x;
-                    va[k].y = as * (va[k].y - bd * Kv.y) + bv * Kv.y;
-                    va[k].z = as * (va[k].z - bd * Kv.z) + bv * Kv.z;
-                    va[k].w = as * (va[k].w - bd * Kv.w) + bv * Kv.w;
+                            for (int y = 0; y < x; ++y) acc -= sNm[x * CH + y] * z[y];
+                            z[x] = acc;
+                        }
+                    }
+#pragma unroll
+                    for (int x = 0; x < CH; ++x) {
+                        if (x < nc) {
+                            const float v = sGs[s0 + x] * z[x];
+                            if (tid < DK) sKp[(s0 + x) * DK + tid] = v;
+                            else sCv[(s0 + x) * DV + tid - DK] = v;
+                        }
+                    }
                 }
             }
-            const size_t t = tile_base(u);
+            __syncthreads();
+        };
+        auto body = [&](int u) {
+            const int vl = u / NTILE, tl = u % NTILE;
+            (void)vl;
+            for (int ch = 0; ch < nch; ++ch) {
+                const int s0 = ch * CH, nc = min(CH, nf - s0);
+                // fold factors c[row][t] = Cv - K'_t . row, FB records per transpose-reduce
+                // (value v of the FB*R is held by LPR/(FB*R) lanes)
+                constexpr int FB = 2;
+                for (int g4 = 0; FB * g4 < nc; ++g4) {
+                    float acc[R * FB];
 #pragma unroll
-            for (int k = 0; k < R; ++k) st_stream(a.ckpt + t + (size_t)k * RPP * DK, va[k]);
+                    for (int jj = 0; jj < FB; ++jj) {
+                        const int t = min(FB * g4 + jj, nc - 1);
+                        const float4 Kp = *reinterpret_cast<const float4*>(sKp + (s0 + t) * DK + 4 * col4);
+#pragma unroll
+                        for (int k = 0; k < R; ++k) acc[jj * R + k] = dot4(va[k], Kp);
+                    }
+                    const float r = row_reduce<R * FB, LPR>(acc, lane);
+                    const int vi = q / (LPR / (R * FB));
+                    const int t = FB * g4 + vi / R, k = vi % R;
+                    if (t < nc && q % (LPR / (R * FB)) == 0) {
+                        const int i = tl * DVT + row0 + k * RPP;
+                        sCw[(rg + RGW * k) * CH + t] = sCv[(s0 + t) * DV + i] - r;
+                    }
+                }
+                wave_sync();
+                const float dc = sDc[ch];
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    va[k].x *= dc; va[k].y *= dc; va[k].z *= dc; va[k].w *= dc;
+                }
+                // rank-nc update; the fold factors of a row are read by all its lanes at once
+                for (int t = 0; t < nc; ++t) {
+                    const float4 Kv = io::ld4(sK, (s0 + t) * DK + 4 * col4);
+#pragma unroll
+                    for (int k = 0; k < R; ++k) {
+                        const float c = sCw[(rg + RGW * k) * CH + t];
+                        va[k].x += c * Kv.x; va[k].y += c * Kv.y; va[k].z += c * Kv.z; va[k].w += c * Kv.w;
+                    }
+                }
+                wave_sync();                        // these reads precede the next chunk's writes
+            }
+            const size_t tb = tile_base(u);
+#pragma unroll
+            for (int k = 0; k < R; ++k) st_stream(a.ckpt + tb + (size_t)k * RPP * DK, va[k]);
             outputs(u, va);
         };
+        prepare(0);
         for (int u = 0; u + 1 < nunit; ++u) {
             issue_tile(u + 1, vb);
             body(u);
+            if ((u + 1) % NTILE == 0) prepare((u + 1) / NTILE);
             rotate();
         }
         body(nunit - 1);
@@ -535,16 +657,25 @@ bool gdn_shape_supported(int dk, int dv) {
     return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
 }
 
-static void gdn_chunking(int rv, int* nchunk, int* per) {
-    *per = rv < kGdnMaxVHeads ? rv : kGdnMaxVHeads;
-    *nchunk = (rv + *per - 1) / *per;
+static int gdn_positions(int mode, int n_pos) {
+    return (mode == kGdnSpec) ? n_pos : (mode == kGdnDecode ? 1 : 0);
+}
+
+// Value heads per workgroup: up to kGdnMaxVHeads, fewer when one workgroup's LDS
+// staging would not fit; the last chunk of a q/k head takes the remainder.
+static void gdn_chunking(int dk, int dv, int L, int rv, int mode, int n_pos, int io_bytes, int* nchunk,
+                         int* per) {
+    const int T = gdn_positions(mode, n_pos);
+    int p = rv < kGdnMaxVHeads ? rv : kGdnMaxVHeads;
+    while (p > 1 && sizeof(float) * (size_t)GdnSmem(dk, dv, L, T, mode, p, io_bytes).total > kGdnMaxSmemBytes) --p;
+    *per = p;
+    *nchunk = (rv + p - 1) / p;
 }
 
 size_t gdn_smem_bytes(int dk, int dv, int L, int rv, int mode, int n_pos, int io_bytes) {
     int nchunk, per;
-    gdn_chunking(rv, &nchunk, &per);
-    const int T = (mode == kGdnSpec) ? n_pos : (mode == kGdnDecode ? 1 : 0);
-    return sizeof(float) * (size_t)GdnSmem(dk, dv, L, T, mode, per, io_bytes).total;
+    gdn_chunking(dk, dv, L, rv, mode, n_pos, io_bytes, &nchunk, &per);
+    return sizeof(float) * (size_t)GdnSmem(dk, dv, L, gdn_positions(mode, n_pos), mode, per, io_bytes).total;
 }
 
 template <int DK, int DV, typename IO>
@@ -567,9 +698,10 @@ hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t str
     if (a.dk == 128 && a.dv == 128) fn = gdn_pick<128, 128>(io, mode);
     if (!fn) return hipErrorInvalidValue;
     GdnArgs args = a;
-    gdn_chunking(a.hv / a.hk, &args.nchunk, &args.vheads_per_chunk);
     if (mode != kGdnSpec) args.n_pos = (mode == kGdnDecode) ? 1 : 0;
-    const size_t smem = gdn_smem_bytes(a.dk, a.dv, a.L, a.hv / a.hk, mode, args.n_pos, io == kIoBF16 ? 2 : 4);
+    const int io_bytes = io == kIoBF16 ? 2 : 4;
+    gdn_chunking(a.dk, a.dv, a.L, a.hv / a.hk, mode, args.n_pos, io_bytes, &args.nchunk, &args.vheads_per_chunk);
+    const size_t smem = gdn_smem_bytes(a.dk, a.dv, a.L, a.hv / a.hk, mode, args.n_pos, io_bytes);
     void* kargs[] = {&args};
     const dim3 grid((unsigned)((size_t)a.batch * a.hk * args.nchunk));
     hipError_t e = hipLaunchKernel(fn, grid, dim3(kGdnThreads), kargs, smem, stream);
