@@ -97,9 +97,13 @@ struct GroupSmem {
     }
 };
 
-// LP: kind of low-precision read copy (kLpNone, kLpBF16, kLpF16, kLpFP8)
+// LP: kind of low-precision read copy (kLpNone, kLpBF16, kLpF16, kLpFP8).  Decode steps
+// that read a copy stream half or a quarter of the fp32 bytes per tile and are held to
+// four waves per SIMD (measured faster despite a few spilled registers); the other
+// instances keep the register budget the compiler picks.
 template <int P, int N, typename IO, int LP, int MODE>
-__global__ void __launch_bounds__(kThreads) mamba2_replay_kernel(Mamba2Args a) {
+__global__ void __launch_bounds__(kThreads, (LP != kLpNone && MODE == kDecode) ? 4 : 1)
+mamba2_replay_kernel(Mamba2Args a) {
     constexpr bool LOWP = LP != kLpNone;
     using io = Io<IO>;
     using Raw4 = typename io::Raw4;
