@@ -150,3 +150,19 @@ def test_gdn_L1_equals_conventional_kernel():
         c = gpu.conventional(s)
         assert_fp32_close(o.cpu().numpy(), c.cpu().numpy(), f"step {t}", rel=1e-5)
         assert_fp32_close(gpu.state.ckpt.cpu().numpy(), gpu.conv_state.cpu().numpy(), f"state {t}", rel=1e-5)
+
+
+def test_gdn_largest_window_L64():
+    B, HV, HK, dk, dv, L = 2, 2, 1, 64, 64, 64
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=33)
+    st = gen.static
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    gpu = GpuGdn(desc, st)
+    rep = og.GDNReplay(st.ckpt, L, HK)
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        ref, flushed = rep.step(**s)
+        assert_fp32_close(gpu.step(s).cpu().numpy(), ref, f"step {t}")
+        if flushed.all():
+            assert_fp32_close(gpu.state.ckpt.cpu().numpy(), rep.ckpt, f"checkpoint step {t}")
+    assert np.array_equal(gpu.cursor.cpu().numpy(), np.full(B, (2 * L + 1) % L, np.int32))

@@ -276,3 +276,21 @@ def test_explicit_flush_equals_conventional_state():
     ck = gpu.state.ckpt.clone()
     gpu.flush()  # empty buffer: checkpoint bit-unchanged
     assert torch.equal(gpu.state.ckpt, ck)
+
+
+def test_largest_window_L64():
+    """The largest buffer the library takes (L = 64) over two full windows."""
+    B, H, P, N, G, L = 2, 4, 64, 64, 1, 64
+    gen = _gen(B, H, P, N, G, "bf16", seed=17)
+    st = gen.static
+    desc = _desc(B, H, P, N, G, L, "bf16")
+    gpu = GpuMamba2(desc, st)
+    rep = om.Mamba2Replay(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        ref, flushed = rep.step(**s)
+        assert_fp32_close(gpu.step(s).cpu().numpy(), ref, f"step {t}")
+        assert np.array_equal(gpu.cursor.cpu().numpy(), rep.cursor.astype(np.int32))
+        if flushed.all():
+            assert_fp32_close(gpu.state.ckpt.cpu().numpy(), rep.ckpt, f"checkpoint step {t}")
+    assert gpu.err.item() == 0

@@ -193,3 +193,20 @@ def test_commit_rejects_out_of_range_and_reset():
     cur = torch.tensor([3, 4, 5, 6], dtype=torch.int32, device=DEV)
     rs.reset_cursors(B, None, cur)
     assert cur.cpu().tolist() == [0, 0, 0, 0]
+
+
+def test_spec_positions_equal_buffer_length():
+    """n_pos = L: every round after the first folds the committed records first."""
+    B, H, P, N, G, L, T = 3, 4, 64, 64, 1, 4, 4
+    gen, st, desc, gpu = _setup(B, H, P, N, G, L, seed=25, n_pos=T)
+    spec = om.Mamba2Spec(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    for r in range(10):
+        s = gen.step(n_pos=T)
+        n_keep = gen.accepted(T - 1) + 1
+        ref, fl_ref = spec.verify(**s)
+        assert_fp32_close(gpu.verify(s).cpu().numpy(), ref, f"round {r}")
+        assert np.array_equal(gpu.flushed.cpu().numpy(), fl_ref.astype(np.int32))
+        assert bool(fl_ref.all()) == (r > 0)
+        spec.commit(n_keep)
+        gpu.commit(n_keep)
+    assert gpu.err.item() == 0
