@@ -404,17 +404,21 @@ mamba2_replay_kernel(Mamba2Args a) {
                     }
                 }
             }
-            // rows before st (flushed windows) still need D x_j for position j's own row
-            for (int jj = 0; jj < jn; ++jj) {
-                const int j = j0 + jj;
-                const int o = (hl * T1 + j) * P + 4 * p4;
-                float4 yv = y[jj];
-                if (nstored + j < st) {     // empty window (AR flush step): only D x_j
-                    const float4 xj = io::cvt4(io::ldraw4(xrow(h, nstored + j), 4 * p4));
-                    yv = make_float4(Dh * xj.x, Dh * xj.y, Dh * xj.z, Dh * xj.w);
+            // rows before st (flushed windows) still need D x_j for position j's own row;
+            // a constant trip count keeps y[] in registers
+#pragma unroll
+            for (int jj = 0; jj < kPosBatch; ++jj) {
+                if (jj < jn) {
+                    const int j = j0 + jj;
+                    const int o = (hl * T1 + j) * P + 4 * p4;
+                    float4 yv = y[jj];
+                    if (nstored + j < st) {     // empty window (AR flush step): only D x_j
+                        const float4 xj = io::cvt4(io::ldraw4(xrow(h, nstored + j), 4 * p4));
+                        yv = make_float4(Dh * xj.x, Dh * xj.y, Dh * xj.z, Dh * xj.w);
+                    }
+                    *reinterpret_cast<float4*>(sY + o) = yv;
+                    *reinterpret_cast<Raw4*>(sZ + o) = io::ldraw4(zin, pos_x(h, j) + 4 * p4);
                 }
-                *reinterpret_cast<float4*>(sY + o) = yv;
-                *reinterpret_cast<Raw4*>(sZ + o) = io::ldraw4(zin, pos_x(h, j) + 4 * p4);
             }
         }
         __syncthreads();
