@@ -43,7 +43,7 @@ struct GdnShape {
 // LDS layout (4-byte words) of the replay kernel.  NR bounds the window rows (stored
 // records plus this call's positions), T1 the positions.
 struct GdnSmem {
-    int NR, T1, oK, oV, oAl, oBe, oQ, oU, oCoef, oAcc;
+    int NR, T1, oK, oV, oAl, oBe, oQ, oU, oAcc;
     int oKp, oCv, oNm, oPf, oGs, oDc, oCw, total;
     __host__ __device__ GdnSmem(int DK, int DV, int L, int T, int mode, int NV, int io_bytes) {
         NR = (mode == kGdnSpec) ? L + T : L;
@@ -54,8 +54,7 @@ struct GdnSmem {
         oBe = oAl + NV * NR;                       // [NV][NR]
         oQ = oBe + NV * NR;                        // [T1][DK]
         oU = oQ + T1 * DK;                         // [NV][T1][DK]  carried-back q
-        oCoef = oU + NV * T1 * DK;                 // [NV][T1][NR]  beta_s kappa_s
-        oAcc = oCoef + NV * T1 * NR;               // [NV][T1][DV]  sum_s beta_s kappa_s v_s
+        oAcc = oU + NV * T1 * DK;                  // [NV][T1][DV]  sum_s beta_s kappa_s v_s
         // fold in matrix form, one value head at a time (see the fold branch)
         constexpr int CH = kGdnFoldChunk;
         oKp = oAcc + NV * T1 * DV;                 // [L][DK]   K' rows of every chunk
@@ -163,7 +162,6 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     float* sBe = smem + lay.oBe;
     float* sQ = smem + lay.oQ;
     float* sU = smem + lay.oU;
-    float* sCoef = smem + lay.oCoef;
     float* sAcc = smem + lay.oAcc;
 
     const int row0 = tid / LPR;
@@ -238,6 +236,9 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     // ---- carry each position's q back through its window --------------------------------
     // Position j's chain covers rows nstored + j down to st.  A wave runs TC chains of
     // one value head in lockstep over the rows (they share k_s, alpha_s and beta_s).
+    // The record terms sum_s beta_s kappa_s v_s[i] ride along: beta_s kappa_s is the
+    // same in every lane after the all-reduce, and each lane adds its own columns i.
+    constexpr int VPL = DV / kWave;  // record-term columns per lane
     if (Tb > 0) {
         const int ngrp = (Tb + TC - 1) / TC;
         for (int task = wave; task < nv * ngrp; task += NWAVE) {
@@ -252,6 +253,11 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
             const float* al = sAl + vl * NR;
             const float* be = sBe + vl * NR;
             const int jtop = min(j0 + TC, Tb) - 1;
+            float acc[TC][VPL];
+#pragma unroll
+            for (int cc = 0; cc < TC; ++cc)
+#pragma unroll
+                for (int m = 0; m < VPL; ++m) acc[cc][m] = 0.f;
             for (int s = nstored + jtop; s >= st; --s) {
                 float kap[TC];
 #pragma unroll
@@ -263,12 +269,16 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
                 for (int cc = 0; cc < TC; ++cc) kap[cc] = group_allreduce<kWave>(kap[cc], lane);
                 const float as = al[s], bs = be[s];
+                float vs[VPL];
+#pragma unroll
+                for (int m = 0; m < VPL; ++m) vs[m] = io::ld(sV, (vl * NR + s) * DV + lane + m * kWave);
 #pragma unroll
                 for (int cc = 0; cc < TC; ++cc) {
                     const int j = min(j0 + cc, Tb - 1);
                     const bool on = s <= nstored + j;     // row s lies in position j's window
                     const float bk = on ? bs * kap[cc] : 0.f;
-                    if (lane == 0 && j0 + cc < Tb) sCoef[(vl * T1 + j) * NR + s] = bk;
+#pragma unroll
+                    for (int m = 0; m < VPL; ++m) acc[cc][m] += bk * vs[m];
                     if (on) {
 #pragma unroll
                         for (int m = 0; m < UPL; ++m) u[cc][m] = as * (u[cc][m] - bk * io::ld(sK, s * DK + lane + m * kWave));
@@ -280,18 +290,10 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 if (j0 + cc < Tb) {
 #pragma unroll
                     for (int m = 0; m < UPL; ++m) sU[(vl * T1 + j0 + cc) * DK + lane + m * kWave] = u[cc][m];
+#pragma unroll
+                    for (int m = 0; m < VPL; ++m) sAcc[(vl * T1 + j0 + cc) * DV + lane + m * kWave] = acc[cc][m];
                 }
             }
-        }
-        __syncthreads();
-        // ---- record terms sum_s beta_s kappa_s v_s[i] of every (value head, position) --
-        for (int task = tid; task < nv * Tb * DV; task += kGdnThreads) {
-            const int i = task % DV, vj = task / DV;
-            const int vl = vj / Tb, j = vj - vl * Tb;
-            float acc = 0.f;
-            for (int s = st; s <= nstored + j; ++s)
-                acc += sCoef[(vl * T1 + j) * NR + s] * io::ld(sV, (vl * NR + s) * DV + i);
-            sAcc[(vl * T1 + j) * DV + i] = acc;
         }
         __syncthreads();
     }
