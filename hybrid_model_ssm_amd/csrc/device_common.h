@@ -262,7 +262,7 @@ __device__ __forceinline__ float group_allreduce(float x, int lane) {
 // Maximum over an aligned group of W lanes, returned to all of them (same partners as
 // group_allreduce).
 template <int W>
-__device__ __forceinline__ float group_allmax(float x, int lane) {
+__device__ __forceinline__ float group_allmax(float x) {
     if constexpr (W >= 64) {
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
         x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -434,8 +434,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
             __syncthreads();
         };
         auto body = [&](int u) {
-            const int vl = u / NTILE, tl = u % NTILE;
-            (void)vl;
+            const int tl = u % NTILE;
             for (int ch = 0; ch < nch; ++ch) {
                 const int s0 = ch * CH, nc = min(CH, nf - s0);
                 // fold factors c[row][t] = Cv - K'_t . row, FB records per transpose-reduce

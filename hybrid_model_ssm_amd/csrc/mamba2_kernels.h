@@ -581,7 +581,7 @@ mamba2_replay_kernel(Mamba2Args a) {
                 if constexpr (LP == kLpFP8) {
                     if (store_lp) {
                         amax = fmaxf(fmaxf(fabsf(va[k].x), fabsf(va[k].y)), fmaxf(fabsf(va[k].z), fabsf(va[k].w)));
-                        amax = group_allmax<LPR>(amax, lane);
+                        amax = group_allmax<LPR>(amax);
                     }
                 }
                 if (!MASK || row0 + k * RPP < P) {
