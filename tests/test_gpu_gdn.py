@@ -166,3 +166,23 @@ def test_gdn_largest_window_L64():
         if flushed.all():
             assert_fp32_close(gpu.state.ckpt.cpu().numpy(), rep.ckpt, f"checkpoint step {t}")
     assert np.array_equal(gpu.cursor.cpu().numpy(), np.full(B, (2 * L + 1) % L, np.int32))
+
+
+def test_gdn_full_batch_small_heads():
+    """Every one of B=256 sequences (4 value heads, 2 q/k heads, dk = dv = 128, L=16)
+    for 2L+1 steps, two flushes included: outputs and flushed checkpoints of the whole
+    batch against the oracle."""
+    B, HV, HK, dk, dv, L = 256, 4, 2, 128, 128, 16
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=35)
+    st = gen.static
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    gpu = GpuGdn(desc, st)
+    rep = og.GDNReplay(st.ckpt, L, HK)
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        ref, flushed = rep.step(**s)
+        assert_fp32_close(gpu.step(s).cpu().numpy(), ref, f"step {t}")
+        if flushed.all():
+            assert_fp32_close(gpu.state.ckpt.cpu().numpy(), rep.ckpt, f"checkpoint step {t}")
+    assert np.array_equal(gpu.cursor.cpu().numpy(), np.full(B, (2 * L + 1) % L, np.int32))
+    assert gpu.err.item() == 0

@@ -199,3 +199,27 @@ def test_gdn_spec_rejects_bad_arguments():
                            z(2, 64, 2, 128, dt=torch.float32), z(2, 64, 8, 128, dt=torch.float32),
                            z(2, 64, 8, dt=torch.float32), z(2, 64, 8, dt=torch.float32),
                            z(2, 64, 8, 128, dt=torch.float32), fl)
+
+
+def test_gdn_spec_full_batch_small_heads():
+    """All B=256 sequences (4 value heads, 2 q/k heads, dk = dv = 128, L=16, 4
+    positions) for 10 rounds against the oracle."""
+    B, HV, HK, dk, dv, L, T = 256, 4, 2, 128, 128, 16, 4
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=45)
+    st = gen.static
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    gpu = GpuGdnSpec(desc, st, T)
+    spec = og.GDNSpec(st.ckpt, L, HK)
+    n_flush = 0
+    for r in range(10):
+        s = gen.step(n_pos=T)
+        n_keep = gen.accepted(T - 1) + 1
+        ref, fl_ref = spec.verify(**s)
+        assert_fp32_close(gpu.verify(s).cpu().numpy(), ref, f"round {r}")
+        assert np.array_equal(gpu.flushed.cpu().numpy(), fl_ref.astype(np.int32))
+        n_flush += int(fl_ref.sum())
+        spec.commit(n_keep)
+        gpu.commit(n_keep)
+        assert np.array_equal(gpu.head.cpu().numpy(), spec.head.astype(np.int32))
+        assert np.array_equal(gpu.committed.cpu().numpy(), spec.committed.astype(np.int32))
+    assert n_flush > B // 2 and gpu.err.item() == 0

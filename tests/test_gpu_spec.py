@@ -210,3 +210,24 @@ def test_spec_positions_equal_buffer_length():
         spec.commit(n_keep)
         gpu.commit(n_keep)
     assert gpu.err.item() == 0
+
+
+def test_spec_full_batch_small_heads():
+    """All B=256 sequences (H=8, G=2, P=64, N=128, L=16, 4 positions) for 10 rounds:
+    every output, flushed flag and cursor against the oracle."""
+    B, H, P, N, G, L, T = 256, 8, 64, 128, 2, 16, 4
+    gen, st, desc, gpu = _setup(B, H, P, N, G, L, seed=26)
+    spec = om.Mamba2Spec(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    n_flush = 0
+    for r in range(10):
+        s = gen.step(n_pos=T)
+        n_keep = gen.accepted(T - 1) + 1
+        ref, fl_ref = spec.verify(**s)
+        assert_fp32_close(gpu.verify(s).cpu().numpy(), ref, f"round {r}")
+        assert np.array_equal(gpu.flushed.cpu().numpy(), fl_ref.astype(np.int32))
+        n_flush += int(fl_ref.sum())
+        spec.commit(n_keep)
+        gpu.commit(n_keep)
+        assert np.array_equal(gpu.head.cpu().numpy(), spec.head.astype(np.int32))
+        assert np.array_equal(gpu.committed.cpu().numpy(), spec.committed.astype(np.int32))
+    assert n_flush > B // 2 and gpu.err.item() == 0
