@@ -35,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -52,11 +53,19 @@ COPY_BYTES = 1 << 30
 MiB = float(1 << 20)
 
 
+def _code_only(text):
+    """Source text without comments and blank space, so that editing a comment does not
+    mark counters taken on the same code as stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,16 +8,17 @@
 // the checkpoint S_c and a buffer of (k, v, alpha, beta) records.  Without forming
 // S_t, carry q back through the window, newest record first,
 //     kappa = k_s . u;   acc += beta_s kappa v_s;   u = alpha_s (u - beta_s kappa k_s),
-// so that S_t q = S_c u + acc.  The chain is sequential in s but only dk long; each
-// value head's chain runs on its own wave while the first checkpoint tile is in
-// flight.  The flush applies the window's updates to the checkpoint row by row (rows
-// are independent) and stores it once.
+// so that S_t q = S_c u + acc.  The chain is sequential in s but only dk long; the
+// chains run on the workgroup's waves while the first checkpoint tile is in flight.
+// The flush applies the window's updates to the checkpoint (rows are independent; the
+// updates of up to 16 records are applied together in matrix form, see the fold
+// branch) and stores it once.  Speculative verification runs one chain per position.
 //
 // Decomposition: the replay kernel runs one 256-thread workgroup per (sequence, q/k
-// head) and streams the [64, dk] tiles of that head's value heads (k records and q
-// are shared by them); the conventional kernel runs one workgroup per (sequence, value
-// head, 64-row tile).  dk/4 consecutive lanes cover one row of a tile with 16-byte
-// loads.
+// head, up to four of its value heads) and streams the [64, dk] tiles of those value
+// heads (k records and q are shared by them); the conventional kernel runs one
+// workgroup per (sequence, value head, 64-row tile).  dk/4 consecutive lanes cover one
+// row of a tile with 16-byte loads.
 
 #include "device_common.h"
 #include "launch.h"

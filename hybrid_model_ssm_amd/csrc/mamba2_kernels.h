@@ -26,7 +26,7 @@
 //
 // Modes share one kernel body:
 //   kDecode  one autoregressive step (flushes in place when the buffer fills)
-//   kFold    fold the stored records only (explicit flush / bf16 copy refresh)
+//   kFold    fold the stored records only (explicit flush / read-copy refresh)
 //   kSpec    speculative verification over n_pos positions on the circular buffer
 //            ("ReplaySSM" README, benefit "Cheap rollback": output-only verification,
 //            rejected inputs dropped by moving a pointer)

@@ -198,7 +198,7 @@ replayssm_status replayssm_mamba2_decode_state_and_output(const replayssm_mamba2
  * Fold the 0..L-1 records each sequence holds into its checkpoint (same fold as
  * the flush step, over the stored records only), refresh ckpt_lp when it is set,
  * and set cursor_out[b] = 0.  With c = 0 the checkpoint is left bit-unchanged and
- * only ckpt_lp is (re)created, which is how the bf16 copy is initialised.  Used to
+ * only ckpt_lp is (re)created, which is how a read copy is initialised.  Used to
  * hand a sequence's whole state over (checkpoint save, migration).
  *   cursor_in, cursor_out  int32 [batch], distinct;  A f32 [nheads].
  */

@@ -76,6 +76,13 @@ def test_bench_refuses_several_gpus():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) { return x + 1; }  // one\n/* two */"
+    b = "int f(int x) {\n  return x + 1;\n}  // changed comment"
+    c = "int f(int x) { return x + 2; }"
+    assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
+
+
 def test_committed_counter_summary_parses():
     traffic, src = bench.committed_traffic()
     assert traffic is None or traffic > 1e9
