@@ -45,7 +45,7 @@ struct GdnShape {
 // records plus this call's positions), T1 the positions.
 struct GdnSmem {
     int NR, T1, oK, oV, oAl, oBe, oQ, oU, oAcc;
-    int oKp, oCv, oNm, oPf, oGs, oDc, oCw, total;
+    int oKp, oCv, oNm, oPf, oGs, oDc, total;
     __host__ __device__ GdnSmem(int DK, int DV, int L, int T, int mode, int NV, int io_bytes) {
         NR = (mode == kGdnSpec) ? L + T : L;
         T1 = T > 1 ? T : 1;
@@ -63,11 +63,8 @@ struct GdnSmem {
         oPf = oCv + L * DV;                        // [L]       decay products before each record
         oGs = oPf + L;                             // [L]       decay products after each record
         oDc = oGs + L;                             // [L/CH+1]  decay of each chunk
-        // [4][16][CH] fold factors of each wave's rows while tiles are folded; the same
-        // words hold the [CH][CH] coupling of one chunk's records while K' is formed
-        oCw = oDc + L / CH + 1;
-        oNm = oCw;
-        total = oCw + (kGdnThreads / 64) * 16 * CH;
+        oNm = oDc + L / CH + 1;                    // [CH][CH]  coupling of one chunk's records
+        total = oNm + CH * CH;
     }
 };
 
@@ -176,9 +173,26 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
 #pragma unroll
         for (int k = 0; k < R; ++k) v[k] = ld_stream(a.ckpt + t + (size_t)k * RPP * DK);
     };
+    // Fold steps hold a tile in the lane mapping of the 16x16x4 matrix instructions:
+    // wave w takes rows 16w..16w+15 of the 64, lane l row 16w + (l & 15) and, in each
+    // 16-column block cb, columns 16cb + 4(l >> 4) .. +3 (R = DK/16 blocks).
+    const int fr = lane & 15, fg = lane >> 4;
+    static_assert(R * 16 == DK, "fold mapping: one 16-column block per tile register");
+    auto tile_base_f = [&](int u) -> size_t {
+        const int vl = u / NTILE, tl = u % NTILE;
+        return ((sHV + hv0 + vl) * DV + tl * DVT + 16 * wave + fr) * (size_t)DK + 4 * fg;
+    };
+    auto issue_tile_f = [&](int u, float4 (&v)[R]) {
+        const size_t t = tile_base_f(u);
+#pragma unroll
+        for (int k = 0; k < R; ++k) v[k] = ld_stream(a.ckpt + t + 16 * k);
+    };
     const int nunit = nv * NTILE;
     float4 va[R], vb[R];
-    if (!idle) issue_tile(0, va);
+    if (!idle) {
+        if (fold) issue_tile_f(0, va);
+        else issue_tile(0, va);
+    }
 
     // ---- stage the window -------------------------------------------------------------
     auto slot_of = [&](int s) {
@@ -362,7 +376,6 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         // transpose-reduce per 4 records) and a rank-nc update, instead of nc sequential
         // row all-reduces.
         constexpr int CH = kGdnFoldChunk;
-        constexpr int RGW = kWave / LPR;            // row groups of one wave
         const int nch = (nf + CH - 1) / CH;
         float* sKp = smem + lay.oKp;
         float* sCv = smem + lay.oCv;
@@ -370,13 +383,6 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         float* sPf = smem + lay.oPf;
         float* sGs = smem + lay.oGs;
         float* sDc = smem + lay.oDc;
-        float* sCw = smem + lay.oCw + wave * (16 * CH);
-        const int rg = lane / LPR;
-        auto wave_sync = [&]() {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        };
         auto prepare = [&](int vl) {               // K' and Cv of every chunk of value head vl
             const float* al = sAl + vl * NR;
             const float* be = sBe + vl * NR;
@@ -435,54 +441,63 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
             __syncthreads();
         };
         auto body = [&](int u) {
-            const int tl = u % NTILE;
+            const int vl = u / NTILE, tl = u % NTILE;
+            const int i = tl * DVT + 16 * wave + fr;          // this lane's row of the value head
             for (int ch = 0; ch < nch; ++ch) {
                 const int s0 = ch * CH, nc = min(CH, nf - s0);
-                // fold factors c[row][t] = Cv - K'_t . row, FB records per transpose-reduce
-                // (value v of the FB*R is held by LPR/(FB*R) lanes)
-                constexpr int FB = 2;
-                for (int g4 = 0; FB * g4 < nc; ++g4) {
-                    float acc[R * FB];
+                // p'[t][row] = K'_t . row for the chunk's records t < 16 (rows of K' past nc
+                // read as zero); lane l ends with t = 4(l >> 4) + j, j < 4, of its row
+                rssm_v4f p = {0.f, 0.f, 0.f, 0.f};
+                const bool tin = fr < nc;
 #pragma unroll
-                    for (int jj = 0; jj < FB; ++jj) {
-                        const int t = min(FB * g4 + jj, nc - 1);
-                        const float4 Kp = *reinterpret_cast<const float4*>(sKp + (s0 + t) * DK + 4 * col4);
-#pragma unroll
-                        for (int k = 0; k < R; ++k) acc[jj * R + k] = dot4(va[k], Kp);
-                    }
-                    const float r = row_reduce<R * FB, LPR>(acc, lane);
-                    const int vi = q / (LPR / (R * FB));
-                    const int t = FB * g4 + vi / R, k = vi % R;
-                    if (t < nc && q % (LPR / (R * FB)) == 0) {
-                        const int i = tl * DVT + row0 + k * RPP;
-                        sCw[(rg + RGW * k) * CH + t] = sCv[(s0 + t) * DV + i] - r;
-                    }
+                for (int cb = 0; cb < R; ++cb) {
+                    const float4 kp = tin ? *reinterpret_cast<const float4*>(sKp + (s0 + fr) * DK + 16 * cb + 4 * fg)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.x, va[cb].x, p, 0, 0, 0);
+                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.y, va[cb].y, p, 0, 0, 0);
+                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.z, va[cb].z, p, 0, 0, 0);
+                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.w, va[cb].w, p, 0, 0, 0);
                 }
-                wave_sync();
+                float c[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 4 * fg + j;
+                    c[j] = (t < nc) ? sCv[(s0 + t) * DV + i] - p[j] : 0.f;
+                }
                 const float dc = sDc[ch];
+                // row += sum_t c_t k_t, as (block of 16 columns)^T += K^T c^T: the k index of
+                // matrix instruction j is record 4(l >> 4) + j on both operands
 #pragma unroll
-                for (int k = 0; k < R; ++k) {
-                    va[k].x *= dc; va[k].y *= dc; va[k].z *= dc; va[k].w *= dc;
-                }
-                // rank-nc update; the fold factors of a row are read by all its lanes at once
-                for (int t = 0; t < nc; ++t) {
-                    const float4 Kv = io::ld4(sK, (s0 + t) * DK + 4 * col4);
+                for (int cb = 0; cb < R; ++cb) {
+                    rssm_v4f acc = {dc * va[cb].x, dc * va[cb].y, dc * va[cb].z, dc * va[cb].w};
 #pragma unroll
-                    for (int k = 0; k < R; ++k) {
-                        const float c = sCw[(rg + RGW * k) * CH + t];
-                        va[k].x += c * Kv.x; va[k].y += c * Kv.y; va[k].z += c * Kv.z; va[k].w += c * Kv.w;
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 4 * fg + j;
+                        const float kv = (t < nc) ? io::ld(sK, (s0 + t) * DK + 16 * cb + fr) : 0.f;
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, c[j], acc, 0, 0, 0);
                     }
+                    va[cb] = make_float4(acc[0], acc[1], acc[2], acc[3]);
                 }
-                wave_sync();                        // these reads precede the next chunk's writes
             }
-            const size_t tb = tile_base(u);
+            const size_t tb = tile_base_f(u);
 #pragma unroll
-            for (int k = 0; k < R; ++k) st_stream(a.ckpt + tb + (size_t)k * RPP * DK, va[k]);
-            outputs(u, va);
+            for (int k = 0; k < R; ++k) st_stream(a.ckpt + tb + 16 * k, va[k]);
+            // outputs from the new rows: each row is spread over the 4 lanes l, l^16, l^32, l^48
+            if constexpr (MODE != kGdnFold) {
+                for (int j = 0; j < Tb; ++j) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int cb = 0; cb < R; ++cb)
+                        part += dot4(va[cb], *reinterpret_cast<const float4*>(sU + (vl * T1 + j) * DK + 16 * cb + 4 * fg));
+                    part = exchange<16>(part, part, lane);
+                    part = exchange<32>(part, part, lane);
+                    if (fg == 0) a.out[out_index(vl, j, i)] = scale * (part + sAcc[(vl * T1 + j) * DV + i]);
+                }
+            }
         };
         prepare(0);
         for (int u = 0; u + 1 < nunit; ++u) {
-            issue_tile(u + 1, vb);
+            issue_tile_f(u + 1, vb);
             body(u);
             if ((u + 1) % NTILE == 0) prepare((u + 1) / NTILE);
             rotate();
