@@ -45,7 +45,7 @@ struct GdnShape {
 // records plus this call's positions), T1 the positions.
 struct GdnSmem {
     int NR, T1, oK, oV, oAl, oBe, oQ, oU, oAcc;
-    int oKp, oCv, oNm, oPf, oGs, oDc, total;
+    int oKp, oCv, oDc, oGr, oNm, total;
     __host__ __device__ GdnSmem(int DK, int DV, int L, int T, int mode, int NV, int io_bytes) {
         NR = (mode == kGdnSpec) ? L + T : L;
         T1 = T > 1 ? T : 1;
@@ -60,11 +60,10 @@ struct GdnSmem {
         constexpr int CH = kGdnFoldChunk;
         oKp = oAcc + NV * T1 * DV;                 // [L][DK]   K' rows of every chunk
         oCv = oKp + L * DK;                        // [L][DV]   record part of the fold factors
-        oPf = oCv + L * DV;                        // [L]       decay products before each record
-        oGs = oPf + L;                             // [L]       decay products after each record
-        oDc = oGs + L;                             // [L/CH+1]  decay of each chunk
-        oNm = oDc + L / CH + 1;                    // [CH][CH]  coupling of one chunk's records
-        total = oNm + CH * CH;
+        oDc = oCv + L * DV;                        // [L/CH+1]  decay of each chunk
+        oGr = oDc + L / CH + 1;                    // [L][CH]   k_s . k_t within each chunk
+        oNm = oGr + L * CH;                        // [L][CH]   coupling of records within a chunk
+        total = oNm + L * CH;
     }
 };
 
@@ -379,61 +378,77 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         const int nch = (nf + CH - 1) / CH;
         float* sKp = smem + lay.oKp;
         float* sCv = smem + lay.oCv;
+        float* sGr = smem + lay.oGr;
         float* sNm = smem + lay.oNm;
-        float* sPf = smem + lay.oPf;
-        float* sGs = smem + lay.oGs;
         float* sDc = smem + lay.oDc;
+        // Gram matrix of the k rows within each chunk, shared by the value heads:
+        // sGr[s][y] = k_s . k_t for the chunk's earlier row t = s - (s % CH) + y
+        for (int pr = tid; pr < nf * CH; pr += kGdnThreads) {
+            const int s = pr / CH, y = pr % CH, x = s % CH;
+            if (y < x) {
+                const int t = s - x + y;
+                float m = 0.f;
+                for (int jj = 0; jj < DK4; ++jj) {
+                    const int j4 = (jj + pr) % DK4;     // rotated start: fewer bank conflicts
+                    m += dot4(io::ld4(sK, s * DK + 4 * j4), io::ld4(sK, t * DK + 4 * j4));
+                }
+                sGr[pr] = m;
+            }
+        }
         auto prepare = [&](int vl) {               // K' and Cv of every chunk of value head vl
             const float* al = sAl + vl * NR;
             const float* be = sBe + vl * NR;
-            for (int ch = 0; ch < nch; ++ch) {
-                const int s0 = ch * CH, nc = min(CH, nf - s0);
-                __syncthreads();                    // earlier readers of sNm, sKp, sCv are done
-                if (tid == 0) {
-                    float pf = 1.f;
-                    for (int x = 0; x < nc; ++x) {
-                        sPf[s0 + x] = pf;
-                        pf *= al[s0 + x];
+            __syncthreads();                        // sGr is complete; earlier readers of sNm, sKp, sCv are done
+            // Nm[s][t] = a_s beta_s (prod_{t<u<s} a_u) (k_t . k_s).  The decay between two
+            // records is a product of the gates in between, never a ratio of running
+            // products: those reach zero in fp32 when gates are small, and 0/0 is NaN.
+            for (int pr = tid; pr < nf * CH; pr += kGdnThreads) {
+                const int s = pr / CH, y = pr % CH, x = s % CH;
+                if (y < x) {
+                    const int t = s - x + y;
+                    float g = al[s] * be[s];
+#pragma unroll
+                    for (int w = 1; w < CH - 1; ++w) {
+                        const int uu = t + w;
+                        const float f = al[min(uu, s)];
+                        g *= (uu < s) ? f : 1.f;
                     }
-                    sDc[ch] = pf;
-                    float gs = 1.f;
-                    for (int x = nc - 1; x >= 0; --x) {
-                        sGs[s0 + x] = gs;
-                        gs *= al[s0 + x];
-                    }
+                    sNm[pr] = g * sGr[pr];
                 }
-                __syncthreads();
-                for (int pr = tid; pr < CH * CH; pr += kGdnThreads) {
-                    const int sr = pr / CH, tr = pr % CH;
-                    if (tr < sr && sr < nc) {
-                        float m = 0.f;
-                        for (int jj = 0; jj < DK4; ++jj) {
-                            const int j4 = (jj + pr) % DK4;     // rotated start: fewer bank conflicts
-                            m += dot4(io::ld4(sK, (s0 + sr) * DK + 4 * j4), io::ld4(sK, (s0 + tr) * DK + 4 * j4));
-                        }
-                        sNm[sr * CH + tr] = al[s0 + sr] * be[s0 + sr] * (sPf[s0 + sr] / sPf[s0 + tr + 1]) * m;
-                    }
-                }
-                __syncthreads();
-                if (tid < DK + DV) {
+            }
+            __syncthreads();
+            // forward substitution through (I + Nm), one column of K (threads < DK) or of
+            // V (the next DV threads) per thread, chunk after chunk:
+            //     z_s = d_s - sum_{t<s} Nm[s][t] z_t,
+            // d_s = a_s beta_s (prod_{u<s} a_u) k_s[col] or beta_s v_s[col]; then
+            // K'/Cv row s = (prod_{u>s} a_u) z_s (products over the chunk's records)
+            if (tid < DK + DV) {
+                for (int ch = 0; ch < nch; ++ch) {
+                    const int s0 = ch * CH, nc = min(CH, nf - s0);
                     float z[CH];
+                    float pf = 1.f;
 #pragma unroll
                     for (int x = 0; x < CH; ++x) {
                         if (x < nc) {
                             const int sx = s0 + x;
-                            float acc = (tid < DK) ? al[sx] * be[sx] * sPf[sx] * io::ld(sK, sx * DK + tid)
+                            float acc = (tid < DK) ? al[sx] * be[sx] * pf * io::ld(sK, sx * DK + tid)
                                                    : be[sx] * io::ld(sV, (vl * NR + sx) * DV + tid - DK);
 #pragma unroll
-                            for (int y = 0; y < x; ++y) acc -= sNm[x * CH + y] * z[y];
+                            for (int y = 0; y < x; ++y) acc -= sNm[sx * CH + y] * z[y];
                             z[x] = acc;
+                            pf *= al[sx];
                         }
                     }
+                    if (tid == 0) sDc[ch] = pf;
+                    float gs = 1.f;
 #pragma unroll
-                    for (int x = 0; x < CH; ++x) {
+                    for (int x = CH - 1; x >= 0; --x) {
                         if (x < nc) {
-                            const float v = sGs[s0 + x] * z[x];
-                            if (tid < DK) sKp[(s0 + x) * DK + tid] = v;
-                            else sCv[(s0 + x) * DV + tid - DK] = v;
+                            const int sx = s0 + x;
+                            const float v = gs * z[x];
+                            if (tid < DK) sKp[sx * DK + tid] = v;
+                            else sCv[sx * DV + tid - DK] = v;
+                            gs *= al[sx];
                         }
                     }
                 }

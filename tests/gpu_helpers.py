@@ -91,3 +91,18 @@ class GpuConventional:
         x, z, B, C, dt = [to_dev(s[k], io) for k in ("x", "z", "B", "C", "dt_raw")]
         rs.selective_state_update(self.desc, self.state, x, z, B, C, dt, self.dt_bias, self.A, self.D, self.out)
         return self.out
+
+
+def degenerate_gdn_gates(s, t):
+    """Set gates at their limits, by value head, in one step's (or round's) inputs in place:
+    head 0 alpha = 0 (the state is cleared), head 1 alpha = 1e-4 (the product of a
+    window's gates falls below the smallest fp32 number), head 2 alpha = 1 (no decay),
+    head 3 beta = 0 (nothing is written), head 4 alpha = 1e-4 on odd t only."""
+    al, be = s["alpha"], s["beta"]
+    al[..., 0] = 0.0
+    al[..., 1] = 1e-4
+    al[..., 2] = 1.0
+    be[..., 3] = 0.0
+    if t % 2:
+        al[..., 4] = 1e-4
+    return s

@@ -8,7 +8,7 @@ import torch
 from hybrid_model_ssm_amd import replayssm as rs
 from hybrid_model_ssm_amd import synth
 from oracle import gdn as og
-from tests.gpu_helpers import DEV, assert_fp32_close, require_gpu, to_dev
+from tests.gpu_helpers import DEV, assert_fp32_close, degenerate_gdn_gates, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -166,6 +166,30 @@ def test_gdn_largest_window_L64():
         if flushed.all():
             assert_fp32_close(gpu.state.ckpt.cpu().numpy(), rep.ckpt, f"checkpoint step {t}")
     assert np.array_equal(gpu.cursor.cpu().numpy(), np.full(B, (2 * L + 1) % L, np.int32))
+
+
+def test_gdn_degenerate_gates():
+    """Gates at their limits (alpha = 0, alpha = 1e-4 so that a window's gate products
+    underflow in fp32, alpha = 1, beta = 0, see degenerate_gdn_gates) through two
+    flushes: outputs and flushed checkpoints against the oracle, no NaN."""
+    B, HV, HK, dk, dv, L = 2, 8, 2, 128, 128, 16
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=37)
+    st = gen.static
+    gpu = GpuGdn(rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16), st)
+    rep = og.GDNReplay(st.ckpt, L, HK)
+    n_flush = 0
+    for t in range(1, 2 * L + 2):
+        s = degenerate_gdn_gates(gen.step(), t)
+        ref, flushed = rep.step(**s)
+        out = gpu.step(s).cpu().numpy()
+        assert np.isfinite(out).all(), f"step {t}"
+        assert_fp32_close(out, ref, f"step {t}")
+        if flushed.all():
+            n_flush += 1
+            ck = gpu.state.ckpt.cpu().numpy()
+            assert np.isfinite(ck).all(), f"checkpoint step {t}"
+            assert_fp32_close(ck, rep.ckpt, f"checkpoint step {t}")
+    assert n_flush == 2
 
 
 def test_gdn_full_batch_small_heads():

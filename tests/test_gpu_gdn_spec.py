@@ -10,7 +10,7 @@ import torch
 from hybrid_model_ssm_amd import replayssm as rs
 from hybrid_model_ssm_amd import synth
 from oracle import gdn as og
-from tests.gpu_helpers import DEV, assert_fp32_close, require_gpu, to_dev
+from tests.gpu_helpers import DEV, assert_fp32_close, degenerate_gdn_gates, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -223,3 +223,31 @@ def test_gdn_spec_full_batch_small_heads():
         assert np.array_equal(gpu.head.cpu().numpy(), spec.head.astype(np.int32))
         assert np.array_equal(gpu.committed.cpu().numpy(), spec.committed.astype(np.int32))
     assert n_flush > B // 2 and gpu.err.item() == 0
+
+
+def test_gdn_spec_degenerate_gates():
+    """Speculative rounds with gates at their limits (alpha = 0, alpha = 1e-4 so that a
+    window's gate products underflow in fp32, alpha = 1, beta = 0) over several folds:
+    outputs, flush flags and folded checkpoints against the oracle."""
+    B, HV, HK, dk, dv, L, T = 2, 8, 4, 128, 128, 8, 4
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=43)
+    st = gen.static
+    gpu = GpuGdnSpec(rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16), st, T)
+    spec = og.GDNSpec(st.ckpt, L, HK)
+    n_flush = 0
+    for r in range(2 * L):
+        s = degenerate_gdn_gates(gen.step(n_pos=T), r)
+        n_keep = gen.accepted(T - 1) + 1
+        ref, fl_ref = spec.verify(**s)
+        out = gpu.verify(s).cpu().numpy()
+        fl = gpu.flushed.cpu().numpy()
+        assert np.array_equal(fl, fl_ref.astype(np.int32)), f"round {r}"
+        assert np.isfinite(out).all(), f"round {r}"
+        assert_fp32_close(out, ref, f"round {r}")
+        for b in range(B):
+            if fl[b]:
+                assert_fp32_close(gpu.state.ckpt[b].cpu().numpy(), spec.ckpt[b], f"round {r} seq {b} fold")
+        n_flush += int(fl.sum())
+        spec.commit(n_keep)
+        gpu.commit(n_keep)
+    assert n_flush >= 2
