@@ -25,6 +25,8 @@ Auxiliary modes used to make the committed rocprofv3 summaries:
     --calibrate-copy        also run a plain 1 GiB device copy (counter calibration)
     --pmc-summarize FETCH_DIR WRITE_DIR  turn two rocprofv3 --pmc runs into a summary
     --stats-summarize STATS_DIR          turn a rocprofv3 --kernel-trace --stats run into a summary
+    --precision-sweep       output error of emulated read and recurrence precisions
+                            (bf16, fp16, fp8) against fp32, over 1024 steps
 """
 
 from __future__ import annotations
@@ -490,6 +492,133 @@ def time_gdn_spec(torch, rs, synth, rounds, warmup, baseline=False):
                 flush_fraction=(n_flush / (B * rounds)) if not baseline else None)
 
 
+SWEEP_WINDOWS = ((0, 16), (16, 64), (64, 256), (256, 1024))
+
+
+def precision_sweep(torch, rs, synth, batch=32):
+    """Emulated read and recurrence precisions (not timed).  Every configuration runs the
+    same 1024 decode steps from the same inputs; its outputs are compared with an fp32
+    conventional run, as sqrt(sum (y - y32)^2 / sum y32^2) over the steps of each window.
+
+    replay  rec=f32 read=X   fp32 checkpoint; non-flush steps read a copy in format X
+    replay  rec=X   read=X   checkpoint rounded to X at every flush (and at the start),
+                             so the recurrence runs in X; non-flush steps read it
+    conv    rec=X            conventional update, state rounded to X after every step
+    """
+    import numpy as np
+    dev = "cuda"
+    nsteps = SWEEP_WINDOWS[-1][1]
+    names = {rs.F32: "f32", rs.BF16: "bf16", rs.F16: "f16", rs.FP8_E4M3: "fp8"}
+    lowp_kind = {rs.BF16: "bf16", rs.F16: "f16", rs.FP8_E4M3: "fp8"}
+    rows = []
+
+    def window_errors(sq_err, sq_ref):
+        return [float(np.sqrt(sq_err[a:b].sum() / sq_ref[a:b].sum())) for a, b in SWEEP_WINDOWS]
+
+    # ---- Mamba2 -------------------------------------------------------------------------
+    gen = synth.mamba2_inputs(HEADLINE, batch=batch)
+    w = dict(synth.WORKLOADS[HEADLINE])
+    H, P, N, G, L = w["nheads"], w["headdim"], w["dstate"], w["ngroups"], w["buffer_len"]
+    desc = rs.Mamba2Desc(batch, H, P, N, G, L, rs.BF16, True)
+    f32 = torch.float32
+    t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
+    st = gen.static
+    ckpt0 = t(st.ckpt, f32)
+    A, D, bias = t(st.A, f32), t(st.D, f32), t(st.dt_bias, f32)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    cfgs = [dict(route="conv", rec=rs.F32, read=rs.F32)]
+    cfgs += [dict(route="replay", rec=rs.F32, read=r) for r in (rs.F32, rs.BF16, rs.F16, rs.FP8_E4M3)]
+    cfgs += [dict(route="replay", rec=r, read=r) for r in (rs.BF16, rs.F16, rs.FP8_E4M3)]
+    cfgs += [dict(route="conv", rec=r, read=r) for r in (rs.BF16, rs.F16, rs.FP8_E4M3)]
+    for c in cfgs:
+        ck = ckpt0.clone()
+        rs.emulate_precision(ck, c["rec"])
+        c["out"] = torch.empty(batch, H, P, dtype=f32, device=dev)
+        c["sq"] = torch.zeros(nsteps, dtype=torch.float64, device=dev)
+        if c["route"] == "conv":
+            c["state"] = ck
+        else:
+            lowp = lowp_kind.get(c["read"]) if c["rec"] == rs.F32 else False
+            c["state"] = rs.Mamba2State.allocate(desc, lowp=lowp, ckpt=ck)
+            c["cur"] = [torch.zeros(batch, dtype=torch.int32, device=dev) for _ in range(2)]
+            if lowp:   # make the read copy: a flush of the empty buffer
+                rs.mamba2_flush(desc, c["state"], c["cur"][0], c["cur"][1], A, err)
+    ref_sq = torch.zeros(nsteps, dtype=torch.float64, device=dev)
+    for i in range(nsteps):
+        s = gen.step()
+        x, z, Bm, Cm = (t(s[k], torch.bfloat16) for k in ("x", "z", "B", "C"))
+        dt = t(s["dt_raw"], torch.bfloat16)
+        for c in cfgs:
+            if c["route"] == "conv":
+                rs.selective_state_update(desc, c["state"], x, z, Bm, Cm, dt, bias, A, D, c["out"])
+                rs.emulate_precision(c["state"], c["rec"])
+            else:
+                cur = c["cur"]
+                rs.mamba2_decode(desc, c["state"], cur[i % 2], cur[1 - i % 2], x, z, Bm, Cm, dt, bias, A, D,
+                                 c["out"], err)
+                if i % L == L - 1:
+                    rs.emulate_precision(c["state"].ckpt, c["rec"])
+        y32 = cfgs[0]["out"].double()
+        ref_sq[i] = (y32 * y32).sum()
+        for c in cfgs[1:]:
+            c["sq"][i] = ((c["out"].double() - y32) ** 2).sum()
+    if err.item() != 0:
+        raise RuntimeError("device error flag set in the precision sweep")
+    ref = ref_sq.cpu().numpy()
+    for c in cfgs[1:]:
+        rows.append(dict(layer="mamba2", route=c["route"], rec=names[c["rec"]],
+                         read=names[c["read"]] if c["route"] == "replay" else names[c["rec"]],
+                         rel_rms=window_errors(c["sq"].cpu().numpy(), ref)))
+    del cfgs
+
+    # ---- Gated DeltaNet (no read copies: recurrence precision only) ------------------------
+    gw = dict(synth.WORKLOADS["gdn_hv32"])
+    HV, HK, dk, dv, GL = gw["num_v_heads"], gw["num_k_heads"], gw["dk"], gw["dv"], gw["buffer_len"]
+    ggen = synth.gdn_inputs("gdn_hv32", batch=batch)
+    gdesc = rs.GdnDesc(batch, HV, HK, dk, dv, GL, rs.BF16)
+    S0 = t(ggen.static.ckpt, f32)
+    gcfgs = [dict(route="conv", rec=rs.F32)]
+    gcfgs += [dict(route="replay", rec=r) for r in (rs.F32, rs.BF16, rs.F16, rs.FP8_E4M3)]
+    gcfgs += [dict(route="conv", rec=r) for r in (rs.BF16, rs.F16, rs.FP8_E4M3)]
+    for c in gcfgs:
+        ck = S0.clone()
+        rs.emulate_precision(ck, c["rec"])
+        c["out"] = torch.empty(batch, HV, dv, dtype=f32, device=dev)
+        c["sq"] = torch.zeros(nsteps, dtype=torch.float64, device=dev)
+        if c["route"] == "conv":
+            c["state"] = ck
+        else:
+            c["state"] = rs.GdnState.allocate(gdesc, ckpt=ck)
+            c["cur"] = [torch.zeros(batch, dtype=torch.int32, device=dev) for _ in range(2)]
+    ref_sq = torch.zeros(nsteps, dtype=torch.float64, device=dev)
+    for i in range(nsteps):
+        s = ggen.step()
+        q, k, v = (t(s[n], torch.bfloat16) for n in ("q", "k", "v"))
+        al, be = t(s["alpha"], f32), t(s["beta"], f32)
+        for c in gcfgs:
+            if c["route"] == "conv":
+                rs.gdn_conventional_decode(gdesc, c["state"], q, k, v, al, be, c["out"])
+                rs.emulate_precision(c["state"], c["rec"])
+            else:
+                cur = c["cur"]
+                rs.gdn_decode(gdesc, c["state"], cur[i % 2], cur[1 - i % 2], q, k, v, al, be, c["out"], err)
+                if i % GL == GL - 1:
+                    rs.emulate_precision(c["state"].ckpt, c["rec"])
+        y32 = gcfgs[0]["out"].double()
+        ref_sq[i] = (y32 * y32).sum()
+        for c in gcfgs[1:]:
+            c["sq"][i] = ((c["out"].double() - y32) ** 2).sum()
+    if err.item() != 0:
+        raise RuntimeError("device error flag set in the precision sweep")
+    ref = ref_sq.cpu().numpy()
+    for c in gcfgs[1:]:
+        rows.append(dict(layer="gdn", route=c["route"], rec=names[c["rec"]],
+                         read=names[c["rec"]], rel_rms=window_errors(c["sq"].cpu().numpy(), ref)))
+    return dict(batch=batch, steps=nsteps, windows=[list(wd) for wd in SWEEP_WINDOWS],
+                workloads=[f"{HEADLINE} at B={batch}", f"gdn_hv32 at B={batch}"],
+                reference="conventional update in fp32 on the same inputs", rows=rows)
+
+
 def ceiling(torch, calibrate_copy=False):
     n = COPY_BYTES // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -673,6 +802,8 @@ def main(argv=None):
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-command", default="")
     ap.add_argument("--stats-summarize", metavar="STATS_DIR")
+    ap.add_argument("--precision-sweep", action="store_true",
+                    help="print the emulated read/recurrence precision sweep (one JSON line) and exit")
     args = ap.parse_args(argv)
 
     if args.stats_summarize:
@@ -697,6 +828,9 @@ def main(argv=None):
         return 2
     rs.lib()
     print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    if args.precision_sweep:
+        print(json.dumps({"precision_sweep": precision_sweep(torch, rs, synth)}), flush=True)
+        return 0
 
     head, hb = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup)
     print(f"[bench] headline {head['seq_tokens_per_s']:.4g} seq-tok/s, {head['hbm_gbps']:.0f} GB/s",

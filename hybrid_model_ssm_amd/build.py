@@ -30,7 +30,7 @@ SOURCES = [("api.cpp", "api", []), ("mamba2_launch.hip", "mamba2_launch", []),
            # the GDN fold's matrix instructions accumulate in ordinary VGPRs, which keeps the
            # kernel at its occupancy (accumulation registers would count on top)
            ("gdn_kernels.hip", "gdn_kernels", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
-           ("cursor_kernels.hip", "cursor_kernels", [])]
+           ("cursor_kernels.hip", "cursor_kernels", []), ("emulate_kernels.hip", "emulate_kernels", [])]
 SOURCES += [("mamba2_inst.hip", f"mamba2_inst_io{io}_part{part}_lp{lp}",
              [f"-DRSSM_IO={io}", f"-DRSSM_PART={part}", f"-DRSSM_LP={lp}"])
             for io in (0, 1) for part in (0, 1, 2, 3) for lp in (0, 1, 2, 3)]

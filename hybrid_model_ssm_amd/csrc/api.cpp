@@ -189,7 +189,7 @@ const char* replayssm_status_string(replayssm_status status) {
     return "unknown status";
 }
 
-int32_t replayssm_version(void) { return 200; }
+int32_t replayssm_version(void) { return 300; }
 
 replayssm_status replayssm_mamba2_decode(const replayssm_mamba2_desc* desc,
                                          const replayssm_mamba2_state* state,
@@ -416,6 +416,18 @@ replayssm_status replayssm_gdn_spec_baseline(const replayssm_gdn_desc* desc, flo
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out;
     a.n_pos = n_pos;
     return hip_status(rssm::launch_gdn_conventional(a, desc->io_dtype, true, stream));
+}
+
+replayssm_status replayssm_emulate_precision(float* data, int64_t rows, int32_t row_len,
+                                             replayssm_dtype dtype, float* row_scale, hipStream_t stream) {
+    REQ(rows >= 0 && row_len >= 4 && row_len % 4 == 0);
+    REQ(dtype == REPLAYSSM_F32 || dtype == REPLAYSSM_BF16 || dtype == REPLAYSSM_F16 ||
+        dtype == REPLAYSSM_FP8_E4M3);
+    REQ(aligned(data, 16) && aligned(row_scale, 4));
+    REQ(data || rows == 0);
+    if (dtype == REPLAYSSM_F32 || rows == 0) return REPLAYSSM_OK;
+    const int kind = dtype == REPLAYSSM_BF16 ? 1 : dtype == REPLAYSSM_F16 ? 2 : 3;
+    return hip_status(rssm::launch_emulate_precision(data, rows, row_len, kind, row_scale, stream));
 }
 
 }  // extern "C"

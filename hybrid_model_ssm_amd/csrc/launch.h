@@ -105,4 +105,9 @@ hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t str
 // snapshots: per-position snapshot baseline (ckpt = snapshots, cursor_in = slot_in)
 hipError_t launch_gdn_conventional(const GdnArgs& a, int io, bool snapshots, hipStream_t stream);
 
+// round rows of an fp32 array in place to the values of a narrower format
+// (kind as lp: 1 bf16, 2 fp16, 3 fp8 with row scales, written to row_scale if set)
+hipError_t launch_emulate_precision(float* data, int64_t rows, int32_t row_len, int kind, float* row_scale,
+                                    hipStream_t stream);
+
 }  // namespace rssm

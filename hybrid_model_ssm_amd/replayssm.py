@@ -34,6 +34,7 @@ EXPORTED = (
     "replayssm_commit", "replayssm_reset_cursors", "replayssm_selective_state_update",
     "replayssm_mamba2_spec_baseline", "replayssm_gdn_decode", "replayssm_gdn_flush",
     "replayssm_gdn_spec_verify", "replayssm_gdn_conventional_decode", "replayssm_gdn_spec_baseline",
+    "replayssm_emulate_precision",
 )
 
 
@@ -105,6 +106,7 @@ def lib():
         "replayssm_gdn_spec_verify": [GD, GS, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_conventional_decode": [GD, _P, _P, _P, _P, _P, _P, _P, _P],
         "replayssm_gdn_spec_baseline": [GD, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P],
+        "replayssm_emulate_precision": [_P, ctypes.c_int64, _I, _I, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -329,6 +331,21 @@ def commit(batch, buffer_len, n_pos, head, committed, flushed, n_keep, err_flags
                                 _ptr(n_pos_seq, torch.int32, "n_pos_seq"),
                                 _ptr(err_flags, torch.int32, "err_flags"), _stream(stream))
     _check(st, "replayssm_commit")
+
+
+def emulate_precision(data, dtype, row_scale=None, stream=None):
+    """Round the fp32 tensor ``data`` (rows along its last dimension) in place to the
+    values of ``dtype`` (BF16, F16, or FP8_E4M3 with one scale per row, written to
+    ``row_scale`` if given; F32 leaves it unchanged)."""
+    if not isinstance(data, torch.Tensor) or data.dim() < 1:
+        raise TypeError("data must be a tensor with at least one dimension")
+    row_len = int(data.shape[-1])
+    rows = int(data.numel() // row_len) if row_len else 0
+    if row_scale is not None and row_scale.numel() != rows:
+        raise ValueError(f"row_scale must hold {rows} values")
+    st = lib().replayssm_emulate_precision(_ptr(data, torch.float32, "data"), rows, row_len, int(dtype),
+                                           _ptr(row_scale, torch.float32, "row_scale"), _stream(stream))
+    _check(st, "replayssm_emulate_precision")
 
 
 def reset_cursors(batch, head, cursor, seq_idx=None, stream=None):

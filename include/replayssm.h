@@ -67,8 +67,9 @@ typedef enum {
 typedef enum {
     REPLAYSSM_F32 = 0,
     REPLAYSSM_BF16 = 1,
-    REPLAYSSM_F16 = 2,      /* read copies only */
-    REPLAYSSM_FP8_E4M3 = 3  /* read copies only: OCP 8-bit float with a scale per row */
+    REPLAYSSM_F16 = 2,      /* read copies and precision emulation only */
+    REPLAYSSM_FP8_E4M3 = 3  /* read copies and precision emulation only: OCP 8-bit float
+                               with a scale per row */
 } replayssm_dtype;
 
 enum { REPLAYSSM_DEVERR_CURSOR = 1, REPLAYSSM_DEVERR_SLOT = 2 };
@@ -406,6 +407,33 @@ replayssm_status replayssm_gdn_spec_baseline(const replayssm_gdn_desc* desc, flo
                                              const int32_t* slot_in, int32_t n_pos, const void* q,
                                              const void* k, const void* v, const float* alpha,
                                              const float* beta, float* out, hipStream_t stream);
+
+/* ======================================================================================
+ * Precision emulation
+ * ====================================================================================== */
+
+/*
+ * Emulated storage precision ("ReplaySSM (a vLLM research fork)", README section on
+ * the precision folders: emulation kernels that keep the read precision apart from
+ * the recurrence precision and expose their rounding).  Rounds each of `rows` rows of
+ * `row_len` fp32 values in `data` (device, 16-byte aligned, row-major) in place to
+ * the value the format holds, so that a state kept in that format can be run through
+ * the fp32 entry points: round a checkpoint after every flush for a low-precision
+ * recurrence in replay form, or a conventional state after every update.
+ *
+ *   dtype = BF16, F16   round to nearest even (F16 overflows to +-inf)
+ *   dtype = FP8_E4M3    per row: scale = amax / 448, value = e4m3(h * (448 / amax)) *
+ *                       scale, the code rounded to nearest even and saturated to +-448
+ *                       (the read-copy format); a zero row stays zero.  If row_scale
+ *                       (device f32 [rows], 4-byte aligned) is set, the scales are
+ *                       written there.
+ *   dtype = F32         nothing to do; OK
+ *
+ * row_len >= 4 and a multiple of 4; rows >= 0.  INVALID_ARGUMENT otherwise, and then
+ * nothing is launched.  Asynchronous on `stream`.
+ */
+replayssm_status replayssm_emulate_precision(float* data, int64_t rows, int32_t row_len,
+                                             replayssm_dtype dtype, float* row_scale, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -2,7 +2,9 @@
 include/replayssm.h declares, and rejects invalid arguments before touching the GPU.
 
 No call here reaches a kernel launch: every call carries at least one invalid
-argument, and the pointers are fake addresses that are never dereferenced.  The
+argument or is one the header documents as launching nothing (precision emulation to
+F32, or of zero rows), and the pointers are fake addresses that are never
+dereferenced.  The
 module is skipped where a GPU is visible so that a regression in the validation
 could never launch a kernel on fake pointers.
 """
@@ -57,7 +59,7 @@ def test_status_strings_and_version(L):
     assert rs.status_string(2) == "unsupported shape"
     assert rs.status_string(3) == "HIP launch failure"
     assert rs.status_string(99) == "unknown status"
-    assert rs.version() == 200
+    assert rs.version() == 300
 
 
 # fake, 256-byte aligned device addresses (never dereferenced)
@@ -241,3 +243,17 @@ def test_binding_refuses_host_tensors(L):
     with pytest.raises(TypeError):
         rs._ptr([1, 2], None, "t")
     assert desc.c().headdim == 16
+
+
+def test_emulate_precision_validation(L):
+    E = L.replayssm_emulate_precision
+    assert E(fake(1), 8, 6, rs.BF16, None, None) == INV              # row length not a multiple of 4
+    assert E(fake(1), 8, 0, rs.BF16, None, None) == INV
+    assert E(fake(1), -1, 8, rs.BF16, None, None) == INV
+    assert E(fake(1), 8, 8, 7, None, None) == INV                    # no such dtype
+    assert E(fake(1) + 4, 8, 8, rs.F16, None, None) == INV           # data not 16-byte aligned
+    assert E(None, 8, 8, rs.F16, None, None) == INV
+    assert E(fake(1), 8, 8, rs.FP8_E4M3, fake(2) + 2, None) == INV   # misaligned scales
+    # documented to launch nothing
+    assert E(fake(1), 8, 8, rs.F32, None, None) == rs.OK
+    assert E(fake(1), 0, 8, rs.FP8_E4M3, None, None) == rs.OK
