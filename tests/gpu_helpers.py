@@ -106,3 +106,16 @@ def degenerate_gdn_gates(s, t):
     if t % 2:
         al[..., 4] = 1e-4
     return s
+
+
+def extreme_mamba2_dt(s, t):
+    """Set dt inputs at their extremes, by head, in one step's (or round's) inputs in place:
+    head 0 dt_raw = 60 (dt ~ 60: the window's decay exp(A sum dt) underflows to 0 in
+    fp32), head 1 dt_raw = -60 (dt ~ 1e-26: no update, no decay), head 2 alternates the
+    two by t, head 3 dt_raw = 30.  All four values are exact in bf16."""
+    dt = s["dt_raw"]
+    dt[..., 0] = 60.0
+    dt[..., 1] = -60.0
+    dt[..., 2] = 60.0 if t % 2 else -60.0
+    dt[..., 3] = 30.0
+    return s

@@ -10,8 +10,8 @@ import torch
 from hybrid_model_ssm_amd import replayssm as rs
 from hybrid_model_ssm_amd import synth
 from oracle import mamba2 as om
-from tests.gpu_helpers import (DEV, GpuConventional, GpuMamba2, assert_fp32_close, require_gpu,
-                               rms_violation, to_dev)
+from tests.gpu_helpers import (DEV, GpuConventional, GpuMamba2, assert_fp32_close, extreme_mamba2_dt,
+                               require_gpu, rms_violation, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -229,6 +229,30 @@ def test_dt_zero_keeps_checkpoint_and_B_zero_decays():
         gpu2.step(s)
     ref = np.exp(st.A[None, :] * dtsum)[:, :, None, None] * st.ckpt
     assert_fp32_close(gpu2.state.ckpt.cpu().numpy(), ref, "B=0 decay")
+
+
+def test_extreme_dt_decays_underflow_cleanly():
+    """dt at its extremes (see extreme_mamba2_dt: decays that underflow to 0 in fp32, dt
+    of 1e-26, alternation of the two) through two flushes: outputs and flushed
+    checkpoints against the oracle, no NaN."""
+    B, H, P, N, G, L = 2, 8, 64, 128, 2, 16
+    gen = _gen(B, H, P, N, G, "bf16", seed=17)
+    st = gen.static
+    gpu = GpuMamba2(_desc(B, H, P, N, G, L, "bf16"), st)
+    rep = om.Mamba2Replay(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    n_flush = 0
+    for t in range(1, 2 * L + 2):
+        s = extreme_mamba2_dt(gen.step(), t)
+        ref, flushed = rep.step(**s)
+        out = gpu.step(s).cpu().numpy()
+        assert np.isfinite(out).all(), f"step {t}"
+        assert_fp32_close(out, ref, f"step {t}")
+        if flushed.all():
+            n_flush += 1
+            ck = gpu.state.ckpt.cpu().numpy()
+            assert np.isfinite(ck).all(), f"checkpoint step {t}"
+            assert_fp32_close(ck, rep.ckpt, f"checkpoint step {t}")
+    assert n_flush == 2 and gpu.err.item() == 0
 
 
 def test_two_runs_bit_identical():

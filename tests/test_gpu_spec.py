@@ -10,7 +10,7 @@ import torch
 from hybrid_model_ssm_amd import replayssm as rs
 from hybrid_model_ssm_amd import synth
 from oracle import mamba2 as om
-from tests.gpu_helpers import DEV, assert_fp32_close, require_gpu, rms_violation, to_dev
+from tests.gpu_helpers import DEV, assert_fp32_close, extreme_mamba2_dt, require_gpu, rms_violation, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -231,3 +231,29 @@ def test_spec_full_batch_small_heads():
         assert np.array_equal(gpu.head.cpu().numpy(), spec.head.astype(np.int32))
         assert np.array_equal(gpu.committed.cpu().numpy(), spec.committed.astype(np.int32))
     assert n_flush > B // 2 and gpu.err.item() == 0
+
+
+def test_spec_extreme_dt():
+    """Speculative rounds with dt at its extremes (see extreme_mamba2_dt) over several
+    folds: outputs, flush flags, folded checkpoints and cursors against the oracle."""
+    B, H, P, N, G, L, T = 4, 8, 64, 128, 2, 8, 4
+    gen, st, desc, gpu = _setup(B, H, P, N, G, L, seed=23, n_pos=T)
+    spec = om.Mamba2Spec(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    n_flush = 0
+    for r in range(2 * L):
+        s = extreme_mamba2_dt(gen.step(n_pos=T), r)
+        n_keep = gen.accepted(T - 1) + 1
+        ref, fl_ref = spec.verify(**s)
+        out = gpu.verify(s).cpu().numpy()
+        fl = gpu.flushed.cpu().numpy()
+        assert np.array_equal(fl, fl_ref.astype(np.int32)), f"round {r}"
+        assert np.isfinite(out).all(), f"round {r}"
+        assert_fp32_close(out, ref, f"round {r}")
+        for b in range(B):
+            if fl[b]:
+                assert_fp32_close(gpu.state.ckpt[b].cpu().numpy(), spec.ckpt[b], f"round {r} seq {b} flush")
+        n_flush += int(fl.sum())
+        spec.commit(n_keep)
+        gpu.commit(n_keep)
+        assert np.array_equal(gpu.committed.cpu().numpy(), spec.committed.astype(np.int32))
+    assert n_flush >= 2 and gpu.err.item() == 0
