@@ -51,6 +51,20 @@ KERNEL_SOURCES = ["hybrid_model_ssm_amd/csrc/mamba2_kernels.h", "hybrid_model_ss
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_pmc.txt")
 STATS_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_kernel_stats.txt")
 REPLAY_KERNEL_TAG = "mamba2_replay_kernel<64, 128, unsigned short, 0, 0>"
+GDN_KERNEL_TAG = "gdn_replay_kernel<128, 128, unsigned short, 0>"
+# kernels with committed HBM counter summaries: the kernel, the sources its hash covers,
+# the summary file and its title lines
+COUNTED = {
+    "headline": dict(tag=REPLAY_KERNEL_TAG, sources=KERNEL_SOURCES, summary=PMC_SUMMARY,
+                     title=["# rocprofv3 HBM counters: Mamba2 replay decode kernel, workload mamba2_h128",
+                            "# (B=256 H=128 P=64 N=128 G=8 L=16, bf16 io, fp32 checkpoint reads)"]),
+    "gdn": dict(tag=GDN_KERNEL_TAG,
+                sources=["hybrid_model_ssm_amd/csrc/gdn_kernels.hip", "hybrid_model_ssm_amd/csrc/device_common.h"],
+                summary=os.path.join(ROOT, "profiles", "gdn_replay_decode_hv32_pmc.txt"),
+                title=["# rocprofv3 HBM counters: Gated DeltaNet replay decode kernel, workload gdn_hv32",
+                       "# (B=256 HV=32 HK=16 dk=dv=128 L=16, bf16 io; 544 dispatches = 34 windows, flushes "
+                       "included)"]),
+}
 COPY_BYTES = 1 << 30
 MiB = float(1 << 20)
 
@@ -63,9 +77,9 @@ def _code_only(text):
     return " ".join(text.split())
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -125,6 +139,14 @@ def gdn_replay_bytes(B, HV, HK, dk, dv, L, io, c):
     per_hv = state + dv * io + 8 + dv * 4 + c * (dv * io + 8) + (0 if fold else dv * io + 8)
     per_hk = 2 * dk * io + c * dk * io + (0 if fold else dk * io)
     return B * HV * per_hv + B * HK * per_hk
+
+
+def gdn_window_bytes():
+    """Average algorithmic bytes per GDN decode launch over one window (gdn_hv32)."""
+    from hybrid_model_ssm_amd import synth
+    w = synth.WORKLOADS["gdn_hv32"]
+    B, HV, HK, dk, dv, L = w["batch"], w["num_v_heads"], w["num_k_heads"], w["dk"], w["dv"], w["buffer_len"]
+    return sum(gdn_replay_bytes(B, HV, HK, dk, dv, L, 2, c) for c in range(L)) / L
 
 
 def gdn_conventional_bytes(B, HV, HK, dk, dv, io):
@@ -706,9 +728,14 @@ def _avg_counter(rows, name_pred, counter):
     return sum(per.values()) / len(per), len(per)
 
 
-def pmc_summarize(fetch_dir, write_dir, out_path, command):
+def pmc_summarize(fetch_dir, write_dir, command, which="headline", algorithmic=None):
+    """Summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) for the kernel
+    COUNTED[which], scaled by what the same counters read for the 1 GiB calibration copy;
+    ``algorithmic``: the byte model's average bytes per dispatch, for the ratio."""
+    spec = COUNTED[which]
+    out_path = spec["summary"]
     fr, wr = _read_counter_csv(fetch_dir), _read_counter_csv(write_dir)
-    is_replay = lambda n: REPLAY_KERNEL_TAG in n  # noqa: E731
+    is_replay = lambda n: spec["tag"] in n  # noqa: E731
     is_copy = lambda n: "MulFunctor" in n  # the calibration kernel: 1 GiB read + 1 GiB write  # noqa: E731
     f_rep, nf = _avg_counter(fr, is_replay, "FETCH_SIZE")
     w_rep, nw = _avg_counter(wr, is_replay, "WRITE_SIZE")
@@ -719,12 +746,10 @@ def pmc_summarize(fetch_dir, write_dir, out_path, command):
     f_scale = COPY_BYTES / (f_cpy * 1024.0)
     w_scale = COPY_BYTES / (w_cpy * 1024.0)
     traffic = f_rep * 1024.0 * f_scale + w_rep * 1024.0 * w_scale
-    lines = [
-        "# rocprofv3 HBM counters: Mamba2 replay decode kernel, workload mamba2_h128",
-        "# (B=256 H=128 P=64 N=128 G=8 L=16, bf16 io, fp32 checkpoint reads)",
+    lines = spec["title"] + [
         f"command: {command}",
-        f"kernel: rssm::{REPLAY_KERNEL_TAG}",
-        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"kernel: rssm::{spec['tag']}",
+        f"kernel_source_sha256_16: {kernel_source_hash(spec['sources'])}",
         f"dispatches: fetch {nf}, write {nw}",
         f"FETCH_SIZE_KiB_per_dispatch: {f_rep:.1f}",
         f"WRITE_SIZE_KiB_per_dispatch: {w_rep:.1f}",
@@ -733,6 +758,9 @@ def pmc_summarize(fetch_dir, write_dir, out_path, command):
         f"scale_write: {w_scale:.4f}",
         f"traffic_bytes_per_launch: {traffic:.0f}",
     ]
+    if algorithmic:
+        lines += [f"algorithmic_bytes_per_launch: {algorithmic:.0f}",
+                  f"traffic_over_algorithmic: {traffic / algorithmic:.4f}"]
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -772,18 +800,20 @@ def stats_summarize(stats_dir, out_path, command, steps=0, warmup=0):
     print("\n".join(lines[:12]))
 
 
-def committed_traffic():
+def committed_traffic(which="headline"):
     """Counter-measured bytes per launch from the committed summary, if it matches the source."""
-    if not os.path.exists(PMC_SUMMARY):
+    spec = COUNTED[which]
+    path = spec["summary"]
+    if not os.path.exists(path):
         return None, "no counter summary committed"
     kv = {}
-    for line in open(PMC_SUMMARY):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(spec["sources"]):
         return None, "kernel source changed since the counters were taken"
-    return float(kv["traffic_bytes_per_launch"]), os.path.relpath(PMC_SUMMARY, ROOT)
+    return float(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
 
 
 # ------------------------------------------------------------------------------------
@@ -801,6 +831,8 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--pmc-kernel", default="headline", choices=sorted(COUNTED),
+                    help="kernel whose counters --pmc-summarize reads")
     ap.add_argument("--stats-summarize", metavar="STATS_DIR")
     ap.add_argument("--precision-sweep", action="store_true",
                     help="print the emulated read/recurrence precision sweep (one JSON line) and exit")
@@ -810,7 +842,8 @@ def main(argv=None):
         stats_summarize(args.stats_summarize, STATS_SUMMARY, args.pmc_command, args.steps, args.warmup)
         return 0
     if args.pmc_summarize:
-        pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], PMC_SUMMARY, args.pmc_command)
+        pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], args.pmc_command, args.pmc_kernel,
+                      algorithmic=gdn_window_bytes() if args.pmc_kernel == "gdn" else None)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the decode path has no cross-GPU exchange); "
@@ -882,6 +915,9 @@ def main(argv=None):
         torch.cuda.empty_cache()
     if "gdn" in groups:
         variants["gdn_hv32_replay"] = time_gdn(torch, rs, synth, 512, 32)
+        tr, src = committed_traffic("gdn")
+        variants["gdn_hv32_replay"].update(traffic_bytes_per_launch=tr, traffic_source=src,
+                                           algorithmic_bytes_per_launch=gdn_window_bytes())
         torch.cuda.empty_cache()
         variants["gdn_hv32_conventional"] = time_gdn(torch, rs, synth, 512, 32, conventional=True)
         torch.cuda.empty_cache()

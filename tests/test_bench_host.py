@@ -87,3 +87,14 @@ def test_committed_counter_summary_parses():
     traffic, src = bench.committed_traffic()
     assert traffic is None or traffic > 1e9
     assert isinstance(src, str)
+    traffic, src = bench.committed_traffic("gdn")
+    assert traffic is None or traffic > 1e8
+    assert isinstance(src, str)
+
+
+def test_gdn_window_bytes_matches_step_models():
+    L = 16
+    per = [bench.gdn_replay_bytes(256, 32, 16, 128, 128, L, 2, c) for c in range(L)]
+    assert bench.gdn_window_bytes() == sum(per) / L
+    # the flush step reads and writes the state once: twice the state bytes of a read
+    assert per[L - 1] - per[0] > 256 * 32 * 128 * 128 * 4 * 0.99
