@@ -15,7 +15,8 @@ source, else null.  ``cpu_baseline`` times the fp64 CPU oracle (replay form) on 
 sample of the same workload and checks the GPU outputs for that sample.
 
 Measured beside the headline, each with its own timed region: the in-library
-conventional read-update-write kernel on the same inputs, the bf16, fp16 and fp8 read
+conventional read-update-write kernel on the same inputs, the headline steps captured
+as a graph and replayed, the bf16, fp16 and fp8 read
 copies, the state-and-output decode route, the B=256/H=64 layer, speculative
 verification (4 positions, commit) against the per-position snapshot baseline, and the
 Gated DeltaNet layer (replay decode and conventional; speculative verification against
@@ -286,6 +287,43 @@ def time_mamba2(torch, rs, synth, name, steps, warmup, **kw):
                bytes_per_step_MiB=nbytes / steps / MiB, hbm_gbps=nbytes / secs / 1e9,
                frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS, steps=steps)
     return res, b
+
+
+def time_mamba2_graph(torch, rs, synth, name, steps, warmup):
+    """The same decode steps captured as one graph of two windows (2L launches, so that
+    flushes keep their rate and the ping-pong cursors line up) and replayed: the launch
+    overhead of single calls taken out.  Times steps // (2L) replays."""
+    b = Mamba2Bench(torch, rs, synth, name)
+    W = 2 * b.L
+    warm = -(-warmup // W) * W
+    for i in range(warm):
+        b.launch(i)
+    torch.cuda.synchronize()
+    import ctypes
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)   # the capturing stream
+        for j in range(W):
+            a = b.args[(warm + j) % len(b.args)]
+            _check(b.fn(*a[:-1], cap), b.fn.__name__)
+    nrep = max(1, steps // W)
+    probe = b.state.ckpt[0, 0].clone()
+    g.replay()                       # one untimed replay; its two flushes must change the checkpoint
+    torch.cuda.synchronize()
+    if torch.equal(probe, b.state.ckpt[0, 0]):
+        raise RuntimeError("the captured graph did not run the decode steps")
+    secs, wall = Timer(torch).run(lambda r: g.replay(), 0, nrep)
+    n = nrep * W
+    done = warm + W + n
+    if not torch.equal(b.cur[done % 2], torch.full_like(b.cur[0], done % b.L)):
+        raise RuntimeError("cursor check failed after the graph replays")
+    if b.err.item() != 0:
+        raise RuntimeError("device error flag set")
+    nbytes = sum(b.bytes_of_step(i) for i in range(n))
+    del g, b
+    return dict(seq_tokens_per_s=synth.WORKLOADS[name]["batch"] * n / secs, ms_per_step=secs * 1e3 / n,
+                steps=n, launches_per_graph=W, bytes_per_step_MiB=nbytes / n / MiB, hbm_gbps=nbytes / secs / 1e9,
+                frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS)
 
 
 def time_spec(torch, rs, synth, rounds, warmup, baseline=False, lowp=False):
@@ -824,7 +862,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1024, help="timed decode steps of the headline")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--only", default="all",
-                    help="all, headline, or a comma list of: conventional,bf16,f16,fp8,so,h64,spec,gdn,gdn_spec")
+                    help="all, headline, or a comma list of: conventional,graph,bf16,f16,fp8,so,h64,spec,gdn,"
+                         "gdn_spec")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--cpu-steps", type=int, default=32)
@@ -883,12 +922,16 @@ def main(argv=None):
 
     variants = {}
     conv = None
-    groups = {"conventional", "bf16", "f16", "fp8", "so", "h64", "spec", "gdn", "gdn_spec"} if args.only == "all" else \
+    groups = {"conventional", "graph", "bf16", "f16", "fp8", "so", "h64", "spec", "gdn", "gdn_spec"} \
+        if args.only == "all" else \
         set() if args.only == "headline" else set(args.only.split(","))
     if "conventional" in groups:
         conv, _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup, conventional=True)
         torch.cuda.empty_cache()
         variants["mamba2_h128_conventional"] = conv
+    if "graph" in groups:
+        variants["mamba2_h128_replay_graph"] = time_mamba2_graph(torch, rs, synth, HEADLINE, args.steps, args.warmup)
+        torch.cuda.empty_cache()
     if "bf16" in groups:
         variants["mamba2_h128_bf16_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup,
                                                            lowp=True)
