@@ -201,10 +201,12 @@ def test_gdn_spec_rejects_bad_arguments():
                            z(2, 64, 8, 128, dt=torch.float32), fl)
 
 
-def test_gdn_spec_full_batch_small_heads():
-    """All B=256 sequences (4 value heads, 2 q/k heads, dk = dv = 128, L=16, 4
-    positions) for 10 rounds against the oracle."""
-    B, HV, HK, dk, dv, L, T = 256, 4, 2, 128, 128, 16, 4
+@pytest.mark.parametrize("B", [256, 300])
+def test_gdn_spec_full_batch_small_heads(B):
+    """All sequences of a full batch (4 value heads, 2 q/k heads, dk = dv = 128, L=16,
+    4 positions) for 10 rounds against the oracle.  Workgroups take the folding
+    sequences first; B=300 spans two 256-sequence chunks of that ordering."""
+    HV, HK, dk, dv, L, T = 4, 2, 128, 128, 16, 4
     gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=45)
     st = gen.static
     desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
