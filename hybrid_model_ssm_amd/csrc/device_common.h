@@ -108,20 +108,14 @@ __device__ __forceinline__ uint2 f32x4_to_f16x4(float4 v) {
     return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
-// Two e4m3 codes (bits 0-7 and 8-15 of the result's source pair) turned into fp16 bit
-// patterns whose values are 2^-8 times the e4m3 values: the sign goes to bit 15 and
-// the 7 exponent/mantissa bits to bits 7-13, which re-biases the exponent from 7 to 15
-// (normal and subnormal codes alike).  x holds code0 << 8 | code1 << 24.
-__device__ __forceinline__ uint32_t e4m3_pair_to_f16_bits(uint32_t x) {
-    return (x & 0x80008000u) | ((x >> 1) & 0x3f803f80u);
-}
+typedef float rssm_v2f __attribute__((ext_vector_type(2)));
 
-// four e4m3 codes (little-endian bytes of w) -> 2^-8 times their values
-__device__ __forceinline__ float4 e4m3x4_to_f32x4_scaled(uint32_t w) {
-    const uint32_t lo = ((w & 0xffu) << 8) | ((w & 0xff00u) << 16);
-    const uint32_t hi = ((w >> 8) & 0xff00u) | (w & 0xff000000u);
-    const float2 a = f16x2_bits_to_f32(e4m3_pair_to_f16_bits(lo));
-    const float2 b = f16x2_bits_to_f32(e4m3_pair_to_f16_bits(hi));
+// four e4m3 codes (little-endian bytes of w) -> their values, by the gfx950 packed
+// conversion (OCP E4M3 decoding, subnormals and NaN included): the low 16-bit word
+// gives bytes 0 and 1, the high word bytes 2 and 3
+__device__ __forceinline__ float4 e4m3x4_to_f32x4(uint32_t w) {
+    const rssm_v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const rssm_v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
     return make_float4(a.x, a.y, b.x, b.y);
 }
 

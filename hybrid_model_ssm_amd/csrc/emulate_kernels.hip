@@ -46,10 +46,8 @@ __global__ void __launch_bounds__(kEmuThreads) emulate_precision_kernel(float* d
             const float inv = amax > 0.f ? 448.0f / amax : 0.f;
             const float scale = amax / 448.0f;
             for (int i = lane; i < n4; i += kWave) {
-                // decode gives 2^-8 times the code's value; 256 * that is exact
-                const float4 d = e4m3x4_to_f32x4_scaled(f32x4_to_e4m3x4(row[i], inv));
-                row[i] = make_float4(d.x * 256.f * scale, d.y * 256.f * scale, d.z * 256.f * scale,
-                                     d.w * 256.f * scale);
+                const float4 d = e4m3x4_to_f32x4(f32x4_to_e4m3x4(row[i], inv));
+                row[i] = make_float4(d.x * scale, d.y * scale, d.z * scale, d.w * scale);
             }
             if (row_scale && lane == 0) row_scale[r] = scale;
         } else {

@@ -14,7 +14,7 @@ struct Mamba2Args {
     float* lp_scale;      // [B,H,P] row scales of an fp8 copy
     void* rec_x;          // [B,H,L,P] io
     void* rec_B;          // [B,G,L,N] io
-    float* rec_dt;        // [B,H,L]
+    float* rec_dt;        // [B,L,H]
     const int32_t* cursor_in;   // AR cursor, or the speculative head
     int32_t* cursor_out;        // AR only
     const int32_t* committed;   // speculative only

@@ -304,11 +304,11 @@ mamba2_replay_kernel(Mamba2Args a) {
         *reinterpret_cast<float4*>(sC + j * N + 4 * n4) = io::cvt4(io::ldraw4(Cin, pos_g(j) + 4 * n4));
     }
     for (int task = tid; task < nh * nrec; task += kThreads) {
-        const int hl = task / nrec, s = task - hl * nrec;
+        const int s = task / nh, hl = task - s * nh;   // a slot's heads are contiguous in rec_dt
         const int h = h0 + hl;
         float dt;
         if (s < nstored) {
-            dt = a.rec_dt[(sH + h) * L + slot_of(s)];
+            dt = a.rec_dt[((size_t)sb * L + slot_of(s)) * H + h];
         } else {
             dt = io::ld(dtin, pos_h(h, s - nstored)) + a.dt_bias[h];
             if (a.dt_softplus) dt = softplus_f32(dt);
@@ -447,7 +447,7 @@ mamba2_replay_kernel(Mamba2Args a) {
             const float r = row_reduce<R, LPR>(acc, lane);
             if (writer) {
                 const int o = hl * T1 * P + pw;
-                a.out[pos_x(h, 0) + pw] = silu_gate_fast(sdec[hl * T1] * r + sY[o], io::ld(sZ, o));
+                sY[o] = silu_gate_fast(sdec[hl * T1] * r + sY[o], io::ld(sZ, o));
             }
         } else if constexpr (MODE == kSpec) {
             const int h = h0 + hl;
@@ -466,7 +466,7 @@ mamba2_replay_kernel(Mamba2Args a) {
                 const int p = row0 + (vi % R) * RPP;
                 if ((q % (LPR / (R * TB))) == 0 && j < Tb && (!MASK || p < P)) {
                     const int o = (hl * T1 + j) * P + p;
-                    a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
+                    sY[o] = silu_gate_fast(sdec[hl * T1 + j] * r + sY[o], io::ld(sZ, o));
                 }
             }
         }
@@ -477,8 +477,8 @@ mamba2_replay_kernel(Mamba2Args a) {
     };
 
     // outputs of head hl from a low-precision tile: same arithmetic as `outputs`, in the
-    // EPL-elements-per-lane mapping.  fp8 tiles decode to 2^-8 times the code values; the
-    // row scale (times 2^8) multiplies the reduced row.
+    // EPL-elements-per-lane mapping.  fp8 tiles decode to the code values; the row scale
+    // multiplies the reduced row.
     auto lp_dot = [&](const uint4& v, int j) -> float {
         const float* c = sC + j * N + EPL * colq;
         const float4 C0 = *reinterpret_cast<const float4*>(c);
@@ -492,8 +492,8 @@ mamba2_replay_kernel(Mamba2Args a) {
         } else {
             const float4 C2 = *reinterpret_cast<const float4*>(c + 8);
             const float4 C3 = *reinterpret_cast<const float4*>(c + 12);
-            return dot4(e4m3x4_to_f32x4_scaled(v.x), C0) + dot4(e4m3x4_to_f32x4_scaled(v.y), C1) +
-                   dot4(e4m3x4_to_f32x4_scaled(v.z), C2) + dot4(e4m3x4_to_f32x4_scaled(v.w), C3);
+            return dot4(e4m3x4_to_f32x4(v.x), C0) + dot4(e4m3x4_to_f32x4(v.y), C1) +
+                   dot4(e4m3x4_to_f32x4(v.z), C2) + dot4(e4m3x4_to_f32x4(v.w), C3);
         }
     };
     auto outputs_lp = [&](int hl, const uint4 (&v)[RQ], float sc) {
@@ -501,7 +501,7 @@ mamba2_replay_kernel(Mamba2Args a) {
             constexpr int LQ = Tq::LPR;
             const int h = h0 + hl;
             const int qq = tid % LQ;
-            const float rs = (LP == kLpFP8) ? sc * 256.0f : 1.0f;
+            const float rs = (LP == kLpFP8) ? sc : 1.0f;
             for (int j0 = 0; j0 < Tb; j0 += TBQ) {
                 float acc[RQ * TBQ];
 #pragma unroll
@@ -516,7 +516,7 @@ mamba2_replay_kernel(Mamba2Args a) {
                 const int p = rowq0 + (vi % RQ) * Tq::RPP;
                 if ((qq % (LQ / (RQ * TBQ))) == 0 && j < Tb && (!Tq::MASK || p < P)) {
                     const int o = (hl * T1 + j) * P + p;
-                    a.out[pos_x(h, j) + p] = silu_gate_fast(sdec[hl * T1 + j] * (rs * r) + sY[o], io::ld(sZ, o));
+                    sY[o] = silu_gate_fast(sdec[hl * T1 + j] * (rs * r) + sY[o], io::ld(sZ, o));
                 }
             }
         }
@@ -613,11 +613,26 @@ mamba2_replay_kernel(Mamba2Args a) {
         body(nh - 1);
     }
 
+    // ---- store the outputs ----------------------------------------------------------------
+    // Each output replaced its record term in sY (the lane that reads an entry writes it);
+    // the workgroup's outputs of one position are one contiguous block of nh * P floats,
+    // stored here in one coalesced pass rather than as scattered words between the
+    // checkpoint loads (scattered writes in the read stream cost far more than their bytes).
+    if constexpr (MODE != kFold) {
+        __syncthreads();
+        for (int task = tid; task < Tb * nh * P4; task += kThreads) {
+            const int p4 = task % P4, jh = task / P4;
+            const int j = jh / nh, hl = jh - j * nh;
+            *reinterpret_cast<float4*>(a.out + pos_x(h0 + hl, j) + 4 * p4) =
+                *reinterpret_cast<const float4*>(sY + (hl * T1 + j) * P + 4 * p4);
+        }
+    }
+
     // ---- append this step's records --------------------------------------------------
     if constexpr (MODE != kFold) {
         if (MODE == kSpec || !flush) {
-            // speculative rounds may overwrite ring slots that other heads read above
-            if (MODE == kSpec) __syncthreads();
+            // speculative rounds may overwrite ring slots that other heads read above (the
+            // barrier before the output stores orders them)
             const int slot0 = (MODE == kSpec) ? hd + cm : c;
 #pragma unroll
             for (int i = 0; i < kAppendPerThread; ++i) {
@@ -636,9 +651,11 @@ mamba2_replay_kernel(Mamba2Args a) {
                 io::straw4(reinterpret_cast<IO*>(a.rec_x), ((sH + h0 + hl) * L + slot) * P + 4 * p4,
                            io::ldraw4(xin, pos_x(h0 + hl, j) + 4 * p4));
             }
+            // one slot's dt of the workgroup's heads: one contiguous block (scattered 4-byte
+            // stores into the read stream are costly)
             for (int task = tid; task < nh * Tb; task += kThreads) {
-                const int hl = task / Tb, j = task - hl * Tb;
-                a.rec_dt[(sH + h0 + hl) * L + (slot0 + j) % L] = sdt[hl * NR + nstored + j];
+                const int j = task / nh, hl = task - j * nh;
+                a.rec_dt[((size_t)sb * L + (slot0 + j) % L) * H + h0 + hl] = sdt[hl * NR + nstored + j];
             }
             // the group's B records: with several workgroups per group the host appends
             // them in a separate launch (speculative rounds only)

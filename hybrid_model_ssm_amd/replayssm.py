@@ -204,7 +204,7 @@ class Mamba2State:
             ckpt=ckpt,
             rec_x=torch.zeros(B, H, L, P, dtype=io, device=device),
             rec_B=torch.zeros(B, G, L, N, dtype=io, device=device),
-            rec_dt=torch.zeros(B, H, L, dtype=torch.float32, device=device),
+            rec_dt=torch.zeros(B, L, H, dtype=torch.float32, device=device),
             ckpt_lp=torch.zeros(B, H, P, N, dtype=lp_t, device=device) if kind else None,
             lp_scale=torch.zeros(B, H, P, dtype=torch.float32, device=device) if kind == "fp8" else None,
         )

@@ -118,7 +118,8 @@ typedef struct {
  *            precisions": rounding of the copy never enters the recurrence).
  *   rec_x    io   [batch, nheads, buffer_len, headdim]   x records (exact copies)
  *   rec_B    io   [batch, ngroups, buffer_len, dstate]   B records (exact copies)
- *   rec_dt   f32  [batch, nheads, buffer_len]            dt after softplus
+ *   rec_dt   f32  [batch, buffer_len, nheads]            dt after softplus (slot-major: the
+ *            dt of one step is a contiguous row)
  *   lp_dtype dtype of ckpt_lp (ignored when ckpt_lp is NULL):
  *            REPLAYSSM_BF16, REPLAYSSM_F16  round to nearest even from ckpt;
  *            REPLAYSSM_FP8_E4M3  OCP e4m3 (bias 7, 3 mantissa bits, largest 448, no

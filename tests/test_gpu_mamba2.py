@@ -103,13 +103,13 @@ def test_mixed_cursor_phases_with_preloaded_records():
     cursors = np.array([0, 7, 3, 6, 1, 7], np.int32)
     rec_x = synth.round_bf16(rng.standard_normal((B, H, L, P)).astype(np.float32))
     rec_B = synth.round_bf16((rng.standard_normal((B, G, L, N)) / np.sqrt(N)).astype(np.float32))
-    rec_dt = rng.uniform(1e-3, 1e-1, (B, H, L)).astype(np.float32)
+    rec_dt = rng.uniform(1e-3, 1e-1, (B, L, H)).astype(np.float32)
     gpu.state.rec_x.copy_(to_dev(rec_x, torch.bfloat16))
     gpu.state.rec_B.copy_(to_dev(rec_B, torch.bfloat16))
     gpu.state.rec_dt.copy_(to_dev(rec_dt, torch.float32))
     gpu.cur[0].copy_(torch.from_numpy(cursors))
     for b in range(B):
-        rep.records[b] = [(rec_x[b, :, s], rec_B[b, :, s], rec_dt[b, :, s]) for s in range(cursors[b])]
+        rep.records[b] = [(rec_x[b, :, s], rec_B[b, :, s], rec_dt[b, s, :]) for s in range(cursors[b])]
     for t in range(1, 2 * L + 2):
         s = gen.step()
         ref, flushed = rep.step(**s)
