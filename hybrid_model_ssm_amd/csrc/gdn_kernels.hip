@@ -311,11 +311,11 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         *reinterpret_cast<Raw4*>(sV + (vl * NR + s) * DV + 4 * i4) = r;
     }
     for (int task = tid; task < nv * nrec; task += kGdnThreads) {
-        const int vl = task / nrec, s = task - vl * nrec;
-        const size_t hv = sHV + hv0 + vl;
+        const int s = task / nv, vl = task - s * nv;   // a slot's value heads are contiguous
+        const size_t g = ((size_t)sb * L + slot_of(s)) * HV + hv0 + vl;
         const bool rec = s < nstored;
-        sAl[vl * NR + s] = rec ? a.rec_alpha[hv * L + slot_of(s)] : a.alpha[pos_h(vl, s - nstored)];
-        sBe[vl * NR + s] = rec ? a.rec_beta[hv * L + slot_of(s)] : a.beta[pos_h(vl, s - nstored)];
+        sAl[vl * NR + s] = rec ? a.rec_alpha[g] : a.alpha[pos_h(vl, s - nstored)];
+        sBe[vl * NR + s] = rec ? a.rec_beta[g] : a.beta[pos_h(vl, s - nstored)];
     }
     for (int task = tid; task < Tb * DK4; task += kGdnThreads) {
         const int j = task / DK4, j4 = task % DK4;
@@ -409,7 +409,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
             const float r = row_reduce<R, LPR>(acc, lane);
             if (writer) {
                 const int i = tl * DVT + iw;
-                a.out[out_index(vl, 0, i)] = scale * (r + sAcc[vl * DV + i]);
+                sAcc[vl * DV + i] = scale * (r + sAcc[vl * DV + i]);
             }
         } else if constexpr (MODE == kGdnSpec) {
             for (int j0 = 0; j0 < Tb; j0 += TB) {
@@ -426,7 +426,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 const int j = j0 + vi / R;
                 const int i = tl * DVT + row0 + (vi % R) * RPP;
                 if ((q % (LPR / (R * TB))) == 0 && j < Tb)
-                    a.out[out_index(vl, j, i)] = scale * (r + sAcc[(vl * T1 + j) * DV + i]);
+                    sAcc[(vl * T1 + j) * DV + i] = scale * (r + sAcc[(vl * T1 + j) * DV + i]);
             }
         }
     };
@@ -588,7 +588,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                         part += dot4(va[cb], *reinterpret_cast<const float4*>(sU + (vl * T1 + j) * DK + 16 * cb + 4 * fg));
                     part = exchange<16>(part, part, lane);
                     part = exchange<32>(part, part, lane);
-                    if (fg == 0) a.out[out_index(vl, j, i)] = scale * (part + sAcc[(vl * T1 + j) * DV + i]);
+                    if (fg == 0) sAcc[(vl * T1 + j) * DV + i] = scale * (part + sAcc[(vl * T1 + j) * DV + i]);
                 }
             }
         };
@@ -602,6 +602,21 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         body(nunit - 1);
     }
 
+    // ---- store the outputs ----------------------------------------------------------------
+    // Each output replaced its record term in sAcc (the lane that reads an entry writes it);
+    // the workgroup's outputs of one position are one contiguous block of nv * DV floats,
+    // stored in one coalesced pass rather than as scattered words between the checkpoint
+    // loads.
+    if constexpr (MODE != kGdnFold) {
+        __syncthreads();
+        for (int task = tid; task < Tb * nv * DV4; task += kGdnThreads) {
+            const int i4 = task % DV4, jv = task / DV4;
+            const int j = jv / nv, vl = jv - j * nv;
+            *reinterpret_cast<float4*>(a.out + out_index(vl, j, 4 * i4)) =
+                *reinterpret_cast<const float4*>(sAcc + (vl * T1 + j) * DV + 4 * i4);
+        }
+    }
+
     // ---- append this call's records ---------------------------------------------------
     if constexpr (MODE == kGdnDecode) {
         if (!fold) {
@@ -612,9 +627,9 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                            io::ldraw4(vin, iv * DV + 4 * i4));
             }
             for (int vl = tid; vl < nv; vl += kGdnThreads) {
-                const size_t sv = sHV + hv0 + vl, iv = bHV + hv0 + vl;
-                a.rec_alpha[sv * L + c] = a.alpha[iv];
-                a.rec_beta[sv * L + c] = a.beta[iv];
+                const size_t g = ((size_t)sb * L + c) * HV + hv0 + vl, iv = bHV + hv0 + vl;
+                a.rec_alpha[g] = a.alpha[iv];
+                a.rec_beta[g] = a.beta[iv];
             }
             if (chunk == 0) {
                 for (int j4 = tid; j4 < DK4; j4 += kGdnThreads)
@@ -634,10 +649,10 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                        *reinterpret_cast<const Raw4*>(sV + (vl * NR + nstored + j) * DV + 4 * i4));
         }
         for (int task = tid; task < nv * Tb; task += kGdnThreads) {
-            const int vl = task / Tb, j = task - vl * Tb;
-            const size_t hv = sHV + hv0 + vl;
-            a.rec_alpha[hv * L + (slot0 + j) % L] = sAl[vl * NR + nstored + j];
-            a.rec_beta[hv * L + (slot0 + j) % L] = sBe[vl * NR + nstored + j];
+            const int j = task / nv, vl = task - j * nv;
+            const size_t g = ((size_t)sb * L + (slot0 + j) % L) * HV + hv0 + vl;
+            a.rec_alpha[g] = sAl[vl * NR + nstored + j];
+            a.rec_beta[g] = sBe[vl * NR + nstored + j];
         }
         // the q/k head's k records: with several workgroups per q/k head the host
         // appends them in a separate launch

@@ -57,8 +57,8 @@ struct GdnArgs {
     float* ckpt;          // [B,HV,dv,dk]
     void* rec_k;          // [B,HK,L,dk]
     void* rec_v;          // [B,HV,L,dv]
-    float* rec_alpha;     // [B,HV,L]
-    float* rec_beta;      // [B,HV,L]
+    float* rec_alpha;     // [B,L,HV]
+    float* rec_beta;      // [B,L,HV]
     const int32_t* cursor_in;   // AR cursor, or the speculative head
     int32_t* cursor_out;        // AR only
     const int32_t* committed;   // speculative only

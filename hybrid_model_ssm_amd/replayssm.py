@@ -263,8 +263,8 @@ class GdnState:
         return GdnState(ckpt=ckpt,
                         rec_k=torch.zeros(B, HK, L, dk, dtype=io, device=device),
                         rec_v=torch.zeros(B, HV, L, dv, dtype=io, device=device),
-                        rec_alpha=torch.zeros(B, HV, L, dtype=torch.float32, device=device),
-                        rec_beta=torch.zeros(B, HV, L, dtype=torch.float32, device=device))
+                        rec_alpha=torch.zeros(B, L, HV, dtype=torch.float32, device=device),
+                        rec_beta=torch.zeros(B, L, HV, dtype=torch.float32, device=device))
 
     def c(self):
         return GdnStateC(_ptr(self.ckpt, torch.float32, "ckpt"), _ptr(self.rec_k, None, "rec_k"),

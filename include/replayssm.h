@@ -320,8 +320,8 @@ typedef struct {
  *   ckpt       f32 [batch, num_v_heads, dv, dk]
  *   rec_k      io  [batch, num_k_heads, buffer_len, dk]
  *   rec_v      io  [batch, num_v_heads, buffer_len, dv]
- *   rec_alpha  f32 [batch, num_v_heads, buffer_len]
- *   rec_beta   f32 [batch, num_v_heads, buffer_len]
+ *   rec_alpha  f32 [batch, buffer_len, num_v_heads]   (slot-major, as rec_dt)
+ *   rec_beta   f32 [batch, buffer_len, num_v_heads]
  *   slot, num_slots  state-slot map as for Mamba2 (NULL: identity)
  */
 typedef struct {
