@@ -832,6 +832,20 @@ def stats_summarize(stats_dir, out_path, command, steps=0, warmup=0):
             lines.append(f"headline kernel: rssm::{REPLAY_KERNEL_TAG}")
             lines.append(f"headline timed dispatches: {len(timed)} (after {warmup} warmup), "
                          f"average {sum(timed) / len(timed):.1f} us, min {min(timed):.1f}, max {max(timed):.1f}")
+            # every sequence starts at cursor 0, so dispatch i runs at cursor i mod L and the
+            # dispatch at cursor L-1 is the flush step; split the time by the kind of step
+            from hybrid_model_ssm_amd import synth
+            w = synth.WORKLOADS[HEADLINE]
+            L = w["buffer_len"]
+            shape = (w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"], L, 2)
+            for name, cs in (("non-flush", range(L - 1)), ("flush", [L - 1])):
+                d = [t for i, t in enumerate(dur[:warmup + steps]) if i >= warmup and i % L in cs]
+                nbytes = sum(mamba2_replay_bytes(*shape, c) for c in cs) / len(cs)
+                if d:
+                    avg = sum(d) / len(d)
+                    lines.append(f"headline {name} steps (cursor {cs[0]}..{cs[-1]}): {len(d)} dispatches, "
+                                 f"average {avg:.1f} us, min {min(d):.1f}, max {max(d):.1f}; "
+                                 f"{nbytes / 1e6:.1f} MB algorithmic -> {nbytes / avg / 1e3:.0f} GB/s")
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
