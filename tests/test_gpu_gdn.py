@@ -89,6 +89,43 @@ def test_gdn_replay_and_conventional(shape):
     assert gpu.err.item() == 0
 
 
+def test_gdn_mixed_cursor_phases_with_preloaded_records():
+    """Sequences start at different cursors with records already in their buffers (k and v
+    rows, and the slot-major alpha/beta rows), so one launch mixes flushing and
+    non-flushing sequences: outputs, cursors and every folded checkpoint against the
+    oracle over two flushes of each sequence."""
+    B, HV, HK, dk, dv, L = 5, 4, 2, 128, 128, 8
+    rng = np.random.default_rng(7)
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=31)
+    st = gen.static
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    gpu = GpuGdn(desc, st)
+    rep = og.GDNReplay(st.ckpt, L, HK)
+    cursors = np.array([0, 7, 3, 6, 1], np.int32)
+    kk = rng.standard_normal((B, HK, L, dk))
+    rec_k = synth.round_bf16((kk / np.linalg.norm(kk, axis=-1, keepdims=True)).astype(np.float32))
+    rec_v = synth.round_bf16(rng.standard_normal((B, HV, L, dv)).astype(np.float32))
+    rec_al = rng.uniform(0.5, 1.0, (B, L, HV)).astype(np.float32)
+    rec_be = rng.uniform(0.0, 1.0, (B, L, HV)).astype(np.float32)
+    gpu.state.rec_k.copy_(to_dev(rec_k, torch.bfloat16))
+    gpu.state.rec_v.copy_(to_dev(rec_v, torch.bfloat16))
+    gpu.state.rec_alpha.copy_(to_dev(rec_al, torch.float32))
+    gpu.state.rec_beta.copy_(to_dev(rec_be, torch.float32))
+    gpu.cur[0].copy_(torch.from_numpy(cursors))
+    for b in range(B):
+        rep.records[b] = [(og.heads_of_kgroups(rec_k[b, :, s], HV), rec_v[b, :, s].astype(np.float64),
+                           rec_al[b, s].astype(np.float64), rec_be[b, s].astype(np.float64))
+                          for s in range(cursors[b])]
+    for t in range(1, 2 * L + 2):
+        s = gen.step()
+        ref, flushed = rep.step(**s)
+        assert_fp32_close(gpu.step(s).cpu().numpy(), ref, f"step {t}")
+        assert np.array_equal(gpu.cursor.cpu().numpy(), rep.cursor)
+        for b in np.nonzero(flushed)[0]:
+            assert_fp32_close(gpu.state.ckpt[b].cpu().numpy(), rep.ckpt[b], f"seq {b} checkpoint step {t}")
+    assert gpu.err.item() == 0
+
+
 def test_gdn_full_size_sampled():
     """B=256, 32 value heads over 16 q/k heads, dk=dv=128, L=16: 2L+2 steps, 8 sampled
     sequences against the oracle."""
