@@ -33,82 +33,6 @@ constexpr int kGdnMaxVHeads = 4;   // value heads per workgroup
 constexpr int kGdnFoldChunk = 16;  // records folded together in matrix form
 constexpr size_t kGdnMaxSmemBytes = 64 * 1024;
 
-// ---------------------------------------------------------------------------------------
-// Longest-first order of the sequences of a speculative round.  A round folds the
-// buffer of some sequences only (committed + positions > L), and their workgroups run
-// much longer than the rest.  Every workgroup computes the same permutation of the
-// batch -- the folding sequences first, then the others, each part in batch order --
-// and takes the sequence at position `rank`.  The hardware starts workgroups in id
-// order, so the long ones start first and the short ones fill the gaps they leave,
-// instead of a few long ones running alone at the end of the launch.
-//
-// Each thread loads the cursors of one sequence (all loads issued together, so a
-// batch of up to NT sequences costs the one global round trip that loading this
-// workgroup's own cursors costs anyway); the thread holding the chosen sequence hands
-// its cursors to the workgroup through LDS.  The values are returned unchecked.
-// Called by all NT threads (it holds barriers); returns the same value in all of them.
-// ---------------------------------------------------------------------------------------
-struct SpecSeq {
-    int b, sb, Tb, hd, cm;   // batch row, state row, positions, ring head, committed records
-};
-
-template <int NT>
-__device__ SpecSeq spec_sequence_heavy_first(int rank, int batch, int L, int T, const int32_t* slot,
-                                             const int32_t* n_pos_seq, const int32_t* head,
-                                             const int32_t* committed) {
-    constexpr int NW = NT / kWave;
-    __shared__ int s_cnt[NW];
-    __shared__ SpecSeq s_pick;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    auto load = [&](int i) {
-        SpecSeq r;
-        r.b = i;
-        r.sb = slot ? slot[i] : i;
-        r.Tb = n_pos_seq ? n_pos_seq[i] : T;
-        r.hd = head[i];
-        r.cm = committed[i];
-        return r;
-    };
-    int nheavy = 0;
-    if (batch > NT) {   // more than one chunk: count the folding sequences first
-        for (int c0 = 0; c0 < batch; c0 += NT) {
-            bool h = false;
-            if (c0 + tid < batch) {
-                const SpecSeq r = load(c0 + tid);
-                h = r.cm + r.Tb > L;
-            }
-            nheavy += __syncthreads_count(h);
-        }
-    }
-    int before_h = 0, before_l = 0;   // folding and other sequences of earlier chunks
-    for (int c0 = 0; c0 < batch; c0 += NT) {
-        const int i = c0 + tid;
-        const bool in = i < batch;    // the in-range threads are a prefix of the chunk
-        SpecSeq mine{};
-        if (in) mine = load(i);
-        const bool h = in && mine.cm + mine.Tb > L;
-        const uint64_t m = __ballot(h);
-        if (lane == 0) s_cnt[wave] = __popcll(m);
-        __syncthreads();
-        int hw = 0, hc = 0;           // folding ones in earlier waves, in the whole chunk
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            hw += (w < wave) ? s_cnt[w] : 0;
-            hc += s_cnt[w];
-        }
-        if (batch <= NT) nheavy = hc;
-        const int hb = hw + __popcll(m & __lanemask_lt());   // folding ones before i in the chunk
-        const int pos = h ? before_h + hb : nheavy + before_l + (tid - hb);
-        if (in && pos == rank) s_pick = mine;
-        before_h += hc;
-        before_l += min(NT, batch - c0) - hc;
-        __syncthreads();
-    }
-    return s_pick;
-}
-
 template <int DK>
 struct GdnShape {
     static constexpr int LPR = DK / 4;                 // lanes per state row

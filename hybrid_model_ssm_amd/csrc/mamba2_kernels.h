@@ -121,8 +121,7 @@ mamba2_replay_kernel(Mamba2Args a) {
     const int wid = blockIdx.x;
     const int chunk = wid % nchunk;
     const int bg = wid / nchunk;
-    const int b = bg / G;
-    const int g = bg - b * G;
+    const int g = bg % G;
     const int h0 = g * hpg + chunk * a.heads_per_chunk;
     const int nh = min(a.heads_per_chunk, hpg - chunk * a.heads_per_chunk);
     const bool lead = (g == 0 && chunk == 0);  // writes the per-sequence cursor outputs
@@ -133,18 +132,25 @@ mamba2_replay_kernel(Mamba2Args a) {
     // A pad row (state slot -1, or no positions) is skipped; a slot or position count
     // out of range, or a bad cursor, is flagged and skipped.  Skipped rows keep their
     // cursors (cursor_out = cursor_in) and report no flush.
-    const int sb = a.slot ? a.slot[b] : b;
-    const int Tb = (MODE == kSpec && a.n_pos_seq) ? a.n_pos_seq[b] : T;
-    int c = 0, hd = 0, cm = 0;
+    // Speculative rounds take the sequences that fold first (their workgroups run
+    // longest); the ordering hands over the chosen sequence's cursors.
+    int b, sb, Tb, c = 0, hd = 0, cm = 0;
+    if constexpr (MODE == kSpec) {
+        const SpecSeq q = spec_sequence_heavy_first<kThreads>(bg / G, a.batch, L, T, a.slot, a.n_pos_seq,
+                                                              a.cursor_in, a.committed);
+        b = q.b; sb = q.sb; Tb = q.Tb; hd = q.hd; cm = q.cm;
+    } else {
+        b = bg / G;
+        sb = a.slot ? a.slot[b] : b;
+        Tb = T;
+        c = a.cursor_in[b];
+    }
     int err = 0;
     if (sb < -1 || sb >= (a.slot ? a.num_slots : a.batch)) err |= kDevErrSlot;
     if (Tb < 0 || Tb > T) err |= kDevErrCursor;
     if constexpr (MODE == kSpec) {
-        hd = a.cursor_in[b];
-        cm = a.committed[b];
         if (hd < 0 || hd >= L || cm < 0 || cm > L) err |= kDevErrCursor;
     } else {
-        c = a.cursor_in[b];
         if (c < 0 || c >= L) err |= kDevErrCursor;
     }
     if (err || sb < 0 || (MODE == kSpec && Tb == 0)) {
