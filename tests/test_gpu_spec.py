@@ -215,8 +215,8 @@ def test_spec_positions_equal_buffer_length():
 @pytest.mark.parametrize("B", [256, 300])
 def test_spec_full_batch_small_heads(B):
     """All sequences of a full batch (H=8, G=2, P=64, N=128, L=16, 4 positions) for 10
-    rounds: every output, flushed flag and cursor against the oracle (B=300: a batch
-    that is not a power of two)."""
+    rounds: every output, flushed flag and cursor against the oracle.  Workgroups take
+    the folding sequences first; B=300 spans two 256-sequence chunks of that ordering."""
     H, P, N, G, L, T = 8, 64, 128, 2, 16, 4
     gen, st, desc, gpu = _setup(B, H, P, N, G, L, seed=26)
     spec = om.Mamba2Spec(st.ckpt, L, st.A, st.D, st.dt_bias, G)
