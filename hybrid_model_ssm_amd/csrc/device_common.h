@@ -19,12 +19,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
 
 // Input/output element types: float, or bf16 kept as raw uint16_t.
 template <typename IO> struct Io;
@@ -73,9 +67,14 @@ __device__ __forceinline__ float4 bf16x4_to_f32x4(uint2 r) {
                        __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
 }
 
+// four floats -> bf16 rounded to nearest even, as two words of pairs (low half first); the
+// conversion compiles to the gfx950 packed f32 -> bf16 instruction, two values at a time
+typedef __bf16 rssm_bf2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 f32x4_to_bf16x4(float4 v) {
-    return make_uint2(f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16),
-                      f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16));
+    rssm_bf2 a, b;
+    a.x = (__bf16)v.x; a.y = (__bf16)v.y;
+    b.x = (__bf16)v.z; b.y = (__bf16)v.w;
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -119,23 +118,16 @@ __device__ __forceinline__ float4 e4m3x4_to_f32x4(uint32_t w) {
     return make_float4(a.x, a.y, b.x, b.y);
 }
 
-// e4m3 code of x rounded to nearest even, saturated to +-448
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-    const float a = fminf(fabsf(x), 448.0f);
-    uint32_t m;
-    if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
-        m = (uint32_t)__builtin_rintf(a * 512.0f);   // 8 becomes the smallest normal code
-    } else {                                   // keep 3 mantissa bits, re-bias 127 -> 7
-        const uint32_t u = __float_as_uint(a);
-        m = ((u + 0x7ffffu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-    }
-    return sign | m;
-}
-
+// e4m3 codes of four floats scaled by inv (little-endian bytes), rounded to nearest even
+// by the gfx950 packed f32 -> fp8 conversion.  The callers scale rows to at most 448 in
+// magnitude; the conversion rounds magnitudes below 464 (the midpoint past the largest
+// code) to at most 448, which is the saturation the format's encoding asks for (checked
+// against the rounding written out in integer arithmetic at every code value, every
+// midpoint and its neighbours, on the device).
 __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float4 v, float inv) {
-    return f32_to_e4m3(v.x * inv) | (f32_to_e4m3(v.y * inv) << 8) | (f32_to_e4m3(v.z * inv) << 16) |
-           (f32_to_e4m3(v.w * inv) << 24);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v.x * inv, v.y * inv, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v.z * inv, v.w * inv, w, true);
+    return (uint32_t)w;
 }
 
 // ---------------------------------------------------------------------------------------
