@@ -214,9 +214,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 // Each thread loads the cursors of one sequence (all loads issued together, so a
 // batch of up to NT sequences costs the one global round trip that loading this
 // workgroup's own cursors costs anyway); the thread holding the chosen sequence hands
-// its cursors to the workgroup through LDS.  The values are returned unchecked.
-// Called by all NT threads (it holds barriers); returns the same value in all of them.
+// its cursors to the workgroup through LDS.  Every workgroup reads every sequence's
+// cursors, so batches above kHeavyFirstMaxBatch keep batch order (the work would grow
+// with the square of the batch, and a large grid leaves a short tail anyway).  The
+// values are returned unchecked.  Called by all NT threads (it holds barriers); returns
+// the same value in all of them.
 // ---------------------------------------------------------------------------------------
+constexpr int kHeavyFirstMaxBatch = 1024;
+
 struct SpecSeq {
     int b, sb, Tb, hd, cm;   // batch row, state row, positions, ring head, committed records
 };
@@ -240,6 +245,7 @@ __device__ SpecSeq spec_sequence_heavy_first(int rank, int batch, int L, int T, 
         r.cm = committed[i];
         return r;
     };
+    if (batch > kHeavyFirstMaxBatch) return load(rank);
     int nheavy = 0;
     if (batch > NT) {   // more than one chunk: count the folding sequences first
         for (int c0 = 0; c0 < batch; c0 += NT) {

@@ -227,6 +227,31 @@ def test_gdn_spec_full_batch_small_heads(B):
     assert n_flush > B // 2 and gpu.err.item() == 0
 
 
+def test_gdn_spec_batch_above_ranking_limit():
+    """A batch above the longest-first ranking's limit (1024 sequences) keeps batch order:
+    B=1100 (2 value heads, 1 q/k head, dk = dv = 64, L=16, 4 positions) for 6 rounds with
+    folds against the oracle."""
+    B, HV, HK, dk, dv, L, T = 1100, 2, 1, 64, 64, 16, 4
+    gen = synth.GDNInputs(B, HV, HK, dk, dv, io="bf16", seed=46)
+    st = gen.static
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    gpu = GpuGdnSpec(desc, st, T)
+    spec = og.GDNSpec(st.ckpt, L, HK)
+    n_flush = 0
+    for r in range(6):
+        s = gen.step(n_pos=T)
+        n_keep = gen.accepted(T - 1) + 1
+        ref, fl_ref = spec.verify(**s)
+        assert_fp32_close(gpu.verify(s).cpu().numpy(), ref, f"round {r}")
+        assert np.array_equal(gpu.flushed.cpu().numpy(), fl_ref.astype(np.int32))
+        n_flush += int(fl_ref.sum())
+        spec.commit(n_keep)
+        gpu.commit(n_keep)
+        assert np.array_equal(gpu.head.cpu().numpy(), spec.head.astype(np.int32))
+        assert np.array_equal(gpu.committed.cpu().numpy(), spec.committed.astype(np.int32))
+    assert n_flush > 0 and gpu.err.item() == 0
+
+
 def test_gdn_spec_degenerate_gates():
     """Speculative rounds with gates at their limits (alpha = 0, alpha = 1e-4 so that a
     window's gate products underflow in fp32, alpha = 1, beta = 0) over several folds:

@@ -235,6 +235,28 @@ def test_spec_full_batch_small_heads(B):
     assert n_flush > B // 2 and gpu.err.item() == 0
 
 
+def test_spec_batch_above_ranking_limit():
+    """A batch above the longest-first ranking's limit (1024 sequences) keeps batch order:
+    B=1100 (H=2, G=1, P=N=16, L=16, 4 positions) for 6 rounds with folds, every output,
+    flushed flag and cursor against the oracle."""
+    B, H, P, N, G, L, T = 1100, 2, 16, 16, 1, 16, 4
+    gen, st, desc, gpu = _setup(B, H, P, N, G, L, seed=27)
+    spec = om.Mamba2Spec(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    n_flush = 0
+    for r in range(6):
+        s = gen.step(n_pos=T)
+        n_keep = gen.accepted(T - 1) + 1
+        ref, fl_ref = spec.verify(**s)
+        assert_fp32_close(gpu.verify(s).cpu().numpy(), ref, f"round {r}")
+        assert np.array_equal(gpu.flushed.cpu().numpy(), fl_ref.astype(np.int32))
+        n_flush += int(fl_ref.sum())
+        spec.commit(n_keep)
+        gpu.commit(n_keep)
+        assert np.array_equal(gpu.head.cpu().numpy(), spec.head.astype(np.int32))
+        assert np.array_equal(gpu.committed.cpu().numpy(), spec.committed.astype(np.int32))
+    assert n_flush > 0 and gpu.err.item() == 0
+
+
 def test_spec_extreme_dt():
     """Speculative rounds with dt at its extremes (see extreme_mamba2_dt) over several
     folds: outputs, flush flags, folded checkpoints and cursors against the oracle."""
