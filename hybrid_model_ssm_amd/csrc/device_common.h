@@ -19,7 +19,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-
 // Input/output element types: float, or bf16 kept as raw uint16_t.
 template <typename IO> struct Io;
 

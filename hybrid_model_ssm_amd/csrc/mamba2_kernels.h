@@ -445,7 +445,6 @@ mamba2_replay_kernel(Mamba2Args a) {
     constexpr int TB = (MODE == kSpec) ? (LPR / R >= 2 ? 2 : 1) : 1;
     auto outputs = [&](int hl, const float4 (&v)[R]) {
         if constexpr (MODE == kDecode || MODE == kDecodeSO) {
-            const int h = h0 + hl;
             const float4 Cv = *reinterpret_cast<const float4*>(sC + 4 * col4);
             float acc[R];
 #pragma unroll
@@ -456,7 +455,6 @@ mamba2_replay_kernel(Mamba2Args a) {
                 sY[o] = silu_gate_fast(sdec[hl * T1] * r + sY[o], io::ld(sZ, o));
             }
         } else if constexpr (MODE == kSpec) {
-            const int h = h0 + hl;
             for (int j0 = 0; j0 < Tb; j0 += TB) {
                 float acc[R * TB];
 #pragma unroll
@@ -505,7 +503,6 @@ mamba2_replay_kernel(Mamba2Args a) {
     auto outputs_lp = [&](int hl, const uint4 (&v)[RQ], float sc) {
         if constexpr (MODE != kFold && LOWP) {
             constexpr int LQ = Tq::LPR;
-            const int h = h0 + hl;
             const int qq = tid % LQ;
             const float rs = (LP == kLpFP8) ? sc : 1.0f;
             for (int j0 = 0; j0 < Tb; j0 += TBQ) {
