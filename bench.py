@@ -680,31 +680,89 @@ def precision_sweep(torch, rs, synth, batch=32):
                 reference="conventional update in fp32 on the same inputs", rows=rows)
 
 
-def ceiling(torch, calibrate_copy=False):
+PROBE_LIB = os.path.join(ROOT, "hybrid_model_ssm_amd", "libreplayssm_probes.so")
+# (name, mode, rows per thread, tiles per workgroup, non-temporal loads, non-temporal stores,
+# in place): mode 0 reads, mode 1 reads and writes
+PROBES = [(f"read_{'nt' if ntl else 'plain'}_r{r}_tpw{t}", 0, r, t, ntl, 0, False)
+          for r in (1, 2, 8) for t in (1, 4, 16) for ntl in (0, 1)]
+PROBES += [(f"{'inplace' if ip else 'copy'}_{'nt' if ntl else 'plain'}_{'nt' if nts else 'plain'}_r{r}_tpw{t}",
+            1, r, t, ntl, nts, ip)
+           for ip in (True, False) for r in (1, 2, 8) for t in (1, 4, 16) for ntl in (0, 1) for nts in (0, 1)]
+
+
+def probe_lib():
+    """The benchmark's bandwidth probes (built beside the library; not part of its C ABI)."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise FileNotFoundError(f"{PROBE_LIB} is missing: run python -m hybrid_model_ssm_amd.build")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.replayssm_probe_pass_floats.restype = ctypes.c_int64
+    lib.replayssm_probe_stream.restype = ctypes.c_int
+    lib.replayssm_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+    return lib
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def ceiling(torch, reps=20, repeats=3):
+    """Device bandwidth ceilings from the hand-written streaming probes (1 GiB of fp32 in
+    the replay kernel's [64, 128] tile shape; read, in-place read+write, and copy), each the
+    median of ``repeats`` timed regions of ``reps`` launches (HIP events on the launch
+    stream); GB/s counts bytes read plus bytes written.  torch's elementwise copy (1 GiB in,
+    1 GiB out) is timed beside them: it is the kernel the HBM counters are calibrated on."""
+    import ctypes
+    lib = probe_lib()
     n = COPY_BYTES // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    for _ in range(3):
-        torch.mul(a, 1.0, out=b)
-        a.sum()
-    torch.cuda.synchronize()
+    sink = torch.empty(n // lib.replayssm_probe_pass_floats(), dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 20
-    e0.record()
-    for _ in range(reps):
-        torch.mul(a, 1.0, out=b)   # plain streaming read + write of 1 GiB each (also the counter calibration)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_s = e0.elapsed_time(e1) / 1e3 / reps
-    e0.record()
-    for _ in range(reps):
-        a.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    read_s = e0.elapsed_time(e1) / 1e3 / reps
-    del a, b
-    return dict(copy_gbps=2 * COPY_BYTES / copy_s / 1e9, read_gbps=COPY_BYTES / read_s / 1e9,
-                note="torch elementwise mul-by-one (1 GiB read + 1 GiB write) and sum (1 GiB read), fp32")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        secs = []
+        for _ in range(repeats):
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            secs.append(e0.elapsed_time(e1) / 1e3 / reps)
+        return _median(secs)
+
+    probes = {}
+    for name, mode, rpt, tpw, ntl, nts, inplace in PROBES:
+        dst = a if inplace else b
+
+        def launch():
+            st = lib.replayssm_probe_stream(a.data_ptr(), dst.data_ptr(), sink.data_ptr(), n, rpt, tpw, mode,
+                                            ntl, nts, 1.0, stream)
+            if st:
+                raise RuntimeError(f"probe {name} failed with status {st}")
+        secs = timed(launch)
+        moved = COPY_BYTES * (1 if mode == 0 else 2)
+        probes[name] = dict(gbps=moved / secs / 1e9, us=secs * 1e6)
+    torch_copy = timed(lambda: torch.mul(a, 1.0, out=b))
+    torch_inplace = timed(lambda: a.mul_(1.0))
+    del a, b, sink
+    best = lambda pre: max((v["gbps"], k) for k, v in probes.items() if k.startswith(pre))  # noqa: E731
+    r, i, c = best("read_"), best("inplace_"), best("copy_")
+    return dict(read_gbps=r[0], read_probe=r[1], inplace_rw_gbps=i[0], inplace_rw_probe=i[1],
+                copy_gbps=c[0], copy_probe=c[1], torch_copy_gbps=2 * COPY_BYTES / torch_copy / 1e9,
+                torch_inplace_gbps=2 * COPY_BYTES / torch_inplace / 1e9,
+                probes=probes,
+                note="hand-written HIP streaming probes (libreplayssm_probes.so), 1 GiB fp32 in [64,128] tiles, "
+                     "256 threads, tpw = tiles per workgroup (16: replay decode shape, 1: conventional shape); "
+                     "rw GB/s counts read + written bytes; median of 3 timed regions of 20 launches")
 
 
 # ------------------------------------------------------------------------------------
@@ -1030,7 +1088,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
     if variants:
         print("[bench] variants done", file=sys.stderr, flush=True)
-    ceil = ceiling(torch, args.calibrate_copy) if (args.only == "all" or args.calibrate_copy) else None
+    ceil = ceiling(torch) if (args.only == "all" or args.calibrate_copy) else None
     cpu = None
     if oracle_run is not None:
         cpu = cpu_baseline(torch, rs, synth, oracle_run)

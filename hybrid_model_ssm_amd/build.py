@@ -1,4 +1,5 @@
-"""Build libreplayssm.so (HIP for gfx950) in-tree.
+"""Build libreplayssm.so (HIP for gfx950) in-tree, and the benchmark's bandwidth probes
+(libreplayssm_probes.so, not part of the library's C ABI).
 
     python -m hybrid_model_ssm_amd.build            # build the library
     python -m hybrid_model_ssm_amd.build --verbose  # show the hipcc commands
@@ -22,6 +23,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libreplayssm.so")
+PROBE_LIB = os.path.join(PKG, "libreplayssm_probes.so")
+PROBE_SOURCES = [("probes.hip", "probes", [])]
 
 # (source, object name, extra defines); the Mamba2 kernel templates are instantiated in
 # slices (io dtype x replay mode x read copy, and the conventional kernels) that compile
@@ -66,19 +69,26 @@ def _compile(item, verbose):
     return obj
 
 
-def build(verbose=False, jobs=None):
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), int(os.environ.get("MAX_JOBS", 0)) or os.cpu_count() or 4)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose=False, jobs=None):
+    """Compile every source and link the library and the probe library; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    items = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(items), int(os.environ.get("MAX_JOBS", 0)) or os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), items))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

@@ -10,7 +10,6 @@ constexpr int kWave = 64;
 // bits ORed into the caller's err_flags word
 constexpr int kDevErrCursor = 1;
 constexpr int kDevErrSlot = 2;
-constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
 
 // ---------------------------------------------------------------------------------------
 // bf16 <-> f32 (raw 16-bit storage; round to nearest even)
@@ -187,18 +186,6 @@ __device__ __forceinline__ float silu_gate_fast(float y, float z) {
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-}
-
-// ---------------------------------------------------------------------------------------
-// Workgroup -> tile mapping for kernels whose neighbouring workgroups share inputs (the
-// conventional kernels: the heads of one group read the same B/C).  The hardware hands
-// workgroups to the 8 XCDs round robin (id % 8); the remap puts consecutive logical
-// tiles on one XCD so they share its L2.  The replay kernels do not use it: a replay
-// workgroup owns its whole group, and there the hardware order streams faster.
-// ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    if (nblocks % kNumXcd) return bid;
-    return (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -629,79 +629,126 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_spec_append_k_kernel(GdnArgs 
 // beta v (k.q), so both row dots come from the state as loaded.  SNAP: per-position
 // snapshot baseline for speculative decoding -- read snapshot slot_in[b] of
 // [B, n_pos, HV, dv, dk], run the n_pos updates and store the state after each.
-template <int DK, typename IO, bool SNAP>
+//
+// Every state row i of a value head is updated and reduced on its own, so the kernel is
+// cut as the Mamba2 conventional kernel is: dk/4 lanes per row with one 16-byte access
+// each, RPT rows per thread, one workgroup per (256 / (dk/4)) * RPT consecutive rows of
+// one value head, whose (b, hv) is computed once per workgroup.
+#ifndef RSSM_CONV_RPT
+#define RSSM_CONV_RPT 2
+#endif
+constexpr int kGdnConvMaxGrid = 1 << 24;   // workgroups per launch; larger problems loop
+constexpr int kGdnConvPosGroup = 4;        // snapshot baseline: positions whose inputs load together
+
+template <int DK, int DV>
+struct GdnConvShape {
+    static constexpr int LPR = DK / 4;                  // lanes per state row
+    static constexpr int RPP = kGdnThreads / LPR;       // rows per pass of the workgroup
+    static constexpr int RPT = (DV / RPP >= RSSM_CONV_RPT) ? RSSM_CONV_RPT : 1;
+    static constexpr int RW = RPP * RPT;                // rows per workgroup (divides DV)
+    static_assert(DV % RW == 0, "a workgroup stays inside one value head");
+};
+
+// One position's small inputs of a conventional GDN step, as loaded.
+template <int RPT>
+struct GdnConvInputs {
+    float4 K, Q;
+    float al, be;
+    float vi[RPT];
+};
+
+template <int DK, int DV, typename IO, bool SNAP>
 __global__ void __launch_bounds__(kGdnThreads) gdn_conventional_kernel(GdnArgs a) {
     using io = Io<IO>;
-    using S = GdnShape<DK>;
-    constexpr int LPR = S::LPR, RPP = S::RPP, R = S::R, DVT = S::DVT;
+    using Sh = GdnConvShape<DK, DV>;
+    constexpr int LPR = Sh::LPR, RPP = Sh::RPP, RPT = Sh::RPT, RW = Sh::RW;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int HV = a.hv, HK = a.hk, dv = a.dv;
-    const int ntile = dv / DVT;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int tile = bid % ntile;
-    const int bhv = bid / ntile;
-    const int b = bhv / HV;
-    const int hv = bhv - b * HV;
-    const int hk = hv / (HV / HK);
-    const int i0 = tile * DVT;
     const int row0 = tid / LPR;
-    const int col4 = tid - row0 * LPR;
+    const int col4 = tid % LPR;
+    const int HV = a.hv, HK = a.hk;
+    const int rv = HV / HK;
     const int T = SNAP ? a.n_pos : 1;
-    const size_t SS = (size_t)dv * DK;   // one value head's state
-
-    size_t src;
-    if constexpr (SNAP) {
-        int sl = a.cursor_in[b];
-        sl = sl < 0 ? 0 : (sl >= T ? T - 1 : sl);
-        src = ((size_t)(b * T + sl) * HV + hv) * SS;
-    } else {
-        src = (size_t)bhv * SS;
-    }
-    src += (size_t)i0 * DK + 4 * col4;
-    float4 v[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-        v[k] = *reinterpret_cast<const float4*>(a.ckpt + src + (size_t)(row0 + k * RPP) * DK);
+    const int64_t nchunks = (int64_t)a.batch * HV * (DV / RW);
+    constexpr size_t SS = (size_t)DV * DK;   // one value head's state
+    const IO* kin = reinterpret_cast<const IO*>(a.k);
+    const IO* qin = reinterpret_cast<const IO*>(a.q);
     const IO* vin = reinterpret_cast<const IO*>(a.v);
     const int q = tid % LPR;
-    const int ridx = q / (LPR / R);
-    const int iw = row0 + ridx * RPP;
+    const int ridx = q / (LPR / RPT);                   // row this lane writes after the reduce
+    const bool writer = (q % (LPR / RPT)) == 0;
 
-    for (int j = 0; j < T; ++j) {
-        const size_t ph = SNAP ? (size_t)(b * T + j) * HV + hv : (size_t)bhv;       // value head, position
-        const size_t qk_off = (SNAP ? (size_t)(b * T + j) * HK + hk : (size_t)b * HK + hk) * DK;
-        const float4 Kv = io::ld4(reinterpret_cast<const IO*>(a.k), qk_off + 4 * col4);
-        const float4 Qv = io::ld4(reinterpret_cast<const IO*>(a.q), qk_off + 4 * col4);
-        const float al = a.alpha[ph], be = a.beta[ph];
-        const float kq = group_allreduce<LPR>(dot4(Kv, Qv), lane);
-
-        float d[R], e[R];
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            d[k] = dot4(v[k], Kv);
-            e[k] = dot4(v[k], Qv);
+    for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+        const int64_t bhv = chunk / (DV / RW);
+        const int i = (int)(chunk % (DV / RW)) * RW + row0;   // this lane's first row
+        const int b = (int)(bhv / HV), hv = (int)(bhv - (int64_t)(bhv / HV) * HV);
+        const int hk = hv / rv;
+        size_t src;
+        if constexpr (SNAP) {
+            int sl = a.cursor_in[b];
+            sl = sl < 0 ? 0 : (sl >= T ? T - 1 : sl);
+            src = ((size_t)(b * T + sl) * HV + hv) * SS + (size_t)i * DK + 4 * col4;
+        } else {
+            src = (size_t)bhv * SS + (size_t)i * DK + 4 * col4;
         }
-        row_allreduce<R, LPR>(d, lane);
-        const size_t dst = (SNAP ? ((size_t)(b * T + j) * HV + hv) * SS : (size_t)bhv * SS) +
-                           (size_t)i0 * DK + 4 * col4;
+        float4 v[RPT];
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const float bd = be * d[k];
-            const float bv = be * io::ld(vin, ph * dv + i0 + row0 + k * RPP);
-            v[k].x = al * (v[k].x - bd * Kv.x) + bv * Kv.x;
-            v[k].y = al * (v[k].y - bd * Kv.y) + bv * Kv.y;
-            v[k].z = al * (v[k].z - bd * Kv.z) + bv * Kv.z;
-            v[k].w = al * (v[k].w - bd * Kv.w) + bv * Kv.w;
-            *reinterpret_cast<float4*>(a.ckpt + dst + (size_t)(row0 + k * RPP) * DK) = v[k];
-        }
-        float dsel = d[0];
+        for (int k = 0; k < RPT; ++k) v[k] = ld_stream(a.ckpt + src + (size_t)k * RPP * DK);
+        auto load_in = [&](int j) {
+            const size_t ph = SNAP ? (size_t)(b * T + j) * HV + hv : (size_t)bhv;
+            const size_t qk_off = (SNAP ? (size_t)(b * T + j) * HK + hk : (size_t)b * HK + hk) * DK;
+            GdnConvInputs<RPT> in;
+            in.K = io::ld4(kin, qk_off + 4 * col4);
+            in.Q = io::ld4(qin, qk_off + 4 * col4);
+            in.al = a.alpha[ph];
+            in.be = a.beta[ph];
 #pragma unroll
-        for (int k = 1; k < R; ++k) dsel = (k == ridx) ? d[k] : dsel;
-        const float r = row_reduce<R, LPR>(e, lane);
-        if ((q % (LPR / R)) == 0) {
-            const float vi = io::ld(vin, ph * dv + i0 + iw);
-            a.out[ph * dv + i0 + iw] = a.scale * (al * (r - be * dsel * kq) + be * vi * kq);
+            for (int k = 0; k < RPT; ++k) in.vi[k] = io::ld(vin, ph * DV + i + k * RPP);
+            return in;
+        };
+        // positions in unrolled groups of kGdnConvPosGroup, each group's inputs loaded
+        // together (a loop-carried wait would hold every position until the previous
+        // store landed)
+        constexpr int GRP = SNAP ? kGdnConvPosGroup : 1;
+        for (int j0 = 0; j0 < T; j0 += GRP) {
+            GdnConvInputs<RPT> in[GRP];
+#pragma unroll
+            for (int jj = 0; jj < GRP; ++jj) in[jj] = load_in(min(j0 + jj, T - 1));   // no branch between loads
+#pragma unroll
+            for (int jj = 0; jj < GRP; ++jj) {
+                const int j = j0 + jj;
+                if (j < T) {
+                    const float4 Kv = in[jj].K, Qv = in[jj].Q;
+                    const float al = in[jj].al, be = in[jj].be;
+                    const float kq = group_allreduce<LPR>(dot4(Kv, Qv), lane);
+                    float d[RPT], e[RPT];
+#pragma unroll
+                    for (int k = 0; k < RPT; ++k) {
+                        d[k] = dot4(v[k], Kv);
+                        e[k] = dot4(v[k], Qv);
+                    }
+                    row_allreduce<RPT, LPR>(d, lane);     // every lane needs its rows' S k
+                    const float er = row_reduce<RPT, LPR>(e, lane);
+                    const size_t dst = SNAP ? ((size_t)(b * T + j) * HV + hv) * SS + (size_t)i * DK + 4 * col4 : src;
+                    float dw = d[0], vw = in[jj].vi[0];
+#pragma unroll
+                    for (int k = 0; k < RPT; ++k) {
+                        const float bd = be * d[k];
+                        const float bv = be * in[jj].vi[k];
+                        v[k].x = al * (v[k].x - bd * Kv.x) + bv * Kv.x;
+                        v[k].y = al * (v[k].y - bd * Kv.y) + bv * Kv.y;
+                        v[k].z = al * (v[k].z - bd * Kv.z) + bv * Kv.z;
+                        v[k].w = al * (v[k].w - bd * Kv.w) + bv * Kv.w;
+                        st_stream(a.ckpt + dst + (size_t)k * RPP * DK, v[k]);
+                        dw = (k == ridx) ? d[k] : dw;
+                        vw = (k == ridx) ? in[jj].vi[k] : vw;
+                    }
+                    if (writer) {
+                        const size_t ph = SNAP ? (size_t)(b * T + j) * HV + hv : (size_t)bhv;
+                        a.out[ph * DV + i + ridx * RPP] = a.scale * (al * (er - be * dw * kq) + be * vw * kq);
+                    }
+                }
+            }
         }
     }
 }
@@ -772,28 +819,31 @@ hipError_t launch_gdn_replay(const GdnArgs& a, int io, int mode, hipStream_t str
     return hipLaunchKernel(app, dim3(blocks), dim3(kGdnThreads), kargs, 0, stream);
 }
 
+template <int DK, int DV, typename IO>
+static const void* gdn_conv_pick(bool snapshots) {
+    return snapshots ? (const void*)&gdn_conventional_kernel<DK, DV, IO, true>
+                     : (const void*)&gdn_conventional_kernel<DK, DV, IO, false>;
+}
+
+template <int DK, int DV>
+static const void* gdn_conv_pick_io(int io, bool snapshots, int* rows_per_wg) {
+    *rows_per_wg = GdnConvShape<DK, DV>::RW;
+    return io == kIoBF16 ? gdn_conv_pick<DK, DV, uint16_t>(snapshots) : gdn_conv_pick<DK, DV, float>(snapshots);
+}
+
 hipError_t launch_gdn_conventional(const GdnArgs& a, int io, bool snapshots, hipStream_t stream) {
     const void* fn = nullptr;
-    if (a.dk == 64) {
-        if (io == kIoBF16)
-            fn = snapshots ? (const void*)&gdn_conventional_kernel<64, uint16_t, true>
-                           : (const void*)&gdn_conventional_kernel<64, uint16_t, false>;
-        else
-            fn = snapshots ? (const void*)&gdn_conventional_kernel<64, float, true>
-                           : (const void*)&gdn_conventional_kernel<64, float, false>;
-    } else if (a.dk == 128) {
-        if (io == kIoBF16)
-            fn = snapshots ? (const void*)&gdn_conventional_kernel<128, uint16_t, true>
-                           : (const void*)&gdn_conventional_kernel<128, uint16_t, false>;
-        else
-            fn = snapshots ? (const void*)&gdn_conventional_kernel<128, float, true>
-                           : (const void*)&gdn_conventional_kernel<128, float, false>;
-    }
+    int rows_per_wg = 1;
+    if (a.dk == 64 && a.dv == 64) fn = gdn_conv_pick_io<64, 64>(io, snapshots, &rows_per_wg);
+    if (a.dk == 64 && a.dv == 128) fn = gdn_conv_pick_io<64, 128>(io, snapshots, &rows_per_wg);
+    if (a.dk == 128 && a.dv == 64) fn = gdn_conv_pick_io<128, 64>(io, snapshots, &rows_per_wg);
+    if (a.dk == 128 && a.dv == 128) fn = gdn_conv_pick_io<128, 128>(io, snapshots, &rows_per_wg);
     if (!fn) return hipErrorInvalidValue;
     GdnArgs args = a;
     if (!snapshots) args.n_pos = 1;
     void* kargs[] = {&args};
-    const dim3 grid((unsigned)((size_t)a.batch * a.hv * (a.dv / 64)));
+    const int64_t want = (int64_t)a.batch * a.hv * (a.dv / rows_per_wg);
+    const dim3 grid((unsigned)(want < kGdnConvMaxGrid ? want : kGdnConvMaxGrid));
     return hipLaunchKernel(fn, grid, dim3(kGdnThreads), kargs, 0, stream);
 }
 

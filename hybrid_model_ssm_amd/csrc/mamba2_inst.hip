@@ -41,6 +41,7 @@ const void* RSSM_CONV_PTR_NAME(RSSM_IO)(int P, int N, bool snap) {
 #undef X
     return nullptr;
 }
+
 #endif
 
 }  // namespace rssm

@@ -707,85 +707,150 @@ __global__ void __launch_bounds__(kThreads) mamba2_spec_append_B_kernel(Mamba2Ar
 
 // ---------------------------------------------------------------------------------------
 // Conventional read-update-write step ("Why SSM layers slow down hybrid models": load
-// the state, update it, read the output, store it -- every step), with the same tiling
-// so that it is a fair baseline.  SNAP: per-position snapshot baseline for speculative
-// decoding -- read snapshot slot_in[b], run the n_pos updates, store all n_pos states.
+// the state, update it, read the output, store it -- every step).  SNAP: per-position
+// snapshot baseline for speculative decoding -- read snapshot slot_in[b], run the n_pos
+// updates, store all n_pos states.
+//
+// Every state row (b, h, p) is updated and reduced on its own (y[p] = h[p,:] . C), so
+// the kernel is cut finely: LPR = N/4 lanes per row with one 16-byte access each, RPT
+// rows per thread, one workgroup per RW = (256/LPR) * RPT consecutive rows.  Small
+// chunks per workgroup keep the memory touched by the workgroups in flight within a
+// narrow window, which an in-place read-modify-write stream needs to approach the
+// device's read+write limit (whole 32 KiB heads per workgroup stream 15% slower); a few
+// rows per thread share the per-head work (dt, its softplus and decay, B and C) so that
+// the vector ALU, which one 16-byte access per lane would keep busy, stays off the
+// critical path.  When RW divides P a workgroup stays inside one head and its (b, h)
+// is computed once in scalar registers; otherwise each lane finds its own row's head.
 // ---------------------------------------------------------------------------------------
+#ifndef RSSM_CONV_RPT
+#define RSSM_CONV_RPT 2
+#endif
+constexpr int kConvMaxGrid = 1 << 24;   // workgroups per launch; larger problems loop
+constexpr int kConvPosGroup = 4;        // snapshot baseline: positions whose inputs load together
+
+template <int P, int N>
+struct ConvShape {
+    static constexpr int LPR = N / 4;                   // lanes per state row
+    static constexpr int RPP = kThreads / LPR;          // rows per pass of the workgroup
+    static constexpr int RPT = (P / RPP >= RSSM_CONV_RPT) ? RSSM_CONV_RPT : 1;   // rows per thread
+    static constexpr int RW = RPP * RPT;                // rows per workgroup
+    static constexpr bool ONE_HEAD = (P % RW) == 0;     // a workgroup stays inside one head
+};
+
+// One position's small inputs of a conventional Mamba2 step, as loaded (no arithmetic, so
+// the compiler issues every load of a position together).
+template <int RPT>
+struct ConvInputs {
+    float dt_raw;
+    float x[RPT], z[RPT];
+    float4 B, C;
+};
+
 template <int P, int N, typename IO, bool SNAP>
 __global__ void __launch_bounds__(kThreads) mamba2_conventional_kernel(Mamba2ConvArgs a) {
     using io = Io<IO>;
-    using Tl = Mamba2Tile<P, N>;
-    constexpr int LPR = Tl::LPR, RPP = Tl::RPP, R = Tl::R;
-    constexpr bool MASK = Tl::MASK;
+    using Sh = ConvShape<P, N>;
+    constexpr int LPR = Sh::LPR, RPP = Sh::RPP, RPT = Sh::RPT, RW = Sh::RW;
+    constexpr bool ONE_HEAD = Sh::ONE_HEAD;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int H = a.nheads, G = a.ngroups;
-    const int hpg = H / G;
-    const int bh = xcd_remap(blockIdx.x, gridDim.x);
-    const int b = bh / H;
-    const int h = bh - b * H;
-    const int g = h / hpg;
-    const int T = SNAP ? a.n_pos : 1;
     const int row0 = tid / LPR;
     const int col4 = tid % LPR;
-    constexpr size_t PN = (size_t)P * N;
-
-    size_t src;
-    if constexpr (SNAP) {
-        int sl = a.slot_in[b];
-        sl = sl < 0 ? 0 : (sl >= T ? T - 1 : sl);
-        src = ((size_t)(b * T + sl) * H + h) * PN;
-    } else {
-        src = (size_t)bh * PN;
-    }
-    src += (size_t)row0 * N + 4 * col4;
-    float4 v[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-        if (!MASK || row0 + k * RPP < P)
-            v[k] = *reinterpret_cast<const float4*>(a.state + src + (size_t)k * RPP * N);
-    const float Ah = a.A[h], Dh = a.D[h], bias = a.dt_bias[h];
+    const int H = a.nheads, G = a.ngroups;
+    const int hpg = H / G;
+    const int T = SNAP ? a.n_pos : 1;
+    const int64_t rows = (int64_t)a.batch * H * P;
+    const int64_t nchunks = (rows + RW - 1) / RW;
     const IO* xin = reinterpret_cast<const IO*>(a.x);
     const IO* zin = reinterpret_cast<const IO*>(a.z);
     const IO* Bin = reinterpret_cast<const IO*>(a.B);
     const IO* Cin = reinterpret_cast<const IO*>(a.C);
     const IO* dtin = reinterpret_cast<const IO*>(a.dt_raw);
+    constexpr size_t PN = (size_t)P * N;
     const int q = tid % LPR;
-    const int ridx = q / (LPR / R);
-    const int pw = row0 + ridx * RPP;
-    const bool writer = (q % (LPR / R)) == 0 && (!MASK || pw < P);
+    const int ridx = q / (LPR / RPT);                   // row this lane writes after the reduce
+    const bool writer = (q % (LPR / RPT)) == 0;
 
-    for (int j = 0; j < T; ++j) {
-        const size_t xo = SNAP ? ((size_t)(b * T + j) * H + h) * P : (size_t)bh * P;
-        const size_t go = SNAP ? ((size_t)(b * T + j) * G + g) * N : (size_t)(b * G + g) * N;
-        const size_t ho = SNAP ? (size_t)(b * T + j) * H + h : (size_t)bh;
-        float dt = io::ld(dtin, ho) + bias;
-        if (a.dt_softplus) dt = softplus_f32(dt);
-        const float dA = expf(dt * Ah);
-        const float4 Bv = io::ld4(Bin, go + 4 * col4);
-        const float4 Cv = io::ld4(Cin, go + 4 * col4);
-        float acc[R];
-        const size_t dst = (SNAP ? ((size_t)(b * T + j) * H + h) * PN : (size_t)bh * PN) +
-                           (size_t)row0 * N + 4 * col4;
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const int p = row0 + k * RPP;
-            if (!MASK || p < P) {
-                const float xd = dt * io::ld(xin, xo + p);
-                v[k].x = dA * v[k].x + xd * Bv.x;
-                v[k].y = dA * v[k].y + xd * Bv.y;
-                v[k].z = dA * v[k].z + xd * Bv.z;
-                v[k].w = dA * v[k].w + xd * Bv.w;
-                *reinterpret_cast<float4*>(a.state + dst + (size_t)k * RPP * N) = v[k];
-                acc[k] = dot4(v[k], Cv);
-            } else {
-                acc[k] = 0.f;
-            }
+    for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+        int64_t bh;   // b * H + h of this lane's rows
+        int p;        // this lane's first row within the head (the others follow RPP apart)
+        if constexpr (ONE_HEAD) {
+            bh = chunk / (P / RW);
+            p = (int)(chunk % (P / RW)) * RW + row0;
+        } else {
+            const int64_t r = chunk * RW + row0;
+            if (r >= rows) continue;                    // whole rows drop out together
+            bh = r / P;
+            p = (int)(r % P);
         }
-        const float r = row_reduce<R, LPR>(acc, lane);
-        if (writer) {
-            const float y = r + Dh * io::ld(xin, xo + pw);
-            a.out[xo + pw] = silu_gate(y, io::ld(zin, xo + pw));
+        const int b = (int)(bh / H), h = (int)(bh - (int64_t)(bh / H) * H);
+        const int g = h / hpg;
+        size_t src;
+        if constexpr (SNAP) {
+            int sl = a.slot_in[b];
+            sl = sl < 0 ? 0 : (sl >= T ? T - 1 : sl);
+            src = ((size_t)(b * T + sl) * H + h) * PN + (size_t)p * N + 4 * col4;
+        } else {
+            src = (size_t)bh * PN + (size_t)p * N + 4 * col4;
+        }
+        float4 v[RPT];
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) v[k] = ld_stream(a.state + src + (size_t)k * RPP * N);
+        auto load_in = [&](int j) {
+            const size_t xo = (SNAP ? ((size_t)(b * T + j) * H + h) * P : (size_t)bh * P) + p;
+            const size_t go = SNAP ? ((size_t)(b * T + j) * G + g) * N : (size_t)(b * G + g) * N;
+            const size_t ho = SNAP ? (size_t)(b * T + j) * H + h : (size_t)bh;
+            ConvInputs<RPT> in;
+            in.dt_raw = io::ld(dtin, ho);
+#pragma unroll
+            for (int k = 0; k < RPT; ++k) {
+                in.x[k] = io::ld(xin, xo + k * RPP);
+                in.z[k] = io::ld(zin, xo + k * RPP);
+            }
+            in.B = io::ld4(Bin, go + 4 * col4);
+            in.C = io::ld4(Cin, go + 4 * col4);
+            return in;
+        };
+        const float Ah = a.A[h], Dh = a.D[h], bias = a.dt_bias[h];
+        // positions in unrolled groups of kConvPosGroup, each group's inputs loaded together
+        // (a loop-carried wait would hold every position until the previous store landed)
+        constexpr int GRP = SNAP ? kConvPosGroup : 1;
+        for (int j0 = 0; j0 < T; j0 += GRP) {
+            ConvInputs<RPT> in[GRP];
+#pragma unroll
+            for (int jj = 0; jj < GRP; ++jj) in[jj] = load_in(min(j0 + jj, T - 1));   // no branch between loads
+#pragma unroll
+            for (int jj = 0; jj < GRP; ++jj) {
+                const int j = j0 + jj;
+                if (j < T) {
+                    const float u = in[jj].dt_raw + bias;
+                    const float dt = a.dt_softplus ? softplus_f32(u) : u;
+                    const float dA = expf(dt * Ah);
+                    float acc[RPT];
+                    const size_t dst = SNAP ? ((size_t)(b * T + j) * H + h) * PN + (size_t)p * N + 4 * col4 : src;
+#pragma unroll
+                    for (int k = 0; k < RPT; ++k) {
+                        const float xd = dt * in[jj].x[k];
+                        v[k].x = dA * v[k].x + xd * in[jj].B.x;
+                        v[k].y = dA * v[k].y + xd * in[jj].B.y;
+                        v[k].z = dA * v[k].z + xd * in[jj].B.z;
+                        v[k].w = dA * v[k].w + xd * in[jj].B.w;
+                        st_stream(a.state + dst + (size_t)k * RPP * N, v[k]);
+                        acc[k] = dot4(v[k], in[jj].C);
+                    }
+                    const float y = row_reduce<RPT, LPR>(acc, lane);
+                    if (writer) {
+                        float xw = in[jj].x[0], zw = in[jj].z[0];
+#pragma unroll
+                        for (int k = 1; k < RPT; ++k) {
+                            xw = (k == ridx) ? in[jj].x[k] : xw;
+                            zw = (k == ridx) ? in[jj].z[k] : zw;
+                        }
+                        const size_t xo = (SNAP ? ((size_t)(b * T + j) * H + h) * P : (size_t)bh * P) + p + ridx * RPP;
+                        a.out[xo] = silu_gate_fast(y + Dh * xw, zw);
+                    }
+                }
+            }
         }
     }
 }

@@ -48,6 +48,15 @@ static const void* find_replay(int P, int N, int io, int lp, int mode) {
     return nullptr;
 }
 
+// rows of the state one conventional workgroup covers
+static int conv_rows_per_wg(int P, int N) {
+#define X(PP, NN) \
+    if (P == PP && N == NN) return ConvShape<PP, NN>::RW;
+    RSSM_SHAPES(X)
+#undef X
+    return 1;
+}
+
 static const void* find_conv(int P, int N, int io, bool snap) {
     return io == kIoBF16 ? conv_kernel_ptr_io1(P, N, snap) : conv_kernel_ptr_io0(P, N, snap);
 }
@@ -77,7 +86,10 @@ hipError_t launch_mamba2_conventional(const Mamba2ConvArgs& a, int io, bool snap
     if (!fn) return hipErrorInvalidValue;
     Mamba2ConvArgs args = a;
     void* kargs[] = {&args};
-    const dim3 grid((unsigned)((size_t)a.batch * a.nheads));
+    const int64_t rows = (int64_t)a.batch * a.nheads * a.headdim;
+    const int64_t rows_per_wg = conv_rows_per_wg(a.headdim, a.dstate);
+    const int64_t want = (rows + rows_per_wg - 1) / rows_per_wg;
+    const dim3 grid((unsigned)(want < kConvMaxGrid ? want : kConvMaxGrid));
     return hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
 }
 

@@ -1,0 +1,150 @@
+// Streaming-bandwidth probes: the device ceilings the decode kernels are measured against.
+//
+// Built as its own library (libreplayssm_probes.so) for the benchmark only; it is not part
+// of the decode library's C ABI.  The probes move fp32 tiles of 128-float rows the way the
+// decode kernels stream the checkpoint: 256 threads, 32 consecutive lanes per row with
+// 16-byte accesses, R rows per thread, so a tile is [8R rows, 128] (R = 8: one 64 x 128
+// head of the Mamba2 checkpoint, 32 KiB; R = 1: 4 KiB, one 16-byte access per thread).  A
+// workgroup owns TPW consecutive tiles and loads tile t+1 while it finishes tile t, as the
+// replay kernels do; TPW = 16 with R = 8 is the replay kernel's 16 heads per workgroup,
+// TPW = 1 with R = 8 the conventional kernel's one head per workgroup.
+//
+//   mode 0 (read):        sum each tile's values; one float per workgroup to `sink`
+//   mode 1 (read+write):  dst[tile] = scale * src[tile]; dst == src is the in-place
+//                         update of the flush and conventional steps, dst != src a copy
+//
+// Loads and stores are plain or non-temporal (the decode kernels stream the checkpoint
+// with non-temporal accesses).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm_probe {
+
+constexpr int kThreads = 256;
+constexpr int kCols = 128;                   // floats per row
+constexpr int kLpr = kCols / 4;              // lanes per row (16-byte accesses)
+constexpr int kRpp = kThreads / kLpr;        // rows per pass of the workgroup
+constexpr int64_t kPassFloats = (int64_t)kRpp * kCols;   // one 16-byte access per thread
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ v4f load4(const float* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    else return *reinterpret_cast<const v4f*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store4(float* p, v4f v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+    else *reinterpret_cast<v4f*>(p) = v;
+}
+
+template <int R, int TPW, bool NTL, bool NTS, int MODE>
+__global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src, float* dst,
+                                                                 float* sink, float scale) {
+    constexpr int kR = R;
+    constexpr int64_t kTileFloats = kR * kPassFloats;
+    const int tid = threadIdx.x;
+    const int row0 = tid / kLpr;
+    const int col4 = tid % kLpr;
+    const int64_t first = (int64_t)blockIdx.x * TPW;   // this workgroup's first tile
+    const int64_t lane_off = (int64_t)row0 * kCols + 4 * col4;
+    v4f va[kR], vb[kR];
+    auto issue = [&](int t, v4f (&v)[kR]) {
+        const float* p = src + (first + t) * kTileFloats + lane_off;
+#pragma unroll
+        for (int k = 0; k < kR; ++k) v[k] = load4<NTL>(p + (int64_t)k * kRpp * kCols);
+    };
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    auto finish = [&](int t, const v4f (&v)[kR]) {
+        if constexpr (MODE == 0) {
+#pragma unroll
+            for (int k = 0; k < kR; ++k) acc += v[k];
+        } else {
+            float* p = dst + (first + t) * kTileFloats + lane_off;
+#pragma unroll
+            for (int k = 0; k < kR; ++k) store4<NTS>(p + (int64_t)k * kRpp * kCols, v[k] * scale);
+        }
+    };
+    issue(0, va);
+    for (int t = 0; t + 1 < TPW; ++t) {
+        issue(t + 1, vb);
+        finish(t, va);
+#pragma unroll
+        for (int k = 0; k < kR; ++k) va[k] = vb[k];
+    }
+    finish(TPW - 1, va);
+    if constexpr (MODE == 0) {
+        // one value per workgroup keeps the loads live; the order of the sum is irrelevant
+        __shared__ float part[kThreads / 64];
+        float s = acc.x + acc.y + acc.z + acc.w;
+        for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+        if ((tid & 63) == 0) part[tid / 64] = s;
+        __syncthreads();
+        if (tid == 0) sink[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+    }
+}
+
+template <int R, int TPW, int MODE>
+static const void* pick_nt(bool ntl, bool nts) {
+    if (ntl) return nts ? (const void*)&stream_probe_kernel<R, TPW, true, true, MODE>
+                        : (const void*)&stream_probe_kernel<R, TPW, true, false, MODE>;
+    return nts ? (const void*)&stream_probe_kernel<R, TPW, false, true, MODE>
+               : (const void*)&stream_probe_kernel<R, TPW, false, false, MODE>;
+}
+
+template <int R, int TPW>
+static const void* pick_mode(int mode, bool ntl, bool nts) {
+    return mode == 0 ? pick_nt<R, TPW, 0>(ntl, false) : pick_nt<R, TPW, 1>(ntl, nts);
+}
+
+template <int R>
+static const void* pick(int tpw, int mode, bool ntl, bool nts) {
+    return tpw == 1 ? pick_mode<R, 1>(mode, ntl, nts)
+         : tpw == 4 ? pick_mode<R, 4>(mode, ntl, nts)
+                    : pick_mode<R, 16>(mode, ntl, nts);
+}
+
+}  // namespace rssm_probe
+
+extern "C" {
+
+// Floats one workgroup moves per tile pass (one 16-byte access per thread); a tile with
+// R rows per thread is R times that.
+int64_t replayssm_probe_pass_floats(void) { return rssm_probe::kPassFloats; }
+
+// One probe launch on `stream`.
+//   src       device f32 [n_floats], 16-byte aligned (read by every mode)
+//   dst       mode 1: device f32 [n_floats], 16-byte aligned (may equal src); mode 0: ignored
+//   sink      mode 0: device f32 [number of workgroups] (one sum each); mode 1: ignored
+//   n_floats  > 0 and a multiple of pass_floats * rows_per_thread * tiles_per_wg;
+//             the grid is n_floats / that (at most 2^31 - 1 workgroups)
+//   rows_per_thread in {1, 2, 8};  tiles_per_wg in {1, 4, 16}
+//   mode      0 read, 1 read+write;  nt_load / nt_store: nonzero for non-temporal accesses
+// Returns 0 on success, 1 for an invalid argument (nothing launched), 3 when the launch failed.
+int replayssm_probe_stream(const float* src, float* dst, float* sink, int64_t n_floats, int32_t rows_per_thread,
+                           int32_t tiles_per_wg, int32_t mode, int32_t nt_load, int32_t nt_store, float scale,
+                           hipStream_t stream) {
+    using namespace rssm_probe;
+    if (!src || (reinterpret_cast<uintptr_t>(src) & 15) || n_floats <= 0) return 1;
+    if (rows_per_thread != 1 && rows_per_thread != 2 && rows_per_thread != 8) return 1;
+    if (tiles_per_wg != 1 && tiles_per_wg != 4 && tiles_per_wg != 16) return 1;
+    const int64_t per_wg = kPassFloats * rows_per_thread * tiles_per_wg;
+    if (n_floats % per_wg) return 1;
+    if (mode == 0 && !sink) return 1;
+    if (mode == 1 && (!dst || (reinterpret_cast<uintptr_t>(dst) & 15))) return 1;
+    if (mode != 0 && mode != 1) return 1;
+    const int64_t grid = n_floats / per_wg;
+    if (grid > INT32_MAX) return 1;
+    const bool ntl = nt_load != 0, nts = nt_store != 0;
+    const void* fn = rows_per_thread == 1 ? pick<1>(tiles_per_wg, mode, ntl, nts)
+                   : rows_per_thread == 2 ? pick<2>(tiles_per_wg, mode, ntl, nts)
+                                          : pick<8>(tiles_per_wg, mode, ntl, nts);
+    void* args[] = {(void*)&src, (void*)&dst, (void*)&sink, (void*)&scale};
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+    return e == hipSuccess ? 0 : 3;
+}
+
+}  // extern "C"
