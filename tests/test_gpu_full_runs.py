@@ -1,0 +1,313 @@
+"""GPU parity over every step of each workload's full run, on 8 sampled sequences.
+
+The workloads are the full-size configurations (batch 256): mamba2_h64 (256 steps),
+mamba2_h128 (1024 steps, run with fp32 checkpoint reads and, in lockstep, with bf16,
+fp16 and fp8 read copies), mamba2_spec_h128 (256 speculative rounds of 4 positions),
+gdn_hv32 (512 steps) and gdn_spec_hv32 (256 rounds).  The whole batch runs on the GPU:
+its inputs cycle the workload's first 2L steps (drawn by the workload's seeded
+generator and kept on the device, as the benchmark does), except that the 8 sampled
+sequences (the first and the last included) get fresh inputs every step from a second
+seeded generator.  The fp64 oracle runs those 8 sequences over the whole run.
+
+Bars: outputs max |d| <= 1e-4 (1 + |ref|) elementwise (fp32 reads); every flushed
+checkpoint of a sampled sequence against the oracle's checkpoint at the same bar;
+cursors (and flushed, head, committed) of the whole batch bit for bit.  Read copies:
+every step within the copy's rounding bound, |d| <= |g(z)| decay (eps . |C|) + 1e-4 (1 +
+|ref|) with eps the format's half unit in the last place at the checkpoint the copy
+was made of (oracle.readcopy.copy_error_bound), and for the 16-bit copies also within
+2e-2 RMS(ref) (fp8 keeps 3 mantissa bits, 16 times the bf16 rounding; its max|d|/RMS
+is printed, not asserted); the fp32
+checkpoint after every flush bit-identical to the fp32-read run (the copy's rounding
+never enters the recurrence: "ReplaySSM" README, benefit "Separate state precisions").
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_model_ssm_amd import replayssm as rs
+from hybrid_model_ssm_amd import synth
+from oracle import gdn as og
+from oracle import mamba2 as om
+from oracle import readcopy as rc
+from tests.gpu_helpers import DEV, GpuMamba2, assert_fp32_close, require_gpu, rms_violation, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = np.array([0, 1, 37, 100, 128, 201, 254, 255])
+POOL = 32          # 2L device-resident steps, as the benchmark cycles
+SAMPLE_SEED = 500  # offset of the sampled rows' generator seed from the workload's
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class PooledSteps:
+    """Device inputs of the whole batch for each step: the workload's first POOL steps
+    cycled, with the sampled rows replaced by fresh draws of ``sample_gen``.  ``types``
+    maps each input name to its device dtype.  Speculative workloads also give each
+    round's kept-position counts (the pool's for the other rows, fresh for the sample)."""
+
+    def __init__(self, gen, sample_gen, types, n_pos=None, sample=SAMPLE):
+        self.gen, self.sample_gen, self.types, self.n_pos = gen, sample_gen, types, n_pos
+        self.idx = torch.from_numpy(sample).to(DEV)
+        self.pool, self.keeps = [], []
+        for _ in range(POOL):
+            s = gen.step(n_pos=n_pos) if n_pos else gen.step()
+            self.pool.append({k: to_dev(s[k], types[k]) for k in types})
+            if n_pos:
+                self.keeps.append(gen.accepted(n_pos - 1) + 1)
+        self.bufs = {k: torch.empty_like(v) for k, v in self.pool[0].items()}
+
+    def step(self, t):
+        """Returns (device inputs of the whole batch, host inputs of the sample, kept
+        counts of the whole batch or None)."""
+        s = self.sample_gen.step(n_pos=self.n_pos) if self.n_pos else self.sample_gen.step()
+        for k, buf in self.bufs.items():
+            buf.copy_(self.pool[t % POOL][k])
+            buf[self.idx] = to_dev(s[k], self.types[k])
+        keep = None
+        if self.n_pos:
+            keep = self.keeps[t % POOL].copy()
+            keep[SAMPLE] = self.sample_gen.accepted(self.n_pos - 1) + 1
+        return self.bufs, s, keep
+
+
+def _mamba2_pooled(name, n_pos=None):
+    w = synth.WORKLOADS[name]
+    gen = synth.mamba2_inputs(name)
+    sgen = synth.Mamba2Inputs(len(SAMPLE), w["nheads"], w["headdim"], w["dstate"], w["ngroups"], io=w["io"],
+                              seed=w["seed"] + SAMPLE_SEED, draw_ckpt=False)
+    io = torch.bfloat16 if w["io"] == "bf16" else torch.float32
+    return w, gen, PooledSteps(gen, sgen, {k: io for k in ("x", "z", "B", "C", "dt_raw")}, n_pos=n_pos)
+
+
+# ---------------------------------------------------------------------------------------
+# Mamba2 autoregressive decode: mamba2_h64 (256 steps), mamba2_h128 (1024 steps, with the
+# three read copies in lockstep)
+# ---------------------------------------------------------------------------------------
+
+_FP8_LUT = np.array([rc.e4m3_value(c) for c in range(256)])
+
+
+def _copy_eps(h, kind):
+    """Rounding bound of a copy made of a checkpoint equal to ``h`` up to the fp32 fold's
+    rounding (1e-4 relative headroom on the format's half unit in the last place)."""
+    scale = np.max(np.abs(h), axis=-1) / 448.0 if kind == "fp8" else None
+    return rc.copy_error_bound(h, kind, scale) * (1 + 1e-4)
+
+
+def _copy_values_fast(state, kind):
+    """Values the kernels read from a copy (host float64); fp8 codes through the format's
+    value table."""
+    if kind == "fp8":
+        codes = state.ckpt_lp[torch.from_numpy(SAMPLE).to(DEV)].cpu().numpy()
+        scale = state.lp_scale[torch.from_numpy(SAMPLE).to(DEV)].cpu().numpy().astype(np.float64)
+        return _FP8_LUT[codes] * scale[..., None]
+    return state.ckpt_lp[torch.from_numpy(SAMPLE).to(DEV)].to(torch.float64).cpu().numpy()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,kinds", [("mamba2_h64", ()), ("mamba2_h128", ("bf16", "f16", "fp8"))],
+                         ids=["mamba2_h64", "mamba2_h128"])
+def test_mamba2_every_step_of_the_run(name, kinds):
+    w, gen, steps = _mamba2_pooled(name)
+    st = gen.static
+    B, H, G, L = w["batch"], w["nheads"], w["ngroups"], w["buffer_len"]
+    desc = rs.Mamba2Desc(B, H, w["headdim"], w["dstate"], G, L, rs.BF16, True)
+    fp = GpuMamba2(desc, st)
+    lps = {k: GpuMamba2(desc, st, lowp=k) for k in kinds}
+    rep = om.Mamba2Replay(st.ckpt[SAMPLE], L, st.A, st.D, st.dt_bias, G)
+    eps = {k: _copy_eps(st.ckpt[SAMPLE].astype(np.float64), k) for k in kinds}
+    idx = torch.from_numpy(SAMPLE).to(DEV)
+    worst = {k: 0.0 for k in kinds}
+    worst_rms = {k: 0.0 for k in kinds}
+    n_flush = 0
+    for t in range(1, w["steps"] + 1):
+        dev, s, _ = steps.step(t - 1)
+        ref, flushed = rep.step(**s)
+        args = [dev[k] for k in ("x", "z", "B", "C", "dt_raw")]
+        outs = {}
+        for key, run in [("f32", fp)] + list(lps.items()):
+            rs.mamba2_decode(desc, run.state, run.cur[run.flip], run.cur[1 - run.flip], *args, run.dt_bias,
+                             run.A, run.D, run.out, run.err)
+            run.flip ^= 1
+            outs[key] = run.out[idx].cpu().numpy()
+        assert_fp32_close(outs["f32"], ref, f"{name} step {t}")
+        assert torch.equal(fp.cursor, torch.full((B,), t % L, dtype=torch.int32, device=DEV)), f"step {t}"
+        if kinds and not flushed.all():
+            # the copy's rounding through this step's read: |g(z)| decay (eps . |C|)
+            dts = np.stack([np.stack([r[2] for r in rep.records[b]]) for b in range(len(SAMPLE))])
+            decay = np.stack([om.window_coefficients(dts[b], st.A)[0] for b in range(len(SAMPLE))])
+            gmag = np.abs(om.gate(np.ones_like(s["z"], dtype=np.float64), s["z"]))
+            absC = np.abs(om.heads_of_groups(s["C"], H))[..., None]          # [8, H, N, 1]
+        for k, run in lps.items():
+            assert torch.equal(run.cursor, fp.cursor), f"{k} step {t}"
+            if flushed.all():       # flush steps read the fp32 checkpoint
+                assert_fp32_close(outs[k], ref, f"{k} flush step {t}")
+                continue
+            bound = gmag * decay[..., None] * np.matmul(eps[k], absC)[..., 0]
+            v = float(np.max(np.abs(outs[k] - ref) / (bound + 1e-4 * (1 + np.abs(ref)))))
+            worst[k] = max(worst[k], v)
+            assert v <= 1.0, f"{k} step {t}: {v:.3g} of the rounding bound"
+            vr = rms_violation(outs[k], ref)
+            worst_rms[k] = max(worst_rms[k], vr)
+            if k != "fp8":   # 2e-2 RMS is the bar for 16-bit reads; fp8 keeps 3 mantissa bits
+                assert vr <= 1.0, f"{k} step {t}: max|d| / (2e-2 RMS) = {vr:.3g}"
+        if flushed.all():
+            n_flush += 1
+            assert_fp32_close(fp.state.ckpt[idx].cpu().numpy(), rep.ckpt, f"{name} checkpoint step {t}")
+            for k, run in lps.items():
+                assert torch.equal(run.state.ckpt, fp.state.ckpt), f"{k} step {t}: fp32 checkpoint differs"
+                eps[k] = _copy_eps(rep.ckpt, k)
+                if n_flush % 8 == 1 or t == w["steps"]:
+                    got = _copy_values_fast(run.state, k)
+                    e = eps[k] + 1e-5 * np.abs(rep.ckpt) + 2e-6
+                    c = float(np.max(np.abs(got - rep.ckpt) / e))
+                    assert c <= 1.0, f"{k} copy refreshed at step {t}: {c:.3g} of the bound"
+        else:
+            assert not flushed.any()
+    assert n_flush == w["steps"] // L
+    assert fp.err.item() == 0 and all(run.err.item() == 0 for run in lps.values())
+    print(f"{name}: {w['steps']} steps, worst read-copy errors (of the rounding bound) {worst}, "
+          f"(of 2e-2 RMS) {worst_rms}")
+
+
+# ---------------------------------------------------------------------------------------
+# Mamba2 speculative verification: mamba2_spec_h128, 256 rounds
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.timeout(900)
+def test_mamba2_spec_every_round_of_the_run():
+    name = "mamba2_spec_h128"
+    w = synth.WORKLOADS[name]
+    T = w["n_pos"]
+    _, gen, rounds = _mamba2_pooled(name, n_pos=T)
+    st = gen.static
+    B, H, G, L = w["batch"], w["nheads"], w["ngroups"], w["buffer_len"]
+    desc = rs.Mamba2Desc(B, H, w["headdim"], w["dstate"], G, L, rs.BF16, True)
+    state = rs.Mamba2State.allocate(desc, ckpt=to_dev(st.ckpt, torch.float32))
+    A, D, bias = (to_dev(a, torch.float32) for a in (st.A, st.D, st.dt_bias))
+    z = lambda: torch.zeros(B, dtype=torch.int32, device=DEV)  # noqa: E731
+    head, com, flushed = z(), z(), z()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, T, H, w["headdim"], dtype=torch.float32, device=DEV)
+    spec = om.Mamba2Spec(st.ckpt[SAMPLE], L, st.A, st.D, st.dt_bias, G)
+    idx = torch.from_numpy(SAMPLE).to(DEV)
+    hd_all = np.zeros(B, np.int64)
+    cm_all = np.zeros(B, np.int64)
+    n_flush = 0
+    for r in range(w["rounds"]):
+        dev, s, keep = rounds.step(r)
+        ck_before = state.ckpt[idx].clone()
+        ref, fl_ref = spec.verify(**s)
+        rs.mamba2_spec_verify(desc, state, head, com, T, *(dev[k] for k in ("x", "z", "B", "C", "dt_raw")),
+                              bias, A, D, out, flushed, err)
+        assert_fp32_close(out[idx].cpu().numpy(), ref, f"round {r}")
+        fl = flushed.cpu().numpy()
+        assert np.array_equal(fl, (cm_all + T > L).astype(np.int32)), f"round {r}: flushed"
+        assert np.array_equal(fl[SAMPLE], fl_ref.astype(np.int32)), f"round {r}: flushed (sample)"
+        ck = state.ckpt[idx]
+        for i in range(len(SAMPLE)):
+            if fl_ref[i]:
+                n_flush += 1
+                assert_fp32_close(ck[i].cpu().numpy(), spec.ckpt[i], f"round {r} seq {SAMPLE[i]} fold")
+            else:
+                assert torch.equal(ck[i], ck_before[i]), f"round {r}: checkpoint of seq {SAMPLE[i]} written"
+        rs.commit(B, L, T, head, com, flushed, torch.from_numpy(keep.astype(np.int32)).to(DEV), err)
+        spec.commit(keep[SAMPLE])
+        hd_all = np.where(fl == 1, (hd_all + cm_all) % L, hd_all)
+        cm_all = np.where(fl == 1, 0, cm_all) + keep
+        assert np.array_equal(head.cpu().numpy(), hd_all.astype(np.int32)), f"round {r}: head"
+        assert np.array_equal(com.cpu().numpy(), cm_all.astype(np.int32)), f"round {r}: committed"
+        assert np.array_equal(cm_all[SAMPLE], spec.committed) and np.array_equal(hd_all[SAMPLE], spec.head)
+    assert n_flush > 0 and err.item() == 0
+
+
+# ---------------------------------------------------------------------------------------
+# Gated DeltaNet: gdn_hv32 (512 steps), gdn_spec_hv32 (256 rounds)
+# ---------------------------------------------------------------------------------------
+
+def _gdn_pooled(name, n_pos=None):
+    w = synth.WORKLOADS[name]
+    gen = synth.gdn_inputs(name)
+    sgen = synth.GDNInputs(len(SAMPLE), w["num_v_heads"], w["num_k_heads"], w["dk"], w["dv"], io=w["io"],
+                           seed=w["seed"] + SAMPLE_SEED)
+    io = torch.bfloat16 if w["io"] == "bf16" else torch.float32
+    types = {"q": io, "k": io, "v": io, "alpha": torch.float32, "beta": torch.float32}
+    return w, gen, PooledSteps(gen, sgen, types, n_pos=n_pos)
+
+
+@pytest.mark.timeout(900)
+def test_gdn_every_step_of_the_run():
+    w, gen, steps = _gdn_pooled("gdn_hv32")
+    st = gen.static
+    B, HV, HK, dk, dv, L = (w[k] for k in ("batch", "num_v_heads", "num_k_heads", "dk", "dv", "buffer_len"))
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    state = rs.GdnState.allocate(desc, ckpt=to_dev(st.ckpt, torch.float32))
+    cur = [torch.zeros(B, dtype=torch.int32, device=DEV) for _ in range(2)]
+    out = torch.empty(B, HV, dv, dtype=torch.float32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rep = og.GDNReplay(st.ckpt[SAMPLE], L, HK)
+    idx = torch.from_numpy(SAMPLE).to(DEV)
+    n_flush = 0
+    for t in range(1, w["steps"] + 1):
+        dev, s, _ = steps.step(t - 1)
+        ref, flushed = rep.step(**s)
+        rs.gdn_decode(desc, state, cur[(t - 1) % 2], cur[t % 2], *(dev[k] for k in ("q", "k", "v", "alpha", "beta")),
+                      out, err)
+        assert_fp32_close(out[idx].cpu().numpy(), ref, f"gdn step {t}")
+        assert torch.equal(cur[t % 2], torch.full((B,), t % L, dtype=torch.int32, device=DEV)), f"step {t}"
+        if flushed.all():
+            n_flush += 1
+            assert_fp32_close(state.ckpt[idx].cpu().numpy(), rep.ckpt, f"gdn checkpoint step {t}")
+        else:
+            assert not flushed.any()
+    assert n_flush == w["steps"] // L and err.item() == 0
+
+
+@pytest.mark.timeout(900)
+def test_gdn_spec_every_round_of_the_run():
+    name = "gdn_spec_hv32"
+    w = synth.WORKLOADS[name]
+    T = w["n_pos"]
+    _, gen, rounds = _gdn_pooled(name, n_pos=T)
+    st = gen.static
+    B, HV, HK, dk, dv, L = (w[k] for k in ("batch", "num_v_heads", "num_k_heads", "dk", "dv", "buffer_len"))
+    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
+    state = rs.GdnState.allocate(desc, ckpt=to_dev(st.ckpt, torch.float32))
+    z = lambda: torch.zeros(B, dtype=torch.int32, device=DEV)  # noqa: E731
+    head, com, flushed = z(), z(), z()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, T, HV, dv, dtype=torch.float32, device=DEV)
+    spec = og.GDNSpec(st.ckpt[SAMPLE], L, HK)
+    idx = torch.from_numpy(SAMPLE).to(DEV)
+    hd_all = np.zeros(B, np.int64)
+    cm_all = np.zeros(B, np.int64)
+    n_flush = 0
+    for r in range(w["rounds"]):
+        dev, s, keep = rounds.step(r)
+        ck_before = state.ckpt[idx].clone()
+        ref, fl_ref = spec.verify(**s)
+        rs.gdn_spec_verify(desc, state, head, com, T, *(dev[k] for k in ("q", "k", "v", "alpha", "beta")), out,
+                           flushed, err)
+        assert_fp32_close(out[idx].cpu().numpy(), ref, f"gdn round {r}")
+        fl = flushed.cpu().numpy()
+        assert np.array_equal(fl, (cm_all + T > L).astype(np.int32)), f"round {r}: flushed"
+        assert np.array_equal(fl[SAMPLE], fl_ref.astype(np.int32)), f"round {r}: flushed (sample)"
+        ck = state.ckpt[idx]
+        for i in range(len(SAMPLE)):
+            if fl_ref[i]:
+                n_flush += 1
+                assert_fp32_close(ck[i].cpu().numpy(), spec.ckpt[i], f"gdn round {r} seq {SAMPLE[i]} fold")
+            else:
+                assert torch.equal(ck[i], ck_before[i]), f"round {r}: checkpoint of seq {SAMPLE[i]} written"
+        rs.commit(B, L, T, head, com, flushed, torch.from_numpy(keep.astype(np.int32)).to(DEV), err)
+        spec.commit(keep[SAMPLE])
+        hd_all = np.where(fl == 1, (hd_all + cm_all) % L, hd_all)
+        cm_all = np.where(fl == 1, 0, cm_all) + keep
+        assert np.array_equal(head.cpu().numpy(), hd_all.astype(np.int32)), f"round {r}: head"
+        assert np.array_equal(com.cpu().numpy(), cm_all.astype(np.int32)), f"round {r}: committed"
+    assert n_flush > 0 and err.item() == 0

@@ -182,3 +182,45 @@ def test_gdn_spec_hand_example_single_position(golden_dir):
         out, _ = spec.verify(**ins)
         assert np.allclose(out[0, 0, 0], np.array(st["o"]), atol=1e-12)
         spec.commit([1])
+
+
+def _spec_rounds_vs_conventional(rng, spec, S_kept, rounds, Bt, HV, HK, dk, dv, T):
+    """Run speculative rounds and check every output against the conventional recurrence
+    continued from each sequence's kept state; returns the kept states after the rounds."""
+    for _ in range(rounds):
+        steps = [_rand_step(rng, Bt, HV, HK, dk, dv) for _ in range(T)]
+        ins = {key: np.stack([s[key] for s in steps], 1) for key in steps[0]}
+        out, _ = spec.verify(**ins)
+        S = S_kept.copy()
+        states = []
+        for j in range(T):
+            S, o = og.conventional_step(S, **steps[j])
+            states.append(S)
+            assert np.max(np.abs(out[:, j] - o)) <= 1e-12
+        n_keep = rng.integers(1, T + 1, size=Bt)
+        spec.commit(n_keep)
+        S_kept = np.stack([states[n_keep[b] - 1][b] for b in range(Bt)])
+    return S_kept
+
+
+def test_gdn_spec_reset_starts_a_fresh_sequence():
+    """reset() sets head and committed of the listed sequences to 0 and touches nothing
+    else; with the caller's new checkpoint in place, a reset sequence then follows the
+    conventional recurrence from that checkpoint (the records it held are dropped) while
+    the other sequences continue theirs."""
+    rng = np.random.default_rng(26)
+    Bt, HV, HK, dk, dv, L, T = 3, 4, 2, 6, 5, 7, 3
+    S0 = 0.1 * rng.standard_normal((Bt, HV, dv, dk))
+    spec = og.GDNSpec(S0, L, HK)
+    S_kept = _spec_rounds_vs_conventional(rng, spec, S0.copy(), 5, Bt, HV, HK, dk, dv, T)
+    head0, com0, ck0 = spec.head.copy(), spec.committed.copy(), spec.ckpt.copy()
+    assert com0[1] >= 1                     # the sequence to reset holds committed records
+    spec.reset([1])
+    assert spec.head[1] == 0 and spec.committed[1] == 0
+    assert np.array_equal(spec.head[[0, 2]], head0[[0, 2]])
+    assert np.array_equal(spec.committed[[0, 2]], com0[[0, 2]])
+    assert np.array_equal(spec.ckpt, ck0)   # cursors only
+    S_new = 0.1 * rng.standard_normal((HV, dv, dk))
+    spec.ckpt[1] = S_new                    # the caller supplies the new sequence's checkpoint
+    S_kept[1] = S_new
+    _spec_rounds_vs_conventional(rng, spec, S_kept, 6, Bt, HV, HK, dk, dv, T)

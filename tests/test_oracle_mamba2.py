@@ -331,6 +331,44 @@ def test_spec_reset():
     assert list(spec.head) == [0, 5, 0] and list(spec.committed) == [0, 4, 0]
 
 
+def test_spec_reset_starts_a_fresh_sequence():
+    """After reset() and the caller's new checkpoint, a sequence's outputs follow the
+    conventional recurrence from that checkpoint (its old records are dropped) while the
+    other sequences continue theirs."""
+    Bt, H, P, N, G, L, T = 3, 4, 3, 5, 2, 8, 3
+    gen = synth.Mamba2Inputs(Bt, H, P, N, G, io="f32", seed=27)
+    st = gen.static
+    rng = np.random.default_rng(27)
+    spec = om.Mamba2Spec(st.ckpt, L, st.A, st.D, st.dt_bias, G)
+    h_kept = st.ckpt.astype(np.float64)
+
+    def rounds(n, h_kept):
+        for _ in range(n):
+            s = gen.step(n_pos=T)
+            out, _ = spec.verify(**s)
+            h = h_kept.copy()
+            states = []
+            for j in range(T):
+                h, o = om.conventional_step(h, **{k: v[:, j] for k, v in s.items()}, dt_bias=st.dt_bias,
+                                            A=st.A, D=st.D)
+                states.append(h)
+                assert np.max(np.abs(out[:, j] - o)) <= 1e-12
+            n_keep = rng.integers(1, T + 1, size=Bt)
+            spec.commit(n_keep)
+            h_kept = np.stack([states[n_keep[b] - 1][b] for b in range(Bt)])
+        return h_kept
+
+    h_kept = rounds(5, h_kept)
+    head0, com0 = spec.head.copy(), spec.committed.copy()
+    spec.reset([2])
+    assert spec.head[2] == 0 and spec.committed[2] == 0
+    assert np.array_equal(spec.head[:2], head0[:2]) and np.array_equal(spec.committed[:2], com0[:2])
+    h_new = 0.1 * rng.standard_normal((H, P, N))
+    spec.ckpt[2] = h_new
+    h_kept[2] = h_new
+    rounds(6, h_kept)
+
+
 def test_round_bf16_matches_library_cast():
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(13)
