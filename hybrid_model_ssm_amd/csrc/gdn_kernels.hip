@@ -45,7 +45,7 @@ struct GdnShape {
 // records plus this call's positions), T1 the positions.
 struct GdnSmem {
     int NR, T1, oK, oV, oAl, oBe, oQ, oU, oAcc;
-    int oKp, oCv, oDc, oGr, oNm, total;
+    int oGr, oNm, oGW, oDd, oDc, total;
     __host__ __device__ GdnSmem(int DK, int DV, int L, int T, int mode, int NV, int io_bytes) {
         NR = (mode == kGdnSpec) ? L + T : L;
         T1 = T > 1 ? T : 1;
@@ -56,14 +56,14 @@ struct GdnSmem {
         oQ = oBe + NV * NR;                        // [T1][DK]
         oU = oQ + T1 * DK;                         // [NV][T1][DK]  carried-back q
         oAcc = oU + NV * T1 * DK;                  // [NV][T1][DV]  sum_s beta_s kappa_s v_s
-        // fold in matrix form, one value head at a time (see the fold branch)
+        // fold in matrix form over chunks of CH records (see the fold branch)
         constexpr int CH = kGdnFoldChunk;
-        oKp = oAcc + NV * T1 * DV;                 // [L][DK]   K' rows of every chunk
-        oCv = oKp + L * DK;                        // [L][DV]   record part of the fold factors
-        oDc = oCv + L * DV;                        // [L/CH+1]  decay of each chunk
-        oGr = oDc + L / CH + 1;                    // [L][CH]   k_s . k_t within each chunk
-        oNm = oGr + L * CH;                        // [L][CH]   coupling of records within a chunk
-        total = oNm + L * CH;
+        oGr = oAcc + NV * T1 * DV;                 // [L][CH]       k_s . k_t within each chunk
+        oNm = oGr + L * CH;                        // [NV][L][CH]   coupling of records within a chunk
+        oGW = oNm + NV * L * CH;                   // [NV][L][CH]   G (I + Nm)^-1 of each chunk
+        oDd = oGW + NV * L * CH;                   // [NV][L]       a_s beta_s prod_{u<s} a_u
+        oDc = oDd + NV * L;                        // [NV][L/CH+1]  decay of each chunk
+        total = oDc + NV * (L / CH + 1);
     }
 };
 
@@ -82,7 +82,7 @@ struct GdnSmem {
 //               is position j; if committed + n_pos > L the committed rows are folded
 //               first and every position's chain starts after them.
 template <int DK, int DV, typename IO, int MODE>
-__global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
+__global__ void __launch_bounds__(kGdnThreads, MODE == kGdnSpec ? 4 : 1) gdn_replay_kernel(GdnArgs a) {
     using io = Io<IO>;
     using Raw4 = typename io::Raw4;
     using S = GdnShape<DK>;
@@ -371,22 +371,26 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
         // Matrix form over chunks of up to CH records (s = 0..nc-1 within a chunk, oldest
         // first).  Each record updates every row r of the tile as
         //     r <- a_s r + e_s k_s,   e_s = beta_s v_s[i] - a_s beta_s (r . k_s)
-        // with a_s = alpha_s, so after the chunk
-        //     r <- P r + sum_t c_t k_t,   c = Cv[i] - K' r0,
-        // where P is the chunk's decay, K' = G W D K and Cv = G W diag(beta) V for the
-        // unit lower triangular W = (I + Nm)^-1, Nm[s][t] = a_s beta_s (prod_{t<u<s} a_u)
-        // (k_t . k_s) for t < s, D = diag(a_s beta_s prod_{u<s} a_u), G = diag(prod_{u>t}
-        // a_u).  K' and Cv are formed once per value head by forward substitution, one
-        // column per thread; each tile then needs nc independent row dots (one batched
-        // transpose-reduce per 4 records) and a rank-nc update, instead of nc sequential
-        // row all-reduces.
+        // with a_s = alpha_s.  Unrolling the chunk, e solves (I + Nm) e = beta o v_i - D K r0
+        // with Nm[s][t] = a_s beta_s (prod_{t<u<s} a_u) (k_t . k_s) for t < s and D =
+        // diag(a_s beta_s prod_{u<s} a_u), so after the chunk
+        //     r <- P r0 + K^T c,   c = GW (beta o v_i - D (K r0)),   GW = G (I + Nm)^-1,
+        // P the chunk's decay and G = diag(prod_{u>t} a_u).  GW is a CH x CH matrix per
+        // value head and chunk, formed before the tile loop by forward substitution (one
+        // column per thread); each tile row then needs the nc dots K r0, one CH x CH
+        // product and the rank-nc update, all on the matrix cores.
         constexpr int CH = kGdnFoldChunk;
         const int nch = (nf + CH - 1) / CH;
-        float* sKp = smem + lay.oKp;
-        float* sCv = smem + lay.oCv;
+        // the second tile streams while the fold is prepared; afterwards tile u+1 is in
+        // flight while tile u is folded and tile u+2 is requested once u is done (the last
+        // two units are peeled so that every request is unconditional)
+        if (nunit > 1) issue_tile_f(1, vb);
         float* sGr = smem + lay.oGr;
         float* sNm = smem + lay.oNm;
+        float* sGW = smem + lay.oGW;
+        float* sDd = smem + lay.oDd;
         float* sDc = smem + lay.oDc;
+        const int NDC = L / CH + 1;
         // Gram matrix of the k rows within each chunk, shared by the value heads:
         // sGr[s][y] = k_s . k_t for the chunk's earlier row t = s - (s % CH) + y
         for (int pr = tid; pr < nf * CH; pr += kGdnThreads) {
@@ -401,91 +405,105 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 sGr[pr] = m;
             }
         }
-        auto prepare = [&](int vl) {               // K' and Cv of every chunk of value head vl
+        // per value head and record: d_s = a_s beta_s prod_{u<s} a_u (products over the
+        // chunk's records), and each chunk's decay
+        for (int pr = tid; pr < nv * nch; pr += kGdnThreads) {
+            const int vl = pr / nch, ch = pr - vl * nch;
             const float* al = sAl + vl * NR;
             const float* be = sBe + vl * NR;
-            __syncthreads();                        // sGr is complete; earlier readers of sNm, sKp, sCv are done
-            // Nm[s][t] = a_s beta_s (prod_{t<u<s} a_u) (k_t . k_s).  The decay between two
-            // records is a product of the gates in between, never a ratio of running
-            // products: those reach zero in fp32 when gates are small, and 0/0 is NaN.
-            for (int pr = tid; pr < nf * CH; pr += kGdnThreads) {
-                const int s = pr / CH, y = pr % CH, x = s % CH;
-                if (y < x) {
-                    const int t = s - x + y;
-                    float g = al[s] * be[s];
+            const int s0 = ch * CH, nc = min(CH, nf - s0);
+            float pf = 1.f;
+            for (int x = 0; x < nc; ++x) {
+                sDd[vl * L + s0 + x] = al[s0 + x] * be[s0 + x] * pf;
+                pf *= al[s0 + x];
+            }
+            sDc[vl * NDC + ch] = pf;
+        }
+        __syncthreads();
+        // Nm[s][t] = a_s beta_s (prod_{t<u<s} a_u) (k_t . k_s), per value head.  The decay
+        // between two records is a product of the gates in between, never a ratio of
+        // running products: those reach zero in fp32 when gates are small, and 0/0 is NaN.
+        for (int pr = tid; pr < nv * nf * CH; pr += kGdnThreads) {
+            const int vl = pr / (nf * CH), sy = pr - vl * nf * CH;
+            const int s = sy / CH, y = sy % CH, x = s % CH;
+            if (y < x) {
+                const float* al = sAl + vl * NR;
+                const int t = s - x + y;
+                float g = al[s] * sBe[vl * NR + s];
 #pragma unroll
-                    for (int w = 1; w < CH - 1; ++w) {
-                        const int uu = t + w;
-                        const float f = al[min(uu, s)];
-                        g *= (uu < s) ? f : 1.f;
-                    }
-                    sNm[pr] = g * sGr[pr];
+                for (int w = 1; w < CH - 1; ++w) {
+                    const int uu = t + w;
+                    const float f = al[min(uu, s)];
+                    g *= (uu < s) ? f : 1.f;
+                }
+                sNm[vl * L * CH + sy] = g * sGr[sy];
+            }
+        }
+        __syncthreads();
+        // GW = G (I + Nm)^-1 per value head and chunk: column j of W by forward
+        // substitution, W[x][j] = [x == j] - sum_{y<x} Nm[x][y] W[y][j] (the terms y < j
+        // vanish: W is lower triangular), then row t scaled by g_t = prod_{u>t} a_u.  One
+        // wave per (value head, chunk), 16 of its lanes; rows and columns past the chunk's
+        // records are zero (the rows of Nm there are never written, and only feed rows
+        // that are masked).
+        for (int vc = wave; vc < nv * nch; vc += NWAVE) {
+            const int j = lane;
+            const int vl = vc / nch, ch = vc - vl * nch;
+            const int s0 = ch * CH, nc = min(CH, nf - s0);
+            if (j < CH) {
+                const float* al = sAl + vl * NR;
+                const float* nm = sNm + vl * L * CH + s0 * CH;
+                float wc[CH];
+#pragma unroll
+                for (int x = 0; x < CH; ++x) {
+                    float acc = (x == j) ? 1.f : 0.f;
+#pragma unroll
+                    for (int y = 0; y < x; ++y) acc -= nm[x * CH + y] * wc[y];
+                    wc[x] = (x < nc) ? acc : 0.f;
+                }
+                float gs = 1.f;
+#pragma unroll
+                for (int x = CH - 1; x >= 0; --x) {
+                    if (s0 + x < L) sGW[vl * L * CH + (s0 + x) * CH + j] = (j < nc) ? gs * wc[x] : 0.f;
+                    if (x < nc) gs *= al[s0 + x];
                 }
             }
-            __syncthreads();
-            // forward substitution through (I + Nm), one column of K (threads < DK) or of
-            // V (the next DV threads) per thread, chunk after chunk:
-            //     z_s = d_s - sum_{t<s} Nm[s][t] z_t,
-            // d_s = a_s beta_s (prod_{u<s} a_u) k_s[col] or beta_s v_s[col]; then
-            // K'/Cv row s = (prod_{u>s} a_u) z_s (products over the chunk's records)
-            if (tid < DK + DV) {
-                for (int ch = 0; ch < nch; ++ch) {
-                    const int s0 = ch * CH, nc = min(CH, nf - s0);
-                    float z[CH];
-                    float pf = 1.f;
-#pragma unroll
-                    for (int x = 0; x < CH; ++x) {
-                        if (x < nc) {
-                            const int sx = s0 + x;
-                            float acc = (tid < DK) ? al[sx] * be[sx] * pf * io::ld(sK, sx * DK + tid)
-                                                   : be[sx] * io::ld(sV, (vl * NR + sx) * DV + tid - DK);
-#pragma unroll
-                            for (int y = 0; y < x; ++y) acc -= sNm[sx * CH + y] * z[y];
-                            z[x] = acc;
-                            pf *= al[sx];
-                        }
-                    }
-                    if (tid == 0) sDc[ch] = pf;
-                    float gs = 1.f;
-#pragma unroll
-                    for (int x = CH - 1; x >= 0; --x) {
-                        if (x < nc) {
-                            const int sx = s0 + x;
-                            const float v = gs * z[x];
-                            if (tid < DK) sKp[sx * DK + tid] = v;
-                            else sCv[sx * DV + tid - DK] = v;
-                            gs *= al[sx];
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-        };
+        }
+        __syncthreads();
         auto body = [&](int u) {
             const int vl = u / NTILE, tl = u % NTILE;
             const int i = tl * DVT + 16 * wave + fr;          // this lane's row of the value head
+            const float* be = sBe + vl * NR;
             for (int ch = 0; ch < nch; ++ch) {
                 const int s0 = ch * CH, nc = min(CH, nf - s0);
-                // p'[t][row] = K'_t . row for the chunk's records t < 16 (rows of K' past nc
-                // read as zero); lane l ends with t = 4(l >> 4) + j, j < 4, of its row
-                rssm_v4f p = {0.f, 0.f, 0.f, 0.f};
-                const bool tin = fr < nc;
+                // w[s][row] = k_s . row for the chunk's records s < 16 (rows past nc read as
+                // zero); lane l ends with s = 4(l >> 4) + j, j < 4, of its row
+                rssm_v4f w = {0.f, 0.f, 0.f, 0.f};
+                const bool srow = fr < nc;
 #pragma unroll
                 for (int cb = 0; cb < R; ++cb) {
-                    const float4 kp = tin ? *reinterpret_cast<const float4*>(sKp + (s0 + fr) * DK + 16 * cb + 4 * fg)
+                    const float4 kr = srow ? io::ld4(sK, (s0 + fr) * DK + 16 * cb + 4 * fg)
                                           : make_float4(0.f, 0.f, 0.f, 0.f);
-                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.x, va[cb].x, p, 0, 0, 0);
-                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.y, va[cb].y, p, 0, 0, 0);
-                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.z, va[cb].z, p, 0, 0, 0);
-                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(kp.w, va[cb].w, p, 0, 0, 0);
+                    w = __builtin_amdgcn_mfma_f32_16x16x4f32(kr.x, va[cb].x, w, 0, 0, 0);
+                    w = __builtin_amdgcn_mfma_f32_16x16x4f32(kr.y, va[cb].y, w, 0, 0, 0);
+                    w = __builtin_amdgcn_mfma_f32_16x16x4f32(kr.z, va[cb].z, w, 0, 0, 0);
+                    w = __builtin_amdgcn_mfma_f32_16x16x4f32(kr.w, va[cb].w, w, 0, 0, 0);
                 }
-                float c[4];
+                // c = GW y with y_s = beta_s v_s[i] - d_s w_s: the k index of matrix
+                // instruction j is record 4(l >> 4) + j on both operands, so each lane's y
+                // values feed the instructions as they are; lane l ends with c_t, t = 4(l >> 4)
+                // + j, of its row
+                rssm_v4f cm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int t = 4 * fg + j;
-                    c[j] = (t < nc) ? sCv[(s0 + t) * DV + i] - p[j] : 0.f;
+                    const int sj = 4 * fg + j;
+                    const float y = (sj < nc) ? be[s0 + sj] * io::ld(sV, (vl * NR + s0 + sj) * DV + i) -
+                                                    sDd[vl * L + s0 + sj] * w[j]
+                                              : 0.f;
+                    const float gw = srow ? sGW[vl * L * CH + (s0 + fr) * CH + sj] : 0.f;   // rows past nc: zero
+                    cm = __builtin_amdgcn_mfma_f32_16x16x4f32(gw, y, cm, 0, 0, 0);
                 }
-                const float dc = sDc[ch];
+                const float dc = sDc[vl * NDC + ch];
                 // row += sum_t c_t k_t, as (block of 16 columns)^T += K^T c^T: the k index of
                 // matrix instruction j is record 4(l >> 4) + j on both operands
 #pragma unroll
@@ -495,7 +513,7 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                     for (int j = 0; j < 4; ++j) {
                         const int t = 4 * fg + j;
                         const float kv = (t < nc) ? io::ld(sK, (s0 + t) * DK + 16 * cb + fr) : 0.f;
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, c[j], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, cm[j], acc, 0, 0, 0);
                     }
                     va[cb] = make_float4(acc[0], acc[1], acc[2], acc[3]);
                 }
@@ -516,11 +534,13 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
                 }
             }
         };
-        prepare(0);
-        for (int u = 0; u + 1 < nunit; ++u) {
-            issue_tile_f(u + 1, vb);
+        for (int u = 0; u + 2 < nunit; ++u) {
             body(u);
-            if ((u + 1) % NTILE == 0) prepare((u + 1) / NTILE);
+            rotate();
+            issue_tile_f(u + 2, vb);
+        }
+        if (nunit > 1) {
+            body(nunit - 2);
             rotate();
         }
         body(nunit - 1);
@@ -544,21 +564,22 @@ __global__ void __launch_bounds__(kGdnThreads) gdn_replay_kernel(GdnArgs a) {
     // ---- append this call's records ---------------------------------------------------
     if constexpr (MODE == kGdnDecode) {
         if (!fold) {
+            // the step's record is staged in LDS as an exact copy (row c of the window)
             for (int task = tid; task < nv * DV4; task += kGdnThreads) {
                 const int vl = task / DV4, i4 = task % DV4;
-                const size_t sv = sHV + hv0 + vl, iv = bHV + hv0 + vl;
+                const size_t sv = sHV + hv0 + vl;
                 io::straw4(reinterpret_cast<IO*>(a.rec_v), (sv * L + c) * DV + 4 * i4,
-                           io::ldraw4(vin, iv * DV + 4 * i4));
+                           *reinterpret_cast<const Raw4*>(sV + (vl * NR + c) * DV + 4 * i4));
             }
             for (int vl = tid; vl < nv; vl += kGdnThreads) {
-                const size_t g = ((size_t)sb * L + c) * HV + hv0 + vl, iv = bHV + hv0 + vl;
-                a.rec_alpha[g] = a.alpha[iv];
-                a.rec_beta[g] = a.beta[iv];
+                const size_t g = ((size_t)sb * L + c) * HV + hv0 + vl;
+                a.rec_alpha[g] = sAl[vl * NR + c];
+                a.rec_beta[g] = sBe[vl * NR + c];
             }
             if (chunk == 0) {
                 for (int j4 = tid; j4 < DK4; j4 += kGdnThreads)
                     io::straw4(reinterpret_cast<IO*>(a.rec_k), (((size_t)sb * HK + hk) * L + c) * DK + 4 * j4,
-                               io::ldraw4(kin, pos_qk(0) + 4 * j4));
+                               *reinterpret_cast<const Raw4*>(sK + c * DK + 4 * j4));
             }
         }
     } else if constexpr (MODE == kGdnSpec) {
