@@ -1,34 +1,42 @@
 #!/usr/bin/env python3
 """Decode throughput of the ReplaySSM hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--only headline]
+    python bench.py [--steps K] [--warmup W] [--repeats R] [--only headline]
 
 Headline (``value``): Mamba2 replay decode, one layer, B=256, H=128, P=64, N=128,
-G=8, L=16, bf16 inputs, fp32 checkpoint reads -- seq-tokens/s = batch * K / time
-for exactly K timed decode steps (one kernel launch each, flushes included at their
-true rate of one step in L).  Inputs sit in HBM before the timed region: a pool of
-2L pre-drawn steps is cycled.  ``roofline`` gives the replay kernel's algorithmic
-HBM bytes per launch divided by its average launch time (HIP events on the launch
-stream) against the 8 TB/s peak; ``traffic`` is the counter-measured HBM bytes per
-launch from the committed rocprofv3 summary when it matches the current kernel
-source, else null.  ``cpu_baseline`` times the fp64 CPU oracle (replay form) on a
-sample of the same workload, its sequences sharded over worker processes on the host's
-cores (forked before the GPU is touched), and checks the GPU outputs for that sample.
+G=8, L=16, bf16 inputs, fp32 checkpoint reads -- seq-tokens/s = batch * K / time of
+exactly K decode launches (one kernel launch each), the median of R timed regions.
+Every region starts at a flush step, so it holds ceil(K/L) flushes (exactly the true
+rate of one in L when K is a multiple of L, more otherwise); the untimed steps that
+bring the cursors there are counted in ``timing.setup_steps``.  Inputs sit in HBM
+before a region starts: a pool of 2L pre-drawn steps is cycled.  ``roofline`` gives
+the replay kernel's algorithmic HBM bytes per launch divided by its average launch
+time (HIP events on the launch stream) against the 8 TB/s peak; ``traffic`` is the
+counter-measured HBM bytes per launch from the committed rocprofv3 summary when it
+matches the current kernel source, else null.  ``step_split`` times two further
+windows launch by launch: flush and non-flush steps.  ``cpu_baseline`` times the fp64
+CPU oracle (replay and conventional forms, three workloads) on a sample of each, its
+sequences sharded over worker processes on the host's cores (forked before the GPU is
+touched), and checks the GPU outputs of the headline sample.
 
-Measured beside the headline, each with its own timed region: the in-library
-conventional read-update-write kernel on the same inputs, the headline steps captured
-as a graph and replayed, the bf16, fp16 and fp8 read
+Measured beside the headline, each the median of R regions over whole windows (decode)
+or the workload's rounds (speculative): the in-library conventional read-update-write
+kernel, the headline steps captured as a graph and replayed, the bf16, fp16 and fp8 read
 copies, the state-and-output decode route, the B=256/H=64 layer, speculative
 verification (4 positions, commit) against the per-position snapshot baseline, and the
 Gated DeltaNet layer (replay decode and conventional; speculative verification against
-its snapshot baseline).  ``ceiling`` reports plain device read and copy bandwidth.
+its snapshot baseline).  Each variant carries its counter traffic when a matching
+summary is committed.  ``ceiling`` reports the device's streaming limits from the
+hand-written probes (read, in-place read+write, copy).
 
 Auxiliary modes used to make the committed rocprofv3 summaries:
-    --calibrate-copy        also run a plain 1 GiB device copy (counter calibration)
-    --pmc-summarize FETCH_DIR WRITE_DIR  turn two rocprofv3 --pmc runs into a summary
-    --stats-summarize STATS_DIR          turn a rocprofv3 --kernel-trace --stats run into a summary
-    --precision-sweep       output error of emulated read and recurrence precisions
-                            (bf16, fp16, fp8) against fp32, over 1024 steps
+    --profile-variant NAME   W+K untimed dispatches of one variant and the 1 GiB
+                             calibration copy (run under rocprofv3 --pmc)
+    --pmc-summarize FETCH_DIR WRITE_DIR PROFILE_JSON   two --pmc runs into a summary
+    --stats-summarize STATS_DIR BENCH_JSON   a --kernel-trace --stats run of the default
+                             command into a summary
+    --precision-sweep        output error of emulated read and recurrence precisions
+                             (bf16, fp16, fp8) against fp32, over 1024 steps
 """
 
 from __future__ import annotations
@@ -50,23 +58,7 @@ METRIC = "Mamba2 decode seq-tokens/s at B=256, L=16 + achieved HBM GB/s vs peak"
 PEAK_GBPS = 8000.0
 HEADLINE = "mamba2_h128"
 KERNEL_SOURCES = ["hybrid_model_ssm_amd/csrc/mamba2_kernels.h", "hybrid_model_ssm_amd/csrc/device_common.h"]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_pmc.txt")
-STATS_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_kernel_stats.txt")
 REPLAY_KERNEL_TAG = "mamba2_replay_kernel<64, 128, unsigned short, 0, 0>"
-GDN_KERNEL_TAG = "gdn_replay_kernel<128, 128, unsigned short, 0>"
-# kernels with committed HBM counter summaries: the kernel, the sources its hash covers,
-# the summary file and its title lines
-COUNTED = {
-    "headline": dict(tag=REPLAY_KERNEL_TAG, sources=KERNEL_SOURCES, summary=PMC_SUMMARY,
-                     title=["# rocprofv3 HBM counters: Mamba2 replay decode kernel, workload mamba2_h128",
-                            "# (B=256 H=128 P=64 N=128 G=8 L=16, bf16 io, fp32 checkpoint reads)"]),
-    "gdn": dict(tag=GDN_KERNEL_TAG,
-                sources=["hybrid_model_ssm_amd/csrc/gdn_kernels.hip", "hybrid_model_ssm_amd/csrc/device_common.h"],
-                summary=os.path.join(ROOT, "profiles", "gdn_replay_decode_hv32_pmc.txt"),
-                title=["# rocprofv3 HBM counters: Gated DeltaNet replay decode kernel, workload gdn_hv32",
-                       "# (B=256 HV=32 HK=16 dk=dv=128 L=16, bf16 io; 544 dispatches = 34 windows, flushes "
-                       "included)"]),
-}
 COPY_BYTES = 1 << 30
 MiB = float(1 << 20)
 
@@ -143,14 +135,6 @@ def gdn_replay_bytes(B, HV, HK, dk, dv, L, io, c):
     return B * HV * per_hv + B * HK * per_hk
 
 
-def gdn_window_bytes():
-    """Average algorithmic bytes per GDN decode launch over one window (gdn_hv32)."""
-    from hybrid_model_ssm_amd import synth
-    w = synth.WORKLOADS["gdn_hv32"]
-    B, HV, HK, dk, dv, L = w["batch"], w["num_v_heads"], w["num_k_heads"], w["dk"], w["dv"], w["buffer_len"]
-    return sum(gdn_replay_bytes(B, HV, HK, dk, dv, L, 2, c) for c in range(L)) / L
-
-
 def gdn_conventional_bytes(B, HV, HK, dk, dv, io):
     return B * HV * (2 * dv * dk * 4 + dv * io + 8 + dv * 4) + B * HK * 2 * dk * io
 
@@ -170,30 +154,10 @@ def gdn_spec_baseline_bytes(B, HV, HK, dk, dv, io, T):
     return B * HV * (dv * dk * 4 * (1 + T) + T * (dv * io + 8 + dv * 4)) + B * HK * T * 2 * dk * io
 
 
+
 # ------------------------------------------------------------------------------------
-# timing
+# runners: one kind of dispatch on device-resident inputs
 # ------------------------------------------------------------------------------------
-
-class Timer:
-    """HIP events on the current (launch) stream around exactly ``n`` launches."""
-
-    def __init__(self, torch):
-        self.torch = torch
-
-    def run(self, launch, first, n):
-        torch = self.torch
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        e0.record()
-        for i in range(first, first + n):
-            launch(i)
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-        return e0.elapsed_time(e1) / 1e3, wall
-
 
 def _check(st, name):
     if st != 0:
@@ -201,11 +165,38 @@ def _check(st, name):
         raise rs.ReplaySSMError(st, name)
 
 
-class Mamba2Bench:
-    """Device buffers and pre-marshalled launch arguments for one Mamba2 workload."""
+class Runner:
+    """One workload variant.  ``launch(i)`` enqueues dispatch i (a decode step or a
+    speculative round, counted from the fresh state) on the current stream;
+    ``bytes_of(i)`` and ``tokens_of(i)`` are its algorithmic HBM bytes and the tokens
+    it completes; ``check(n)`` validates the device state after n dispatches.  ``period``
+    is the number of dispatches per window (decode: L, so a flush every L steps)."""
 
-    def __init__(self, torch, rs, synth, name, pool=32, lowp=False, conventional=False, seed_override=None,
-                 state_and_output=False):
+    unit = "seq-tokens/s"
+    period = 1
+    tag = None       # kernel name as rocprofv3 prints it
+    sources = None   # kernel sources the counters depend on
+
+    def bytes_of(self, i):
+        raise NotImplementedError
+
+    def tokens_of(self, i):
+        return self.B
+
+    def check(self, n):
+        pass
+
+
+MAMBA2_SOURCES = ["hybrid_model_ssm_amd/csrc/mamba2_kernels.h", "hybrid_model_ssm_amd/csrc/device_common.h"]
+GDN_SOURCES = ["hybrid_model_ssm_amd/csrc/gdn_kernels.hip", "hybrid_model_ssm_amd/csrc/device_common.h"]
+LP_CODE = {False: 0, "bf16": 1, "f16": 2, "fp8": 3}
+
+
+class Mamba2Runner(Runner):
+    """Mamba2 autoregressive decode: replay (fp32 reads or a read copy, output-only or
+    state-and-output route) or the conventional read-update-write kernel."""
+
+    def __init__(self, torch, rs, synth, name, pool=32, lowp=False, conventional=False, state_and_output=False):
         import ctypes
         self.torch, self.rs = torch, rs
         w = dict(synth.WORKLOADS[name])
@@ -213,37 +204,36 @@ class Mamba2Bench:
         self.B, self.H, self.P, self.N, self.G, self.L = (w["batch"], w["nheads"], w["headdim"], w["dstate"],
                                                           w["ngroups"], w["buffer_len"])
         self.io = 2 if w["io"] == "bf16" else 4
-        gen = synth.mamba2_inputs(name) if seed_override is None else synth.mamba2_inputs(name, seed=seed_override)
+        self.period = 1 if conventional else self.L
+        gen = synth.mamba2_inputs(name)
         st = gen.static
-        self.static = st
         dev = "cuda"
         f32 = torch.float32
         self.desc = rs.Mamba2Desc(self.B, self.H, self.P, self.N, self.G, self.L,
                                   rs.BF16 if w["io"] == "bf16" else rs.F32, True)
         iot = self.desc.torch_io
         t = lambda a, d: torch.from_numpy(a).to(dev).to(d)  # noqa: E731
-        self.ckpt0 = t(st.ckpt, f32)
+        ckpt0 = t(st.ckpt, f32)
         self.A, self.D, self.bias = t(st.A, f32), t(st.D, f32), t(st.dt_bias, f32)
-        self.pool_np = [gen.step() for _ in range(pool)]
-        self.pool = [{k: t(v, iot) for k, v in s.items()} for s in self.pool_np]
+        self.pool = [{k: t(v, iot) for k, v in gen.step().items()} for _ in range(pool)]
         self.out = torch.empty(self.B, self.H, self.P, dtype=f32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.conventional = conventional
-        self.lowp = lowp
-        L = rs.lib()
+        self.conventional, self.lowp = conventional, lowp
+        Lb = rs.lib()
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        self.stream = stream
+        shape = f"{self.P}, {self.N}, {'unsigned short' if self.io == 2 else 'float'}"
         if conventional:
-            self.state_conv = self.ckpt0.clone()
+            self.state = ckpt0
             d = self.desc.c()
             self._keep = [d]
-            self.args = [(ctypes.byref(d), self.state_conv.data_ptr(),
+            self.args = [(ctypes.byref(d), self.state.data_ptr(),
                           *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
                           self.bias.data_ptr(), self.A.data_ptr(), self.D.data_ptr(), self.out.data_ptr(), stream)
                          for p in self.pool]
-            self.fn = L.replayssm_selective_state_update
+            self.fn = Lb.replayssm_selective_state_update
+            self.tag = f"mamba2_conventional_kernel<{shape}, false>"
         else:
-            self.state = rs.Mamba2State.allocate(self.desc, lowp=lowp, ckpt=self.ckpt0.clone())
+            self.state = rs.Mamba2State.allocate(self.desc, lowp=lowp, ckpt=ckpt0)
             self.cur = [torch.zeros(self.B, dtype=torch.int32, device=dev) for _ in range(2)]
             d, s = self.desc.c(), self.state.c()
             self._keep = [d, s]
@@ -257,300 +247,416 @@ class Mamba2Bench:
                                   *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
                                   self.bias.data_ptr(), self.A.data_ptr(), self.D.data_ptr(),
                                   self.out.data_ptr(), self.err.data_ptr(), stream))
-            self.fn = L.replayssm_mamba2_decode_state_and_output if state_and_output else L.replayssm_mamba2_decode
+            self.fn = Lb.replayssm_mamba2_decode_state_and_output if state_and_output else Lb.replayssm_mamba2_decode
+            self.tag = f"mamba2_replay_kernel<{shape}, {LP_CODE[lowp]}, {3 if state_and_output else 0}>"
+        self.sources = MAMBA2_SOURCES
 
     def launch(self, i):
-        a = self.args[i % len(self.args)]
-        st = self.fn(*a)
+        st = self.fn(*self.args[i % len(self.args)])
         if st:
             _check(st, self.fn.__name__)
 
-    def bytes_of_step(self, i):
-        """Algorithmic bytes of the i-th launch (0-based) from a fresh state."""
+    def bytes_of(self, i):
         if self.conventional:
             return mamba2_conventional_bytes(self.B, self.H, self.P, self.N, self.G, self.io)
         return mamba2_replay_bytes(self.B, self.H, self.P, self.N, self.G, self.L, self.io, i % self.L, self.lowp)
 
-
-def time_mamba2(torch, rs, synth, name, steps, warmup, **kw):
-    b = Mamba2Bench(torch, rs, synth, name, **kw)
-    for i in range(warmup):
-        b.launch(i)
-    secs, wall = Timer(torch).run(b.launch, warmup, steps)
-    if not b.conventional:
-        exp = (warmup + steps) % b.L
-        if not torch.equal(b.cur[(warmup + steps) % 2], torch.full_like(b.cur[0], exp)):
-            raise RuntimeError("cursor check failed after the timed region")
-        if b.err.item() != 0:
+    def check(self, n):
+        if self.conventional:
+            return
+        torch = self.torch
+        if not torch.equal(self.cur[n % 2], torch.full_like(self.cur[0], n % self.L)):
+            raise RuntimeError("cursor check failed")
+        if self.err.item() != 0:
             raise RuntimeError("device error flag set")
-    nbytes = sum(b.bytes_of_step(i) for i in range(warmup, warmup + steps))
-    res = dict(seq_tokens_per_s=b.B * steps / secs, ms_per_step=secs * 1e3 / steps, seconds=secs, wall_s=wall,
-               bytes_per_step_MiB=nbytes / steps / MiB, hbm_gbps=nbytes / secs / 1e9,
-               frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS, steps=steps)
-    return res, b
 
 
-def time_mamba2_graph(torch, rs, synth, name, steps, warmup):
-    """The same decode steps captured as one graph of two windows (2L launches, so that
-    flushes keep their rate and the ping-pong cursors line up) and replayed: the launch
-    overhead of single calls taken out.  Times steps // (2L) replays."""
-    b = Mamba2Bench(torch, rs, synth, name)
-    W = 2 * b.L
-    warm = -(-warmup // W) * W
-    for i in range(warm):
-        b.launch(i)
+class SpecRunner(Runner):
+    """Mamba2 or Gated DeltaNet speculative rounds (verify + commit) on the circular
+    buffer, or the per-position snapshot baseline.  Round r uses pool entry r % pool; the
+    kept counts come from the workload's seeded generator."""
+
+    unit = "accepted tokens/s"
+
+    def __init__(self, torch, rs, synth, name, baseline=False, pool=32):
+        import ctypes
+        import numpy as np
+        self.torch = torch
+        w = dict(synth.WORKLOADS[name])
+        self.gdn = w["kind"] == "gdn_spec"
+        self.baseline = baseline
+        self.T, self.L, self.B = w["n_pos"], w["buffer_len"], w["batch"]
+        T, L, B = self.T, self.L, self.B
+        dev = "cuda"
+        f32 = torch.float32
+        t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
+        gen = synth.gdn_inputs(name) if self.gdn else synth.mamba2_inputs(name)
+        st = gen.static
+        if self.gdn:
+            self.HV, self.HK, self.dk, self.dv = w["num_v_heads"], w["num_k_heads"], w["dk"], w["dv"]
+            keys = ("q", "k", "v", "alpha", "beta")
+            types = {"q": torch.bfloat16, "k": torch.bfloat16, "v": torch.bfloat16, "alpha": f32, "beta": f32}
+            desc = rs.GdnDesc(B, self.HV, self.HK, self.dk, self.dv, L, rs.BF16)
+            self.out = torch.empty(B, T, self.HV, self.dv, dtype=f32, device=dev)
+            per_state = (self.HV, self.dv, self.dk)
+        else:
+            self.H, self.P, self.N, self.G = w["nheads"], w["headdim"], w["dstate"], w["ngroups"]
+            keys = ("x", "z", "B", "C", "dt_raw")
+            types = {k: torch.bfloat16 for k in keys}
+            desc = rs.Mamba2Desc(B, self.H, self.P, self.N, self.G, L, rs.BF16, True)
+            self.out = torch.empty(B, T, self.H, self.P, dtype=f32, device=dev)
+            per_state = (self.H, self.P, self.N)
+            self.A, self.D, self.bias = t(st.A, f32), t(st.D, f32), t(st.dt_bias, f32)
+        self.pool, self.keeps = [], []
+        for _ in range(pool):
+            s = gen.step(n_pos=T)
+            self.pool.append({k: t(s[k], types[k]) for k in keys})
+            self.keeps.append(gen.accepted(T - 1) + 1)
+        self.keep_dev = [torch.from_numpy(k.astype(np.int32)).to(dev) for k in self.keeps]
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        Lb = rs.lib()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        d = desc.c()
+        self._keep = [d]
+        io_name = "unsigned short"
+        if baseline:
+            # every snapshot slot starts as the initial state; round r reads the slot of the
+            # last position kept in round r - 1
+            self.snaps = t(st.ckpt, f32).unsqueeze(1).repeat(1, T, *([1] * len(per_state))).contiguous()
+            self.slots = [torch.from_numpy((self.keeps[(r - 1) % pool] - 1).astype(np.int32)).to(dev)
+                          for r in range(pool)]
+            if self.gdn:
+                fn = Lb.replayssm_gdn_spec_baseline
+                self.args = [(ctypes.byref(d), self.snaps.data_ptr(), self.slots[r].data_ptr(), T,
+                              *(p[k].data_ptr() for k in keys), self.out.data_ptr(), stream)
+                             for r, p in enumerate(self.pool)]
+                self.tag = f"gdn_conventional_kernel<{self.dk}, {self.dv}, {io_name}, true>"
+            else:
+                fn = Lb.replayssm_mamba2_spec_baseline
+                self.args = [(ctypes.byref(d), self.snaps.data_ptr(), self.slots[r].data_ptr(), T,
+                              *(p[k].data_ptr() for k in keys), self.bias.data_ptr(), self.A.data_ptr(),
+                              self.D.data_ptr(), self.out.data_ptr(), stream) for r, p in enumerate(self.pool)]
+                self.tag = f"mamba2_conventional_kernel<{self.P}, {self.N}, {io_name}, true>"
+            self.calls = [(fn, a) for a in self.args]
+        else:
+            z = lambda: torch.zeros(B, dtype=torch.int32, device=dev)  # noqa: E731
+            self.head, self.com, self.flushed = z(), z(), z()
+            if self.gdn:
+                self.state = rs.GdnState.allocate(desc, ckpt=t(st.ckpt, f32))
+                s_c = self.state.c()
+                fn = Lb.replayssm_gdn_spec_verify
+                self.args = [(ctypes.byref(d), ctypes.byref(s_c), self.head.data_ptr(), self.com.data_ptr(), T, None,
+                              *(p[k].data_ptr() for k in keys), self.out.data_ptr(), self.flushed.data_ptr(),
+                              self.err.data_ptr(), stream) for p in self.pool]
+                self.tag = f"gdn_replay_kernel<{self.dk}, {self.dv}, {io_name}, 2>"
+            else:
+                self.state = rs.Mamba2State.allocate(desc, ckpt=t(st.ckpt, f32))
+                s_c = self.state.c()
+                fn = Lb.replayssm_mamba2_spec_verify
+                self.args = [(ctypes.byref(d), ctypes.byref(s_c), self.head.data_ptr(), self.com.data_ptr(), T, None,
+                              *(p[k].data_ptr() for k in keys), self.bias.data_ptr(), self.A.data_ptr(),
+                              self.D.data_ptr(), self.out.data_ptr(), self.flushed.data_ptr(), self.err.data_ptr(),
+                              stream) for p in self.pool]
+                self.tag = f"mamba2_replay_kernel<{self.P}, {self.N}, {io_name}, 0, 2>"
+            self._keep.append(s_c)
+            commit = Lb.replayssm_commit
+            self.calls = [(fn, a, (B, L, T, self.head.data_ptr(), self.com.data_ptr(), self.flushed.data_ptr(),
+                                   self.keep_dev[r].data_ptr(), None, self.err.data_ptr(), stream))
+                          for r, a in enumerate(self.args)]
+            self.commit = commit
+        self.sources = GDN_SOURCES if self.gdn else MAMBA2_SOURCES
+        self._model = None
+
+    def launch(self, r):
+        c = self.calls[r % len(self.calls)]
+        _check(c[0](*c[1]), c[0].__name__)
+        if not self.baseline:
+            _check(self.commit(*c[2]), "replayssm_commit")
+
+    def _cursor_model(self, n):
+        """Per-round algorithmic bytes and fold counts of rounds 0..n-1 (host model of the
+        commit rule), and the cursors after them."""
+        import numpy as np
+        hd = np.zeros(self.B, np.int64)
+        cm = np.zeros(self.B, np.int64)
+        out = []
+        for r in range(n):
+            fl = cm + self.T > self.L
+            if self.baseline:
+                nb = (gdn_spec_baseline_bytes(self.B, self.HV, self.HK, self.dk, self.dv, 2, self.T) if self.gdn else
+                      spec_baseline_bytes(self.B, self.H, self.P, self.N, self.G, 2, self.T))
+            else:
+                nb = (gdn_spec_round_bytes(self.HV, self.HK, self.dk, self.dv, self.L, 2, self.T, cm) if self.gdn else
+                      spec_round_bytes(self.H, self.P, self.N, self.G, self.L, 2, self.T, cm))
+            out.append((nb, int(fl.sum())))
+            hd = np.where(fl, (hd + cm) % self.L, hd)
+            cm = np.where(fl, 0, cm) + self.keeps[r % len(self.keeps)]
+        return out, hd, cm
+
+    def bytes_of(self, r):
+        if self._model is None or len(self._model) <= r:
+            self._model = self._cursor_model(max(r + 1, 4096))[0]
+        return self._model[r][0]
+
+    def folds_of(self, r):
+        self.bytes_of(r)
+        return self._model[r][1]
+
+    def tokens_of(self, r):
+        return int(self.keeps[r % len(self.keeps)].sum())
+
+    def check(self, n):
+        import numpy as np
+        if self.baseline:
+            return
+        _, hd, cm = self._cursor_model(n)
+        if not (np.array_equal(self.head.cpu().numpy(), hd.astype(np.int32)) and
+                np.array_equal(self.com.cpu().numpy(), cm.astype(np.int32))):
+            raise RuntimeError("speculative cursors disagree with the host model")
+        if self.err.item() != 0:
+            raise RuntimeError("device error flag set")
+
+
+class GdnRunner(Runner):
+    """Gated DeltaNet autoregressive decode: replay, or the conventional kernel."""
+
+    def __init__(self, torch, rs, synth, name="gdn_hv32", conventional=False, pool=32):
+        import ctypes
+        import numpy as np
+        self.torch = torch
+        w = synth.WORKLOADS[name]
+        self.B, self.HV, self.HK, self.dk, self.dv, self.L = (w[k] for k in ("batch", "num_v_heads", "num_k_heads",
+                                                                            "dk", "dv", "buffer_len"))
+        self.conventional = conventional
+        self.period = 1 if conventional else self.L
+        gen = synth.gdn_inputs(name)
+        st = gen.static
+        dev = "cuda"
+        t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
+        desc = rs.GdnDesc(self.B, self.HV, self.HK, self.dk, self.dv, self.L, rs.BF16)
+        keys = ("q", "k", "v", "alpha", "beta")
+        self.pool = []
+        for _ in range(pool):
+            s = gen.step()
+            self.pool.append({"q": t(s["q"], torch.bfloat16), "k": t(s["k"], torch.bfloat16),
+                              "v": t(s["v"], torch.bfloat16), "alpha": t(s["alpha"], torch.float32),
+                              "beta": t(s["beta"], torch.float32)})
+        self.out = torch.empty(self.B, self.HV, self.dv, dtype=torch.float32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        Lb = rs.lib()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        d = desc.c()
+        self._keep = [d]
+        if conventional:
+            self.S = t(st.ckpt, torch.float32)
+            self.fn = Lb.replayssm_gdn_conventional_decode
+            self.args = [(ctypes.byref(d), self.S.data_ptr(), *(p[k].data_ptr() for k in keys), self.out.data_ptr(),
+                          stream) for p in self.pool]
+            self.tag = f"gdn_conventional_kernel<{self.dk}, {self.dv}, unsigned short, false>"
+        else:
+            self.state = rs.GdnState.allocate(desc, ckpt=t(st.ckpt, torch.float32))
+            s_c = self.state.c()
+            self._keep.append(s_c)
+            self.cur = [torch.zeros(self.B, dtype=torch.int32, device=dev) for _ in range(2)]
+            self.fn = Lb.replayssm_gdn_decode
+            self.args = [(ctypes.byref(d), ctypes.byref(s_c), self.cur[i % 2].data_ptr(), self.cur[1 - i % 2].data_ptr(),
+                          *(self.pool[i % pool][k].data_ptr() for k in keys), self.out.data_ptr(),
+                          self.err.data_ptr(), stream) for i in range(2 * pool)]
+            self.tag = f"gdn_replay_kernel<{self.dk}, {self.dv}, unsigned short, 0>"
+        self.sources = GDN_SOURCES
+
+    def launch(self, i):
+        st = self.fn(*self.args[i % len(self.args)])
+        if st:
+            _check(st, self.fn.__name__)
+
+    def bytes_of(self, i):
+        if self.conventional:
+            return gdn_conventional_bytes(self.B, self.HV, self.HK, self.dk, self.dv, 2)
+        return gdn_replay_bytes(self.B, self.HV, self.HK, self.dk, self.dv, self.L, 2, i % self.L)
+
+    def check(self, n):
+        if self.conventional:
+            return
+        torch = self.torch
+        if not torch.equal(self.cur[n % 2], torch.full_like(self.cur[0], n % self.L)):
+            raise RuntimeError("cursor check failed")
+        if self.err.item() != 0:
+            raise RuntimeError("device error flag set")
+
+
+# variant name -> (group of --only, constructor, workload, dispatches per timed region or None for
+# the headline's whole windows)
+VARIANTS = {
+    "mamba2_h128_conventional": ("conventional", lambda T, R, S: Mamba2Runner(T, R, S, HEADLINE, conventional=True),
+                                 HEADLINE, None),
+    "mamba2_h128_bf16_read": ("bf16", lambda T, R, S: Mamba2Runner(T, R, S, HEADLINE, lowp="bf16"), HEADLINE, None),
+    "mamba2_h128_f16_read": ("f16", lambda T, R, S: Mamba2Runner(T, R, S, HEADLINE, lowp="f16"), HEADLINE, None),
+    "mamba2_h128_fp8_read": ("fp8", lambda T, R, S: Mamba2Runner(T, R, S, HEADLINE, lowp="fp8"), HEADLINE, None),
+    "mamba2_h128_state_and_output": ("so", lambda T, R, S: Mamba2Runner(T, R, S, HEADLINE, state_and_output=True),
+                                     HEADLINE, None),
+    "mamba2_h64_replay": ("h64", lambda T, R, S: Mamba2Runner(T, R, S, "mamba2_h64"), "mamba2_h64", 256),
+    "mamba2_h64_conventional": ("h64", lambda T, R, S: Mamba2Runner(T, R, S, "mamba2_h64", conventional=True),
+                                "mamba2_h64", 256),
+    "spec_h128_verify": ("spec", lambda T, R, S: SpecRunner(T, R, S, "mamba2_spec_h128"), "mamba2_spec_h128", 256),
+    "spec_h128_snapshot_baseline": ("spec", lambda T, R, S: SpecRunner(T, R, S, "mamba2_spec_h128", baseline=True),
+                                    "mamba2_spec_h128", 256),
+    "gdn_hv32_replay": ("gdn", lambda T, R, S: GdnRunner(T, R, S), "gdn_hv32", 512),
+    "gdn_hv32_conventional": ("gdn", lambda T, R, S: GdnRunner(T, R, S, conventional=True), "gdn_hv32", 512),
+    "gdn_spec_hv32_verify": ("gdn_spec", lambda T, R, S: SpecRunner(T, R, S, "gdn_spec_hv32"), "gdn_spec_hv32", 256),
+    "gdn_spec_hv32_snapshot_baseline": ("gdn_spec", lambda T, R, S: SpecRunner(T, R, S, "gdn_spec_hv32",
+                                                                               baseline=True), "gdn_spec_hv32", 256),
+}
+GROUPS = ["conventional", "graph", "bf16", "f16", "fp8", "so", "h64", "spec", "gdn", "gdn_spec"]
+
+
+# ------------------------------------------------------------------------------------
+# timing
+# ------------------------------------------------------------------------------------
+
+def timed_region(torch, launch, first, n):
+    """HIP events on the current (launch) stream around exactly ``n`` launches; returns
+    the seconds between them."""
     torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(first, first + n):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3
+
+
+def measure(torch, r, warmup, n, repeats, start_at=None):
+    """Time ``repeats`` regions of exactly ``n`` dispatches of runner ``r`` after
+    ``warmup`` untimed ones.  With ``start_at`` (a position within r.period), untimed
+    dispatches before the warmup and between regions make every region start at that
+    position (for decode: the flush step).  Returns the region results (seconds, bytes,
+    tokens, folds) and the dispatch count."""
+    i = 0
+    setup = 0
+    if start_at is not None:
+        setup = (start_at - warmup) % r.period
+        for _ in range(setup):
+            r.launch(i)
+            i += 1
+    for _ in range(warmup):
+        r.launch(i)
+        i += 1
+    regions = []
+    for _ in range(repeats):
+        if start_at is not None:
+            while i % r.period != start_at:
+                r.launch(i)
+                i += 1
+        secs = timed_region(torch, r.launch, i, n)
+        regions.append(dict(seconds=secs, first=i, bytes=sum(r.bytes_of(j) for j in range(i, i + n)),
+                            tokens=sum(r.tokens_of(j) for j in range(i, i + n)),
+                            flushes=sum(1 for j in range(i, i + n) if j % r.period == r.period - 1)
+                            if r.period > 1 else None))
+        i += n
+    r.check(i)
+    return regions, setup, i
+
+
+def summarize(regions, n, unit_key="per_dispatch"):
+    """The median region by throughput, with every region's throughput."""
+    rates = [g["tokens"] / g["seconds"] for g in regions]
+    order = sorted(range(len(regions)), key=lambda k: rates[k])
+    med = regions[order[len(order) // 2]]
+    secs = med["seconds"]
+    return dict(value=med["tokens"] / secs, ms_per_dispatch=secs * 1e3 / n, dispatches_per_region=n,
+                regions=len(regions), values_per_region=rates, bytes_per_dispatch_MiB=med["bytes"] / n / MiB,
+                hbm_gbps=med["bytes"] / secs / 1e9, frac_of_peak=med["bytes"] / secs / 1e9 / PEAK_GBPS,
+                flush_dispatches_per_region=med["flushes"])
+
+
+def per_step_split(torch, r, first, n):
+    """Duration of every dispatch of ``n`` (events between consecutive launches on the
+    launch stream), split into flush steps (the last position of each window) and the
+    others; ``first`` is the dispatch index to start at.  Returns averages in us."""
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for k in range(n):
+        r.launch(first + k)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    dur = [ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(n)]
+    fl = [d for k, d in enumerate(dur) if (first + k) % r.period == r.period - 1]
+    nf = [d for k, d in enumerate(dur) if (first + k) % r.period != r.period - 1]
+    fb = [r.bytes_of(first + k) for k in range(n) if (first + k) % r.period == r.period - 1]
+    nb = [r.bytes_of(first + k) for k in range(n) if (first + k) % r.period != r.period - 1]
+    res = dict(dispatches=n, flush_us=sum(fl) / len(fl) if fl else None,
+               nonflush_us=sum(nf) / len(nf) if nf else None)
+    if fl:
+        res["flush_gbps"] = (sum(fb) / len(fb)) / (res["flush_us"] * 1e3)
+    if nf:
+        res["nonflush_gbps"] = (sum(nb) / len(nb)) / (res["nonflush_us"] * 1e3)
+    return res, first + n
+
+
+def time_variant(torch, rs, synth, name, K, W, repeats):
+    """One variant of VARIANTS, timed over whole windows (decode) or the workload's
+    rounds, the median of ``repeats`` regions, with the counter traffic of its committed
+    summary when that matches the current source."""
+    group, make, workload, n = VARIANTS[name]
+    r = make(torch, rs, synth)
+    if n is None:                                   # headline shapes: whole windows covering K
+        n = max(2 * r.period, -(-K // r.period) * r.period)
+    w = -(-W // r.period) * r.period
+    regions, _, _ = measure(torch, r, w, n, repeats)
+    res = summarize(regions, n)
+    res.update(unit=r.unit, workload=workload, kernel=f"rssm::{r.tag}")
+    tr = committed_traffic(name)
+    if tr is not None:
+        res.update(traffic_bytes_per_launch=tr["traffic"], traffic_over_algorithmic=tr["ratio"],
+                   traffic_source=tr["source"])
+    else:
+        res.update(traffic_bytes_per_launch=None, traffic_source=committed_traffic_reason(name))
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_graph(torch, rs, synth, K, W, repeats):
+    """The headline steps captured as one graph of two windows (2L launches, so that
+    flushes keep their rate and the ping-pong cursors line up) and replayed: launch
+    overhead taken out.  Each region replays it ceil(K / 2L) times."""
     import ctypes
+    r = Mamba2Runner(torch, rs, synth, HEADLINE)
+    Wn = 2 * r.L
+    warm = -(-W // Wn) * Wn
+    for i in range(warm):
+        r.launch(i)
+    torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         cap = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)   # the capturing stream
-        for j in range(W):
-            a = b.args[(warm + j) % len(b.args)]
-            _check(b.fn(*a[:-1], cap), b.fn.__name__)
-    nrep = max(1, steps // W)
-    probe = b.state.ckpt[0, 0].clone()
+        for j in range(Wn):
+            a = r.args[(warm + j) % len(r.args)]
+            _check(r.fn(*a[:-1], cap), r.fn.__name__)
+    nrep = max(1, -(-K // Wn))
+    probe = r.state.ckpt[0, 0].clone()
     g.replay()                       # one untimed replay; its two flushes must change the checkpoint
     torch.cuda.synchronize()
-    if torch.equal(probe, b.state.ckpt[0, 0]):
+    if torch.equal(probe, r.state.ckpt[0, 0]):
         raise RuntimeError("the captured graph did not run the decode steps")
-    secs, wall = Timer(torch).run(lambda r: g.replay(), 0, nrep)
-    n = nrep * W
-    done = warm + W + n
-    if not torch.equal(b.cur[done % 2], torch.full_like(b.cur[0], done % b.L)):
-        raise RuntimeError("cursor check failed after the graph replays")
-    if b.err.item() != 0:
-        raise RuntimeError("device error flag set")
-    nbytes = sum(b.bytes_of_step(i) for i in range(n))
-    del g, b
-    return dict(seq_tokens_per_s=synth.WORKLOADS[name]["batch"] * n / secs, ms_per_step=secs * 1e3 / n,
-                steps=n, launches_per_graph=W, bytes_per_step_MiB=nbytes / n / MiB, hbm_gbps=nbytes / secs / 1e9,
-                frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS)
-
-
-def time_spec(torch, rs, synth, rounds, warmup, baseline=False, lowp=False):
-    import ctypes
-    import numpy as np
-    w = synth.WORKLOADS["mamba2_spec_h128"]
-    B, H, P, N, G, L, T = w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"], w["buffer_len"], w["n_pos"]
-    io = 2
-    gen = synth.mamba2_inputs("mamba2_spec_h128")
-    st = gen.static
-    dev = "cuda"
-    f32 = torch.float32
-    t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
-    desc = rs.Mamba2Desc(B, H, P, N, G, L, rs.BF16, True)
-    pool_n = 32
-    pool, keeps = [], []
-    for _ in range(pool_n):
-        s = gen.step(n_pos=T)
-        pool.append({k: t(v, torch.bfloat16) for k, v in s.items()})
-        keeps.append(gen.accepted(T - 1) + 1)
-    keep_dev = [torch.from_numpy(k.astype(np.int32)).to(dev) for k in keeps]
-    A, D, bias = t(st.A, f32), t(st.D, f32), t(st.dt_bias, f32)
-    out = torch.empty(B, T, H, P, dtype=f32, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    Lb = rs.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    d = desc.c()
-    if baseline:
-        snaps = torch.empty(B, T, H, P, N, dtype=f32, device=dev)
-        snaps[:, 0] = t(st.ckpt, f32)
-        slots = [torch.from_numpy((keeps[(r - 1) % pool_n] - 1).astype(np.int32)).to(dev) for r in range(pool_n)]
-        slots[0] = torch.zeros(B, dtype=torch.int32, device=dev)
-
-        def launch(r):
-            p = pool[r % pool_n]
-            _check(Lb.replayssm_mamba2_spec_baseline(ctypes.byref(d), snaps.data_ptr(), slots[r % pool_n].data_ptr(),
-                                                     T, *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
-                                                     bias.data_ptr(), A.data_ptr(), D.data_ptr(), out.data_ptr(),
-                                                     stream), "spec_baseline")
-        keep_state = [snaps]
-    else:
-        state = rs.Mamba2State.allocate(desc, lowp=lowp, ckpt=t(st.ckpt, f32))
-        s_c = state.c()
-        head = torch.zeros(B, dtype=torch.int32, device=dev)
-        com = torch.zeros(B, dtype=torch.int32, device=dev)
-        flushed = torch.zeros(B, dtype=torch.int32, device=dev)
-        if lowp:
-            z0, z1 = torch.zeros_like(head), torch.zeros_like(head)
-            rs.mamba2_flush(desc, state, z0, z1, A, err)
-
-        def launch(r):
-            p = pool[r % pool_n]
-            _check(Lb.replayssm_mamba2_spec_verify(ctypes.byref(d), ctypes.byref(s_c), head.data_ptr(), com.data_ptr(),
-                                                   T, None, *(p[k].data_ptr() for k in ("x", "z", "B", "C", "dt_raw")),
-                                                   bias.data_ptr(), A.data_ptr(), D.data_ptr(), out.data_ptr(),
-                                                   flushed.data_ptr(), err.data_ptr(), stream), "spec_verify")
-            _check(Lb.replayssm_commit(B, L, T, head.data_ptr(), com.data_ptr(), flushed.data_ptr(),
-                                       keep_dev[r % pool_n].data_ptr(), None, err.data_ptr(), stream), "commit")
-        keep_state = [state, s_c]
-    for r in range(warmup):
-        launch(r)
-    secs, wall = Timer(torch).run(launch, warmup, rounds)
-    accepted = sum(int(keeps[r % pool_n].sum()) for r in range(warmup, warmup + rounds))
-    # host model of the cursors (integer rules of the commit call) for the byte count
-    hd = np.zeros(B, np.int64)
-    cm = np.zeros(B, np.int64)
-    nbytes = 0
-    n_flush = 0
-    for r in range(warmup + rounds):
-        fl = cm + T > L
-        if r >= warmup:
-            nbytes += spec_baseline_bytes(B, H, P, N, G, io, T) if baseline else \
-                spec_round_bytes(H, P, N, G, L, io, T, cm, lowp)
-            n_flush += int(fl.sum())
-        hd = np.where(fl, (hd + cm) % L, hd)
-        cm = np.where(fl, 0, cm) + keeps[r % pool_n]
-    if not baseline:
-        if not (np.array_equal(head.cpu().numpy(), hd.astype(np.int32)) and
-                np.array_equal(com.cpu().numpy(), cm.astype(np.int32))):
-            raise RuntimeError("speculative cursors disagree with the host model")
-        if err.item() != 0:
-            raise RuntimeError("device error flag set")
-    del keep_state
-    return dict(accepted_tokens_per_s=accepted / secs, positions_per_s=B * T * rounds / secs,
-                ms_per_round=secs * 1e3 / rounds, rounds=rounds, bytes_per_round_MiB=nbytes / rounds / MiB,
-                hbm_gbps=nbytes / secs / 1e9, frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS,
-                accepted_per_round=accepted / rounds / B,
-                flush_fraction=(n_flush / (B * rounds)) if not baseline else None)
-
-
-def time_gdn(torch, rs, synth, steps, warmup, conventional=False):
-    import ctypes
-    import numpy as np
-    w = synth.WORKLOADS["gdn_hv32"]
-    B, HV, HK, dk, dv, L = w["batch"], w["num_v_heads"], w["num_k_heads"], w["dk"], w["dv"], w["buffer_len"]
-    gen = synth.gdn_inputs("gdn_hv32")
-    st = gen.static
-    dev = "cuda"
-    t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
-    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
-    pool = []
-    for _ in range(32):
-        s = gen.step()
-        pool.append({"q": t(s["q"], torch.bfloat16), "k": t(s["k"], torch.bfloat16), "v": t(s["v"], torch.bfloat16),
-                     "alpha": t(s["alpha"], torch.float32), "beta": t(s["beta"], torch.float32)})
-    out = torch.empty(B, HV, dv, dtype=torch.float32, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    Lb = rs.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    d = desc.c()
-    keys = ("q", "k", "v", "alpha", "beta")
-    if conventional:
-        S = t(st.ckpt, torch.float32)
-
-        def launch(i):
-            p = pool[i % 32]
-            _check(Lb.replayssm_gdn_conventional_decode(ctypes.byref(d), S.data_ptr(), *(p[k].data_ptr() for k in keys),
-                                                        out.data_ptr(), stream), "gdn_conventional")
-        keep = [S]
-    else:
-        state = rs.GdnState.allocate(desc, ckpt=t(st.ckpt, torch.float32))
-        s_c = state.c()
-        cur = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
-
-        def launch(i):
-            p = pool[i % 32]
-            _check(Lb.replayssm_gdn_decode(ctypes.byref(d), ctypes.byref(s_c), cur[i % 2].data_ptr(),
-                                           cur[1 - i % 2].data_ptr(), *(p[k].data_ptr() for k in keys),
-                                           out.data_ptr(), err.data_ptr(), stream), "gdn_decode")
-        keep = [state, s_c, cur]
-    for i in range(warmup):
-        launch(i)
-    secs, wall = Timer(torch).run(launch, warmup, steps)
-    if conventional:
-        nbytes = steps * gdn_conventional_bytes(B, HV, HK, dk, dv, 2)
-    else:
-        nbytes = sum(gdn_replay_bytes(B, HV, HK, dk, dv, L, 2, i % L) for i in range(warmup, warmup + steps))
-        if err.item() != 0:
-            raise RuntimeError("device error flag set")
-    del keep
-    return dict(seq_tokens_per_s=B * steps / secs, ms_per_step=secs * 1e3 / steps, steps=steps,
-                bytes_per_step_MiB=nbytes / steps / MiB, hbm_gbps=nbytes / secs / 1e9,
-                frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS)
-
-
-def time_gdn_spec(torch, rs, synth, rounds, warmup, baseline=False):
-    import ctypes
-    import numpy as np
-    w = synth.WORKLOADS["gdn_spec_hv32"]
-    B, HV, HK, dk, dv, L, T = (w[k] for k in ("batch", "num_v_heads", "num_k_heads", "dk", "dv", "buffer_len",
-                                               "n_pos"))
-    io = 2
-    gen = synth.gdn_inputs("gdn_spec_hv32")
-    st = gen.static
-    dev = "cuda"
-    t = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)  # noqa: E731
-    desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
-    pool_n = 32
-    pool, keeps = [], []
-    for _ in range(pool_n):
-        s = gen.step(n_pos=T)
-        pool.append({"q": t(s["q"], torch.bfloat16), "k": t(s["k"], torch.bfloat16), "v": t(s["v"], torch.bfloat16),
-                     "alpha": t(s["alpha"], torch.float32), "beta": t(s["beta"], torch.float32)})
-        keeps.append(gen.accepted(T - 1) + 1)
-    keep_dev = [torch.from_numpy(k.astype(np.int32)).to(dev) for k in keeps]
-    keys = ("q", "k", "v", "alpha", "beta")
-    out = torch.empty(B, T, HV, dv, dtype=torch.float32, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    Lb = rs.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    d = desc.c()
-    if baseline:
-        snaps = torch.empty(B, T, HV, dv, dk, dtype=torch.float32, device=dev)
-        snaps[:, 0] = t(st.ckpt, torch.float32)
-        slots = [torch.from_numpy((keeps[(r - 1) % pool_n] - 1).astype(np.int32)).to(dev) for r in range(pool_n)]
-        slots[0] = torch.zeros(B, dtype=torch.int32, device=dev)
-
-        def launch(r):
-            p = pool[r % pool_n]
-            _check(Lb.replayssm_gdn_spec_baseline(ctypes.byref(d), snaps.data_ptr(), slots[r % pool_n].data_ptr(), T,
-                                                  *(p[k].data_ptr() for k in keys), out.data_ptr(), stream),
-                   "gdn_spec_baseline")
-        keep_state = [snaps]
-    else:
-        state = rs.GdnState.allocate(desc, ckpt=t(st.ckpt, torch.float32))
-        s_c = state.c()
-        head = torch.zeros(B, dtype=torch.int32, device=dev)
-        com = torch.zeros(B, dtype=torch.int32, device=dev)
-        flushed = torch.zeros(B, dtype=torch.int32, device=dev)
-
-        def launch(r):
-            p = pool[r % pool_n]
-            _check(Lb.replayssm_gdn_spec_verify(ctypes.byref(d), ctypes.byref(s_c), head.data_ptr(), com.data_ptr(), T,
-                                                None, *(p[k].data_ptr() for k in keys), out.data_ptr(), flushed.data_ptr(),
-                                                err.data_ptr(), stream), "gdn_spec_verify")
-            _check(Lb.replayssm_commit(B, L, T, head.data_ptr(), com.data_ptr(), flushed.data_ptr(),
-                                       keep_dev[r % pool_n].data_ptr(), None, err.data_ptr(), stream), "commit")
-        keep_state = [state, s_c]
-    for r in range(warmup):
-        launch(r)
-    secs, wall = Timer(torch).run(launch, warmup, rounds)
-    accepted = sum(int(keeps[r % pool_n].sum()) for r in range(warmup, warmup + rounds))
-    hd = np.zeros(B, np.int64)
-    cm = np.zeros(B, np.int64)
-    nbytes = 0
-    n_flush = 0
-    for r in range(warmup + rounds):
-        fl = cm + T > L
-        if r >= warmup:
-            nbytes += gdn_spec_baseline_bytes(B, HV, HK, dk, dv, io, T) if baseline else \
-                gdn_spec_round_bytes(HV, HK, dk, dv, L, io, T, cm)
-            n_flush += int(fl.sum())
-        hd = np.where(fl, (hd + cm) % L, hd)
-        cm = np.where(fl, 0, cm) + keeps[r % pool_n]
-    if not baseline:
-        if not (np.array_equal(head.cpu().numpy(), hd.astype(np.int32)) and
-                np.array_equal(com.cpu().numpy(), cm.astype(np.int32))):
-            raise RuntimeError("speculative cursors disagree with the host model")
-        if err.item() != 0:
-            raise RuntimeError("device error flag set")
-    del keep_state
-    return dict(accepted_tokens_per_s=accepted / secs, positions_per_s=B * T * rounds / secs,
-                ms_per_round=secs * 1e3 / rounds, rounds=rounds, bytes_per_round_MiB=nbytes / rounds / MiB,
-                hbm_gbps=nbytes / secs / 1e9, frac_of_peak=nbytes / secs / 1e9 / PEAK_GBPS,
-                accepted_per_round=accepted / rounds / B,
-                flush_fraction=(n_flush / (B * rounds)) if not baseline else None)
+    done = warm + Wn
+    n = nrep * Wn
+    regions = []
+    for _ in range(repeats):
+        secs = timed_region(torch, lambda _i: g.replay(), 0, nrep)
+        regions.append(dict(seconds=secs, bytes=sum(r.bytes_of(i) for i in range(n)), tokens=r.B * n,
+                            flushes=n // r.L))
+        done += n
+    r.check(done)
+    res = summarize(regions, n)
+    res.update(unit=r.unit, workload=HEADLINE, launches_per_graph=Wn, kernel=f"rssm::{r.tag}")
+    del g, r
+    torch.cuda.empty_cache()
+    return res
 
 
 SWEEP_WINDOWS = ((0, 16), (16, 64), (64, 256), (256, 1024))
@@ -682,12 +788,14 @@ def precision_sweep(torch, rs, synth, batch=32):
 
 PROBE_LIB = os.path.join(ROOT, "hybrid_model_ssm_amd", "libreplayssm_probes.so")
 # (name, mode, rows per thread, tiles per workgroup, non-temporal loads, non-temporal stores,
-# in place): mode 0 reads, mode 1 reads and writes
-PROBES = [(f"read_{'nt' if ntl else 'plain'}_r{r}_tpw{t}", 0, r, t, ntl, 0, False)
+# in place, skewed tile order): mode 0 reads, mode 1 reads and writes
+PROBES = [(f"read_{'nt' if ntl else 'plain'}_r{r}_tpw{t}", 0, r, t, ntl, 0, False, False)
           for r in (1, 2, 8) for t in (1, 4, 16) for ntl in (0, 1)]
 PROBES += [(f"{'inplace' if ip else 'copy'}_{'nt' if ntl else 'plain'}_{'nt' if nts else 'plain'}_r{r}_tpw{t}",
-            1, r, t, ntl, nts, ip)
+            1, r, t, ntl, nts, ip, False)
            for ip in (True, False) for r in (1, 2, 8) for t in (1, 4, 16) for ntl in (0, 1) for nts in (0, 1)]
+PROBES += [(f"{kind}_nt_nt_r{r}_tpw{t}_skew", 0 if kind == "read" else 1, r, t, 1, 1, kind == "inplace", True)
+           for kind in ("read", "inplace", "copy") for r in (1, 2, 8) for t in (4, 16)]
 
 
 def probe_lib():
@@ -700,7 +808,7 @@ def probe_lib():
     lib.replayssm_probe_stream.restype = ctypes.c_int
     lib.replayssm_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                           ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
     return lib
 
 
@@ -740,12 +848,12 @@ def ceiling(torch, reps=20, repeats=3):
         return _median(secs)
 
     probes = {}
-    for name, mode, rpt, tpw, ntl, nts, inplace in PROBES:
+    for name, mode, rpt, tpw, ntl, nts, inplace, skew in PROBES:
         dst = a if inplace else b
 
         def launch():
             st = lib.replayssm_probe_stream(a.data_ptr(), dst.data_ptr(), sink.data_ptr(), n, rpt, tpw, mode,
-                                            ntl, nts, 1.0, stream)
+                                            ntl, nts, int(skew), 1.0, stream)
             if st:
                 raise RuntimeError(f"probe {name} failed with status {st}")
         secs = timed(launch)
@@ -765,78 +873,179 @@ def ceiling(torch, reps=20, repeats=3):
                      "rw GB/s counts read + written bytes; median of 3 timed regions of 20 launches")
 
 
+
+
 # ------------------------------------------------------------------------------------
 # CPU oracle leg
 # ------------------------------------------------------------------------------------
 
-_ORACLE_JOB = None   # (static, step inputs, L, G): set before the pool forks, read by the workers
+_ORACLE_JOB = None   # (kind, static, step inputs, params): set before the pool forks, read by the workers
+
+# (workload, form, share of the sample's sequences): the oracle's replay form (O-2, O-5)
+# and its conventional recurrence (O-1, O-4); the first is the baseline line's value, the
+# others run on a quarter of its sequences to keep the leg short
+ORACLE_JOBS = [(HEADLINE, "replay", 1.0), (HEADLINE, "conventional", 0.25), ("mamba2_h64", "replay", 0.25),
+               ("mamba2_h64", "conventional", 0.25), ("gdn_hv32", "replay", 0.25), ("gdn_hv32", "conventional", 0.25)]
 
 
 def _oracle_shard(span):
-    """One worker's share of the CPU baseline: the oracle's replay form on sequences
-    [b0, b1) of the sample, every step; returns its outputs and its compute time."""
-    import numpy as np
-    from oracle import mamba2 as om  # the oracle is test infrastructure; used only here
+    """One worker's share of a CPU-baseline job: the oracle on sequences [b0, b1) of the
+    sample, every step; returns its outputs and its compute time."""
+    from threadpoolctl import threadpool_limits   # the oracle (test infrastructure) is used only here
     b0, b1 = span
-    st, steps_in, L, G = _ORACLE_JOB
-    rep = om.Mamba2Replay(st.ckpt[b0:b1], L, st.A, st.D, st.dt_bias, G)
+    kind, form, st, steps_in, prm = _ORACLE_JOB
+    sl = lambda s: {k: v[b0:b1] for k, v in s.items()}  # noqa: E731
+    # one BLAS thread per worker: the workers already use every core
+    with threadpool_limits(limits=1):
+        return _oracle_shard_run(b0, b1, kind, form, st, steps_in, prm, sl)
+
+
+def _oracle_shard_run(b0, b1, kind, form, st, steps_in, prm, sl):
+    import numpy as np
+    from oracle import gdn as og
+    from oracle import mamba2 as om
     t0 = time.perf_counter()
-    outs = [rep.step(**{k: v[b0:b1] for k, v in s.items()})[0] for s in steps_in]
+    outs = []
+    if kind == "mamba2" and form == "replay":
+        rep = om.Mamba2Replay(st.ckpt[b0:b1], prm["L"], st.A, st.D, st.dt_bias, prm["G"])
+        outs = [rep.step(**sl(s))[0] for s in steps_in]
+    elif kind == "mamba2":
+        h = st.ckpt[b0:b1].astype(np.float64)
+        for s in steps_in:
+            h, o = om.conventional_step(h, **sl(s), dt_bias=st.dt_bias, A=st.A, D=st.D)
+            outs.append(o)
+    elif form == "replay":
+        rep = og.GDNReplay(st.ckpt[b0:b1], prm["L"], prm["HK"])
+        outs = [rep.step(**sl(s))[0] for s in steps_in]
+    else:
+        S = st.ckpt[b0:b1].astype(np.float64)
+        for s in steps_in:
+            S, o = og.conventional_step(S, **sl(s))
+            outs.append(o)
     return b0, time.perf_counter() - t0, np.stack(outs)
 
 
 def cpu_oracle_run(synth, nseq, steps):
-    """Time the fp64 oracle (replay form) on ``nseq`` sequences of the headline workload for
-    ``steps`` steps, the sequences sharded over a pool of worker processes (one per host
-    core this process may use, at most 16).  Must run before this process touches the GPU:
-    the workers are forked from it.  The inputs are the ones the GPU run draws (the same
-    seeded generator, the same order)."""
+    """Time the fp64 oracle on ``nseq`` sequences (times the job's share) of each
+    ORACLE_JOBS workload for ``steps`` steps, the sequences sharded over a pool of worker processes (one per host core this
+    process may use, at most 16).  Must run before this process touches the GPU: the
+    workers are forked from it.  The inputs are the ones the GPU runs draw (the same
+    seeded generators, the same order).  Returns one result per job; the first holds the
+    outputs for the GPU check."""
     global _ORACLE_JOB
     import multiprocessing
     import numpy as np
-    gen = synth.mamba2_inputs(HEADLINE)
-    st = gen.static
-    steps_in = [gen.step() for _ in range(steps)]
-    w = synth.WORKLOADS[HEADLINE]
-    _ORACLE_JOB = (st, steps_in, w["buffer_len"], w["ngroups"])
-    workers = max(1, min(16, len(os.sched_getaffinity(0)), nseq))
-    cuts = [round(i * nseq / workers) for i in range(workers + 1)]
-    spans = [(cuts[i], cuts[i + 1]) for i in range(workers) if cuts[i + 1] > cuts[i]]
-    with multiprocessing.get_context("fork").Pool(len(spans)) as pool:
-        t0 = time.perf_counter()
-        res = pool.map(_oracle_shard, spans)
-        wall = time.perf_counter() - t0
-    _ORACLE_JOB = None
-    res.sort(key=lambda r: r[0])
-    outs = np.concatenate([r[2] for r in res], axis=1)   # [steps, nseq, H, P]
-    return dict(nseq=nseq, steps=steps, workers=len(spans), wall=wall,
-                worker_seconds=max(r[1] for r in res), outs=outs)
+    results = []
+    inputs = {}
+    for name, form, share in ORACLE_JOBS:
+        n = max(1, int(round(nseq * share)))
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), n))
+        cuts = [round(i * n / workers) for i in range(workers + 1)]
+        spans = [(cuts[i], cuts[i + 1]) for i in range(workers) if cuts[i + 1] > cuts[i]]
+        w = synth.WORKLOADS[name]
+        kind = "gdn" if w["kind"] == "gdn" else "mamba2"
+        if name not in inputs:
+            gen = synth.gdn_inputs(name) if kind == "gdn" else synth.mamba2_inputs(name)
+            inputs[name] = (gen.static, [gen.step() for _ in range(steps)])
+        st, steps_in = inputs[name]
+        if nseq > w["batch"]:
+            raise ValueError("--cpu-seqs exceeds the batch")
+        prm = dict(L=w["buffer_len"], G=w.get("ngroups"), HK=w.get("num_k_heads"))
+        _ORACLE_JOB = (kind, form, st, steps_in, prm)
+        with multiprocessing.get_context("fork").Pool(len(spans)) as pool:
+            t0 = time.perf_counter()
+            res = pool.map(_oracle_shard, spans)
+            wall = time.perf_counter() - t0
+        _ORACLE_JOB = None
+        res.sort(key=lambda x: x[0])
+        out = dict(workload=name, form=form, nseq=n, steps=steps, workers=len(spans), wall=wall,
+                   worker_seconds=max(x[1] for x in res), value=n * steps / wall)
+        if not results:
+            out["outs"] = np.concatenate([x[2] for x in res], axis=1)   # [steps, nseq, H, P]
+        results.append(out)
+    return results
 
 
-def cpu_baseline(torch, rs, synth, run):
-    """The CPU baseline line from an oracle run (``cpu_oracle_run``), and the check of the
-    GPU's outputs for the same sequences and inputs against it."""
+def cpu_baseline(torch, rs, synth, runs):
+    """The CPU baseline line from the oracle runs (``cpu_oracle_run``), and the check of the
+    GPU's outputs for the first run's sequences and inputs against it."""
     import numpy as np
+    run = runs[0]
     nseq, steps = run["nseq"], run["steps"]
-    b = Mamba2Bench(torch, rs, synth, HEADLINE, pool=max(steps, 1))
+    r = Mamba2Runner(torch, rs, synth, HEADLINE, pool=max(steps, 1))
     worst = 0.0
     for i in range(steps):
-        b.launch(i)
-        g = b.out[:nseq].cpu().numpy()
+        r.launch(i)
+        g = r.out[:nseq].cpu().numpy()
         o = run["outs"][i]
         worst = max(worst, float(np.max(np.abs(g - o) / (1e-4 * (1 + np.abs(o))))))
+    r.check(steps)
+    del r
+    torch.cuda.empty_cache()
     secs = run["wall"]
-    return dict(value=nseq * steps / secs, unit="seq-tokens/s", cores=run["workers"], kind="oracle",
-                sample=f"{nseq} of {b.B} sequences x {steps} decode steps ({steps // b.L} L={b.L} windows with "
-                       f"their flushes) of the {HEADLINE} workload, NumPy float64 replay form, sequences "
-                       f"sharded over {run['workers']} worker processes (wall time of the pool)",
+    return dict(value=run["value"], unit="seq-tokens/s", cores=run["workers"], kind="oracle",
+                sample=f"{nseq} of 256 sequences x {steps} decode steps ({steps // 16} L=16 windows with their "
+                       f"flushes) of the {HEADLINE} workload, NumPy float64 replay form, sequences sharded over "
+                       f"{run['workers']} worker processes (wall time of the pool)",
                 seconds=secs, worker_seconds_max=run["worker_seconds"],
-                gpu_parity_max_violation=worst, gpu_parity_ok=worst <= 1.0)
+                gpu_parity_max_violation=worst, gpu_parity_ok=worst <= 1.0,
+                runs=[{k: v for k, v in x.items() if k != "outs"} for x in runs])
 
 
 # ------------------------------------------------------------------------------------
-# rocprofv3 counter summary
+# rocprofv3 summaries
 # ------------------------------------------------------------------------------------
+
+# summary file of each profiled variant (named for the kernel and the workload)
+PMC_FILES = {
+    "headline": "mamba2_replay_decode_h128_pmc.txt",
+    "mamba2_h128_conventional": "mamba2_conventional_h128_pmc.txt",
+    "mamba2_h128_bf16_read": "mamba2_replay_decode_h128_bf16read_pmc.txt",
+    "mamba2_h128_f16_read": "mamba2_replay_decode_h128_f16read_pmc.txt",
+    "mamba2_h128_fp8_read": "mamba2_replay_decode_h128_fp8read_pmc.txt",
+    "mamba2_h128_state_and_output": "mamba2_state_and_output_h128_pmc.txt",
+    "mamba2_h64_replay": "mamba2_replay_decode_h64_pmc.txt",
+    "mamba2_h64_conventional": "mamba2_conventional_h64_pmc.txt",
+    "spec_h128_verify": "mamba2_spec_verify_h128_pmc.txt",
+    "spec_h128_snapshot_baseline": "mamba2_spec_snapshot_baseline_h128_pmc.txt",
+    "gdn_hv32_replay": "gdn_replay_decode_hv32_pmc.txt",
+    "gdn_hv32_conventional": "gdn_conventional_hv32_pmc.txt",
+    "gdn_spec_hv32_verify": "gdn_spec_verify_hv32_pmc.txt",
+    "gdn_spec_hv32_snapshot_baseline": "gdn_spec_snapshot_baseline_hv32_pmc.txt",
+}
+STATS_SUMMARY = os.path.join(ROOT, "profiles", "mamba2_replay_decode_h128_kernel_stats.txt")
+
+
+def make_runner(torch, rs, synth, name):
+    if name == "headline":
+        return Mamba2Runner(torch, rs, synth, HEADLINE)
+    return VARIANTS[name][1](torch, rs, synth)
+
+
+def profile_variant(torch, rs, synth, name, K, W, out_path):
+    """The dispatches a counter run profiles: ``W`` then ``K`` dispatches of one variant
+    (rounded to whole windows for decode), untimed, then the 1 GiB calibration copy.
+    Writes the kernel name, its dispatch count and their average algorithmic bytes."""
+    r = make_runner(torch, rs, synth, name)
+    n = -(-(W + K) // r.period) * r.period
+    for i in range(n):
+        r.launch(i)
+    torch.cuda.synchronize()
+    r.check(n)
+    info = dict(variant=name, kernel=r.tag, sources=r.sources, dispatches=n,
+                algorithmic_bytes_per_dispatch=sum(r.bytes_of(i) for i in range(n)) / n)
+    del r
+    torch.cuda.empty_cache()
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)   # the counter calibration: 1 GiB read + 1 GiB write
+    torch.cuda.synchronize()
+    os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
+    with open(out_path, "w") as f:
+        json.dump(info, f)
+    print(json.dumps(info))
+
 
 def _read_counter_csv(d):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -861,106 +1070,126 @@ def _avg_counter(rows, name_pred, counter):
     return sum(per.values()) / len(per), len(per)
 
 
-def pmc_summarize(fetch_dir, write_dir, command, which="headline", algorithmic=None):
-    """Summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) for the kernel
-    COUNTED[which], scaled by what the same counters read for the 1 GiB calibration copy;
-    ``algorithmic``: the byte model's average bytes per dispatch, for the ratio."""
-    spec = COUNTED[which]
-    out_path = spec["summary"]
+def pmc_summarize(fetch_dir, write_dir, info_path, command):
+    """Summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of one profiled
+    variant, scaled by what the same counters read for the 1 GiB calibration copy."""
+    info = json.load(open(info_path))
+    name = info["variant"]
+    out_path = os.path.join(ROOT, "profiles", PMC_FILES[name])
     fr, wr = _read_counter_csv(fetch_dir), _read_counter_csv(write_dir)
-    is_replay = lambda n: spec["tag"] in n  # noqa: E731
+    is_kernel = lambda n: info["kernel"] in n  # noqa: E731
     is_copy = lambda n: "MulFunctor" in n  # the calibration kernel: 1 GiB read + 1 GiB write  # noqa: E731
-    f_rep, nf = _avg_counter(fr, is_replay, "FETCH_SIZE")
-    w_rep, nw = _avg_counter(wr, is_replay, "WRITE_SIZE")
-    f_cpy, _ = _avg_counter(fr, is_copy, "FETCH_SIZE")
-    w_cpy, _ = _avg_counter(wr, is_copy, "WRITE_SIZE")
-    if None in (f_rep, w_rep, f_cpy, w_cpy):
-        raise RuntimeError("missing counters for the replay kernel or the calibration copy")
-    f_scale = COPY_BYTES / (f_cpy * 1024.0)
-    w_scale = COPY_BYTES / (w_cpy * 1024.0)
-    traffic = f_rep * 1024.0 * f_scale + w_rep * 1024.0 * w_scale
-    lines = spec["title"] + [
-        f"command: {command}",
-        f"kernel: rssm::{spec['tag']}",
-        f"kernel_source_sha256_16: {kernel_source_hash(spec['sources'])}",
-        f"dispatches: fetch {nf}, write {nw}",
-        f"FETCH_SIZE_KiB_per_dispatch: {f_rep:.1f}",
-        f"WRITE_SIZE_KiB_per_dispatch: {w_rep:.1f}",
-        f"copy_calibration: {COPY_BYTES} B device copy reads FETCH_SIZE {f_cpy:.1f} KiB, WRITE_SIZE {w_cpy:.1f} KiB",
-        f"scale_fetch: {f_scale:.4f}",
-        f"scale_write: {w_scale:.4f}",
-        f"traffic_bytes_per_launch: {traffic:.0f}",
-    ]
-    if algorithmic:
-        lines += [f"algorithmic_bytes_per_launch: {algorithmic:.0f}",
-                  f"traffic_over_algorithmic: {traffic / algorithmic:.4f}"]
+    f_k, nf = _avg_counter(fr, is_kernel, "FETCH_SIZE")
+    w_k, nw = _avg_counter(wr, is_kernel, "WRITE_SIZE")
+    f_c, _ = _avg_counter(fr, is_copy, "FETCH_SIZE")
+    w_c, _ = _avg_counter(wr, is_copy, "WRITE_SIZE")
+    if None in (f_k, w_k, f_c, w_c):
+        raise RuntimeError(f"missing counters for {info['kernel']} or the calibration copy")
+    if nf != info["dispatches"] or nw != info["dispatches"]:
+        raise RuntimeError(f"profiled {nf}/{nw} dispatches of {info['kernel']}, the run made {info['dispatches']}")
+    f_scale = COPY_BYTES / (f_c * 1024.0)
+    w_scale = COPY_BYTES / (w_c * 1024.0)
+    traffic = f_k * 1024.0 * f_scale + w_k * 1024.0 * w_scale
+    alg = info["algorithmic_bytes_per_dispatch"]
+    lines = [f"# rocprofv3 HBM counters: {name} ({VARIANTS[name][2] if name in VARIANTS else HEADLINE})",
+             f"command: {command}",
+             f"kernel: rssm::{info['kernel']}",
+             f"kernel_source_sha256_16: {kernel_source_hash(info['sources'])}",
+             f"dispatches: {nf} (fetch run), {nw} (write run)",
+             f"FETCH_SIZE_KiB_per_dispatch: {f_k:.1f}",
+             f"WRITE_SIZE_KiB_per_dispatch: {w_k:.1f}",
+             f"copy_calibration: {COPY_BYTES} B device copy reads FETCH_SIZE {f_c:.1f} KiB, WRITE_SIZE {w_c:.1f} KiB",
+             f"scale_fetch: {f_scale:.4f}",
+             f"scale_write: {w_scale:.4f}",
+             f"fetch_bytes_per_launch: {f_k * 1024.0 * f_scale:.0f}",
+             f"write_bytes_per_launch: {w_k * 1024.0 * w_scale:.0f}",
+             f"traffic_bytes_per_launch: {traffic:.0f}",
+             f"algorithmic_bytes_per_launch: {alg:.0f}",
+             f"traffic_over_algorithmic: {traffic / alg:.4f}"]
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def stats_summarize(stats_dir, out_path, command, steps=0, warmup=0):
-    """Write the per-kernel summary of a ``rocprofv3 --kernel-trace --stats`` run."""
-    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        raise FileNotFoundError(f"no kernel_stats.csv under {stats_dir}")
-    rows = list(csv.DictReader(open(files[0])))
-    rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
-    lines = ["# rocprofv3 --kernel-trace --stats: kernels of one bench.py run (sorted by total time)",
-             f"command: {command}",
-             f"kernel_source_sha256_16: {kernel_source_hash()}",
-             "calls | avg_us | min_us | max_us | total_ms | kernel"]
-    for r in rows:
-        lines.append("%5d | %8.1f | %8.1f | %8.1f | %8.2f | %s" % (
-            int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
-            float(r["TotalDurationNs"]) / 1e6, r["Name"][:160]))
-    # the headline run is the first warmup+steps dispatches of the replay kernel; the same
-    # kernel instance also serves later workloads of the run, so take them from the trace
-    traces = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
-    if traces and steps:
-        disp = [r for r in csv.DictReader(open(traces[0])) if REPLAY_KERNEL_TAG in r["Kernel_Name"]]
-        disp.sort(key=lambda r: int(r["Start_Timestamp"]))
-        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in disp[:warmup + steps]]
-        timed = dur[warmup:warmup + steps]
-        if timed:
-            lines.append(f"headline kernel: rssm::{REPLAY_KERNEL_TAG}")
-            lines.append(f"headline timed dispatches: {len(timed)} (after {warmup} warmup), "
-                         f"average {sum(timed) / len(timed):.1f} us, min {min(timed):.1f}, max {max(timed):.1f}")
-            # every sequence starts at cursor 0, so dispatch i runs at cursor i mod L and the
-            # dispatch at cursor L-1 is the flush step; split the time by the kind of step
-            from hybrid_model_ssm_amd import synth
-            w = synth.WORKLOADS[HEADLINE]
-            L = w["buffer_len"]
-            shape = (w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"], L, 2)
-            for name, cs in (("non-flush", range(L - 1)), ("flush", [L - 1])):
-                d = [t for i, t in enumerate(dur[:warmup + steps]) if i >= warmup and i % L in cs]
-                nbytes = sum(mamba2_replay_bytes(*shape, c) for c in cs) / len(cs)
-                if d:
-                    avg = sum(d) / len(d)
-                    lines.append(f"headline {name} steps (cursor {cs[0]}..{cs[-1]}): {len(d)} dispatches, "
-                                 f"average {avg:.1f} us, min {min(d):.1f}, max {max(d):.1f}; "
-                                 f"{nbytes / 1e6:.1f} MB algorithmic -> {nbytes / avg / 1e3:.0f} GB/s")
-    os.makedirs(os.path.dirname(out_path), exist_ok=True)
-    with open(out_path, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines[:12]))
-
-
-def committed_traffic(which="headline"):
-    """Counter-measured bytes per launch from the committed summary, if it matches the source."""
-    spec = COUNTED[which]
-    path = spec["summary"]
-    if not os.path.exists(path):
-        return None, "no counter summary committed"
+def _summary_kv(path):
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash(spec["sources"]):
-        return None, "kernel source changed since the counters were taken"
-    return float(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    return kv
+
+
+def committed_traffic(name):
+    """Counter-measured bytes per launch of a variant from its committed summary, if the
+    summary matches the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", PMC_FILES[name])
+    if not os.path.exists(path):
+        return None
+    kv = _summary_kv(path)
+    sources = MAMBA2_SOURCES if "mamba2" in kv.get("kernel", "") else GDN_SOURCES
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources):
+        return None
+    return dict(traffic=float(kv["traffic_bytes_per_launch"]), ratio=float(kv["traffic_over_algorithmic"]),
+                fetch=float(kv["fetch_bytes_per_launch"]), write=float(kv["write_bytes_per_launch"]),
+                source=os.path.relpath(path, ROOT))
+
+
+def committed_traffic_reason(name):
+    path = os.path.join(ROOT, "profiles", PMC_FILES[name])
+    if not os.path.exists(path):
+        return "no counter summary committed"
+    return "kernel source changed since the counters were taken"
+
+
+def stats_summarize(stats_dir, out_path, command, bench_json):
+    """Write the per-kernel summary of a ``rocprofv3 --kernel-trace --stats`` run of the
+    default bench command, with the headline kernel's dispatches split into flush and
+    non-flush steps (the headline runner's dispatches come first and step the cursor by
+    one each, from 0)."""
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_stats.csv under {stats_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
+    tag = REPLAY_KERNEL_TAG
+    lines = ["# rocprofv3 --kernel-trace --stats: kernels of one bench.py run (sorted by total time)",
+             f"command: {command}",
+             f"kernel_source_sha256_16: {kernel_source_hash(MAMBA2_SOURCES)}",
+             "calls | avg_us | min_us | max_us | total_ms | kernel"]
+    for r in rows:
+        lines.append("%5d | %8.1f | %8.1f | %8.1f | %8.2f | %s" % (
+            int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e6, r["Name"][:160]))
+    traces = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    hd = line["headline_dispatches"]
+    if traces:
+        disp = [r for r in csv.DictReader(open(traces[0])) if tag in r["Kernel_Name"]]
+        disp.sort(key=lambda r: int(r["Start_Timestamp"]))
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in disp[:hd["total"]]]
+        timed = [d for i, d in enumerate(dur) if any(f <= i < f + line["steps"] for f in hd["timed_firsts"])]
+        lines.append(f"headline kernel: rssm::{tag}")
+        lines.append(f"headline timed dispatches: {len(timed)} ({len(hd['timed_firsts'])} regions of "
+                     f"{line['steps']}), average {sum(timed) / len(timed):.1f} us, min {min(timed):.1f}, "
+                     f"max {max(timed):.1f}; bench median region average {line['roofline']['avg_launch_us']:.1f} us")
+        from hybrid_model_ssm_amd import synth
+        w = synth.WORKLOADS[HEADLINE]
+        L = w["buffer_len"]
+        shape = (w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"], L, 2)
+        for nm, cs in (("non-flush", range(L - 1)), ("flush", [L - 1])):
+            d = [t for i, t in enumerate(dur) if i % L in cs]
+            nbytes = sum(mamba2_replay_bytes(*shape, c) for c in cs) / len(cs)
+            if d:
+                avg = sum(d) / len(d)
+                lines.append(f"headline {nm} steps (cursor {cs[0]}..{cs[-1]}): {len(d)} dispatches, "
+                             f"average {avg:.1f} us, min {min(d):.1f}, max {max(d):.1f}; "
+                             f"{nbytes / 1e6:.1f} MB algorithmic -> {nbytes / avg / 1e3:.0f} GB/s")
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:14]))
 
 
 # ------------------------------------------------------------------------------------
@@ -968,46 +1197,46 @@ def committed_traffic(which="headline"):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1024, help="timed decode steps of the headline")
+    ap.add_argument("--steps", type=int, default=1024, help="decode steps per timed region of the headline")
     ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--repeats", type=int, default=5, help="timed regions per measurement (median reported)")
     ap.add_argument("--only", default="all",
-                    help="all, headline, or a comma list of: conventional,graph,bf16,f16,fp8,so,h64,spec,gdn,"
-                         "gdn_spec")
+                    help="all, headline, or a comma list of: " + ",".join(GROUPS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=256)
     ap.add_argument("--cpu-steps", type=int, default=32)
-    ap.add_argument("--calibrate-copy", action="store_true")
-    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--profile-variant", metavar="NAME", choices=["headline"] + sorted(VARIANTS),
+                    help="run W+K dispatches of one variant untimed and the calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--profile-out", default=os.path.join("gpurun_out", "profile_variant.json"))
+    ap.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROFILE_JSON"))
     ap.add_argument("--pmc-command", default="")
-    ap.add_argument("--pmc-kernel", default="headline", choices=sorted(COUNTED),
-                    help="kernel whose counters --pmc-summarize reads")
-    ap.add_argument("--stats-summarize", metavar="STATS_DIR")
+    ap.add_argument("--stats-summarize", nargs=2, metavar=("STATS_DIR", "BENCH_JSON"))
     ap.add_argument("--precision-sweep", action="store_true",
                     help="print the emulated read/recurrence precision sweep (one JSON line) and exit")
     args = ap.parse_args(argv)
 
     if args.stats_summarize:
-        stats_summarize(args.stats_summarize, STATS_SUMMARY, args.pmc_command, args.steps, args.warmup)
+        stats_summarize(args.stats_summarize[0], STATS_SUMMARY, args.pmc_command, args.stats_summarize[1])
         return 0
     if args.pmc_summarize:
-        pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], args.pmc_command, args.pmc_kernel,
-                      algorithmic=gdn_window_bytes() if args.pmc_kernel == "gdn" else None)
+        pmc_summarize(*args.pmc_summarize, args.pmc_command)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the decode path has no cross-GPU exchange); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < 0:
-        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.repeats < 1:
+        print("--steps and --repeats must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
 
     # the CPU oracle's worker pool is forked before this process touches the GPU
-    oracle_run = None
-    if not args.no_cpu_baseline and not args.precision_sweep:
+    oracle_runs = None
+    if not args.no_cpu_baseline and not args.precision_sweep and not args.profile_variant:
         from hybrid_model_ssm_amd import synth as synth_cpu
-        oracle_run = cpu_oracle_run(synth_cpu, args.cpu_seqs, args.cpu_steps)
-        print(f"[bench] cpu oracle: {args.cpu_seqs} sequences x {args.cpu_steps} steps on "
-              f"{oracle_run['workers']} worker processes in {oracle_run['wall']:.1f} s", file=sys.stderr, flush=True)
+        oracle_runs = cpu_oracle_run(synth_cpu, args.cpu_seqs, args.cpu_steps)
+        for x in oracle_runs:
+            print(f"[bench] cpu oracle {x['workload']} {x['form']}: {x['nseq']} sequences x {x['steps']} steps on "
+                  f"{x['workers']} worker processes in {x['wall']:.1f} s", file=sys.stderr, flush=True)
 
     import torch
     from hybrid_model_ssm_amd import replayssm as rs
@@ -1020,92 +1249,87 @@ def main(argv=None):
     if args.precision_sweep:
         print(json.dumps({"precision_sweep": precision_sweep(torch, rs, synth)}), flush=True)
         return 0
+    if args.profile_variant:
+        profile_variant(torch, rs, synth, args.profile_variant, args.steps, args.warmup, args.profile_out)
+        return 0
 
-    head, hb = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup)
-    print(f"[bench] headline {head['seq_tokens_per_s']:.4g} seq-tok/s, {head['hbm_gbps']:.0f} GB/s",
-          file=sys.stderr, flush=True)
-    del hb
+    # ---- headline: every timed region starts at a flush step, so a region of K steps holds
+    # ceil(K / L) flushes (K a multiple of L: exactly K / L, the true rate) --------------------
+    hr = Mamba2Runner(torch, rs, synth, HEADLINE)
+    L = hr.L
+    regions, setup, done = measure(torch, hr, args.warmup, args.steps, args.repeats, start_at=L - 1)
+    head = summarize(regions, args.steps)
+    while done % L:                       # the per-step split covers two whole windows
+        hr.launch(done)
+        done += 1
+    split, done = per_step_split(torch, hr, done, 2 * L)
+    hr.check(done)
+    head_dispatches = dict(total=done, setup=setup, timed_firsts=[g["first"] for g in regions])
+    del hr
     torch.cuda.empty_cache()
-    launches = args.steps
-    nbytes_per_launch = head["bytes_per_step_MiB"] * MiB
-    avg_s = head["seconds"] / launches
-    traffic, traffic_src = committed_traffic()
+    print(f"[bench] headline {head['value']:.4g} seq-tok/s, {head['hbm_gbps']:.0f} GB/s "
+          f"(flush steps {split['flush_us']:.1f} us, others {split['nonflush_us']:.1f} us)",
+          file=sys.stderr, flush=True)
+    avg_s = head["ms_per_dispatch"] / 1e3
+    nbytes_per_launch = head["bytes_per_dispatch_MiB"] * MiB
+    tr = committed_traffic("headline")
     roofline = dict(bound="hbm", achieved=nbytes_per_launch / avg_s / 1e9, peak=PEAK_GBPS, unit="GB/s",
-                    frac=nbytes_per_launch / avg_s / 1e9 / PEAK_GBPS, traffic=traffic,
+                    frac=nbytes_per_launch / avg_s / 1e9 / PEAK_GBPS, traffic=tr["traffic"] if tr else None,
                     traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                    traffic_source=traffic_src,
+                    traffic_over_algorithmic=tr["ratio"] if tr else None,
+                    traffic_source=tr["source"] if tr else committed_traffic_reason("headline"),
                     kernel=f"rssm::{REPLAY_KERNEL_TAG}", algorithmic_bytes_per_launch=nbytes_per_launch,
-                    avg_launch_us=avg_s * 1e6, launches=launches)
+                    avg_launch_us=avg_s * 1e6, launches=args.steps)
 
+    groups = set(GROUPS) if args.only == "all" else set() if args.only == "headline" else set(args.only.split(","))
+    unknown = groups - set(GROUPS)
+    if unknown:
+        print(f"unknown --only groups: {sorted(unknown)}", file=sys.stderr)
+        return 2
     variants = {}
-    conv = None
-    groups = {"conventional", "graph", "bf16", "f16", "fp8", "so", "h64", "spec", "gdn", "gdn_spec"} \
-        if args.only == "all" else \
-        set() if args.only == "headline" else set(args.only.split(","))
-    if "conventional" in groups:
-        conv, _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup, conventional=True)
-        torch.cuda.empty_cache()
-        variants["mamba2_h128_conventional"] = conv
+    for name, (group, _, _, _) in VARIANTS.items():
+        if group in groups:
+            variants[name] = time_variant(torch, rs, synth, name, args.steps, args.warmup, args.repeats)
+            print(f"[bench] {name}: {variants[name]['value']:.4g} {variants[name]['unit']}, "
+                  f"{variants[name]['hbm_gbps']:.0f} GB/s", file=sys.stderr, flush=True)
     if "graph" in groups:
-        variants["mamba2_h128_replay_graph"] = time_mamba2_graph(torch, rs, synth, HEADLINE, args.steps, args.warmup)
-        torch.cuda.empty_cache()
-    if "bf16" in groups:
-        variants["mamba2_h128_bf16_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps, args.warmup,
-                                                           lowp=True)
-        torch.cuda.empty_cache()
-    for kind in ("f16", "fp8"):
-        if kind in groups:
-            variants[f"mamba2_h128_{kind}_read"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps,
-                                                                  args.warmup, lowp=kind)
-            torch.cuda.empty_cache()
-    if "so" in groups:
-        variants["mamba2_h128_state_and_output"], _ = time_mamba2(torch, rs, synth, HEADLINE, args.steps,
-                                                                  args.warmup, state_and_output=True)
-        torch.cuda.empty_cache()
-    if "h64" in groups:
-        variants["mamba2_h64_replay"], _ = time_mamba2(torch, rs, synth, "mamba2_h64", 256, 32)
-        torch.cuda.empty_cache()
-        variants["mamba2_h64_conventional"], _ = time_mamba2(torch, rs, synth, "mamba2_h64", 256, 32,
-                                                             conventional=True)
-        torch.cuda.empty_cache()
-    if "spec" in groups:
-        variants["spec_h128_verify"] = time_spec(torch, rs, synth, 256, 32)
-        torch.cuda.empty_cache()
-        variants["spec_h128_snapshot_baseline"] = time_spec(torch, rs, synth, 256, 32, baseline=True)
-        torch.cuda.empty_cache()
-    if "gdn" in groups:
-        variants["gdn_hv32_replay"] = time_gdn(torch, rs, synth, 512, 32)
-        tr, src = committed_traffic("gdn")
-        variants["gdn_hv32_replay"].update(traffic_bytes_per_launch=tr, traffic_source=src,
-                                           algorithmic_bytes_per_launch=gdn_window_bytes())
-        torch.cuda.empty_cache()
-        variants["gdn_hv32_conventional"] = time_gdn(torch, rs, synth, 512, 32, conventional=True)
-        torch.cuda.empty_cache()
-    if "gdn_spec" in groups:
-        variants["gdn_spec_hv32_verify"] = time_gdn_spec(torch, rs, synth, 256, 32)
-        torch.cuda.empty_cache()
-        variants["gdn_spec_hv32_snapshot_baseline"] = time_gdn_spec(torch, rs, synth, 256, 32, baseline=True)
-        torch.cuda.empty_cache()
-    if variants:
-        print("[bench] variants done", file=sys.stderr, flush=True)
-    ceil = ceiling(torch) if (args.only == "all" or args.calibrate_copy) else None
+        variants["mamba2_h128_replay_graph"] = time_graph(torch, rs, synth, args.steps, args.warmup, args.repeats)
+    ceil = ceiling(torch) if args.only == "all" else None
     cpu = None
-    if oracle_run is not None:
-        cpu = cpu_baseline(torch, rs, synth, oracle_run)
+    if oracle_runs is not None:
+        cpu = cpu_baseline(torch, rs, synth, oracle_runs)
         print(f"[bench] cpu baseline {cpu['value']:.4g} seq-tok/s in {cpu['seconds']:.1f}s", file=sys.stderr,
               flush=True)
         if not cpu["gpu_parity_ok"]:
             raise RuntimeError(f"GPU outputs disagree with the oracle: {cpu['gpu_parity_max_violation']}")
 
+    conv = variants.get("mamba2_h128_conventional")
+    ratios = {}
+    pairs = [("mamba2_h128", None, "mamba2_h128_conventional"),
+             ("mamba2_h64", "mamba2_h64_replay", "mamba2_h64_conventional"),
+             ("gdn_hv32", "gdn_hv32_replay", "gdn_hv32_conventional"),
+             ("mamba2_spec_h128", "spec_h128_verify", "spec_h128_snapshot_baseline"),
+             ("gdn_spec_hv32", "gdn_spec_hv32_verify", "gdn_spec_hv32_snapshot_baseline")]
+    for wl, rep_name, conv_name in pairs:
+        rv = head if rep_name is None else variants.get(rep_name)
+        cv = variants.get(conv_name)
+        if rv and cv:
+            ent = dict(speedup=rv["value"] / cv["value"],
+                       algorithmic_bytes_ratio=cv["bytes_per_dispatch_MiB"] / rv["bytes_per_dispatch_MiB"])
+            rt = tr if rep_name is None else committed_traffic(rep_name)
+            ct = committed_traffic(conv_name)
+            if rt and ct:
+                ent["measured_traffic_ratio"] = ct["traffic"] / rt["traffic"]
+            ratios[wl] = ent
     w = synth.WORKLOADS[HEADLINE]
     line = {
         "metric": METRIC,
-        "value": head["seq_tokens_per_s"],
+        "value": head["value"],
         "unit": "seq-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step"],
+        "ms_per_step": head["ms_per_dispatch"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1115,11 +1339,19 @@ def main(argv=None):
                    "dstate": w["dstate"], "ngroups": w["ngroups"], "buffer_len": w["buffer_len"],
                    "io_dtype": w["io"], "checkpoint": "f32", "checkpoint_reads": "f32",
                    "parallelism": "single GPU"},
+        "timing": {"timed_regions": args.repeats, "statistic": "median region",
+                   "values_per_region": head["values_per_region"],
+                   "flush_steps_per_region": head["flush_dispatches_per_region"],
+                   "flush_steps_true_rate": args.steps / L,
+                   "region_start": "a flush step (cursor L-1)", "setup_steps": setup},
+        "step_split": split,
+        "headline_dispatches": head_dispatches,
         "hbm_gbps": head["hbm_gbps"],
         "hbm_frac_of_peak": head["frac_of_peak"],
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "speedup_vs_conventional": (head["seq_tokens_per_s"] / conv["seq_tokens_per_s"]) if conv else None,
+        "speedup_vs_conventional": (head["value"] / conv["value"]) if conv else None,
+        "replay_vs_conventional": ratios,
         "variants": variants,
         "ceiling": ceil,
     }

@@ -14,7 +14,9 @@
 //                         update of the flush and conventional steps, dst != src a copy
 //
 // Loads and stores are plain or non-temporal (the decode kernels stream the checkpoint
-// with non-temporal accesses).
+// with non-temporal accesses).  SKEW: workgroup w walks its tiles starting at tile
+// w % TPW (and wraps), so that the workgroups in flight sit at different offsets of
+// their power-of-two-strided regions instead of all at the same one.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,7 +43,7 @@ __device__ __forceinline__ void store4(float* p, v4f v) {
     else *reinterpret_cast<v4f*>(p) = v;
 }
 
-template <int R, int TPW, bool NTL, bool NTS, int MODE>
+template <int R, int TPW, bool NTL, bool NTS, int MODE, bool SKEW>
 __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src, float* dst,
                                                                  float* sink, float scale) {
     constexpr int kR = R;
@@ -52,8 +54,10 @@ __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src
     const int64_t first = (int64_t)blockIdx.x * TPW;   // this workgroup's first tile
     const int64_t lane_off = (int64_t)row0 * kCols + 4 * col4;
     v4f va[kR], vb[kR];
+    const int rot = SKEW ? (int)(blockIdx.x % TPW) : 0;
+    auto tile = [&](int t) -> int64_t { return first + (t + rot < TPW ? t + rot : t + rot - TPW); };
     auto issue = [&](int t, v4f (&v)[kR]) {
-        const float* p = src + (first + t) * kTileFloats + lane_off;
+        const float* p = src + tile(t) * kTileFloats + lane_off;
 #pragma unroll
         for (int k = 0; k < kR; ++k) v[k] = load4<NTL>(p + (int64_t)k * kRpp * kCols);
     };
@@ -63,7 +67,7 @@ __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src
 #pragma unroll
             for (int k = 0; k < kR; ++k) acc += v[k];
         } else {
-            float* p = dst + (first + t) * kTileFloats + lane_off;
+            float* p = dst + tile(t) * kTileFloats + lane_off;
 #pragma unroll
             for (int k = 0; k < kR; ++k) store4<NTS>(p + (int64_t)k * kRpp * kCols, v[k] * scale);
         }
@@ -87,24 +91,25 @@ __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src
     }
 }
 
-template <int R, int TPW, int MODE>
+template <int R, int TPW, int MODE, bool SKEW>
 static const void* pick_nt(bool ntl, bool nts) {
-    if (ntl) return nts ? (const void*)&stream_probe_kernel<R, TPW, true, true, MODE>
-                        : (const void*)&stream_probe_kernel<R, TPW, true, false, MODE>;
-    return nts ? (const void*)&stream_probe_kernel<R, TPW, false, true, MODE>
-               : (const void*)&stream_probe_kernel<R, TPW, false, false, MODE>;
+    if (ntl) return nts ? (const void*)&stream_probe_kernel<R, TPW, true, true, MODE, SKEW>
+                        : (const void*)&stream_probe_kernel<R, TPW, true, false, MODE, SKEW>;
+    return nts ? (const void*)&stream_probe_kernel<R, TPW, false, true, MODE, SKEW>
+               : (const void*)&stream_probe_kernel<R, TPW, false, false, MODE, SKEW>;
 }
 
-template <int R, int TPW>
+template <int R, int TPW, bool SKEW>
 static const void* pick_mode(int mode, bool ntl, bool nts) {
-    return mode == 0 ? pick_nt<R, TPW, 0>(ntl, false) : pick_nt<R, TPW, 1>(ntl, nts);
+    return mode == 0 ? pick_nt<R, TPW, 0, SKEW>(ntl, false) : pick_nt<R, TPW, 1, SKEW>(ntl, nts);
 }
 
 template <int R>
-static const void* pick(int tpw, int mode, bool ntl, bool nts) {
-    return tpw == 1 ? pick_mode<R, 1>(mode, ntl, nts)
-         : tpw == 4 ? pick_mode<R, 4>(mode, ntl, nts)
-                    : pick_mode<R, 16>(mode, ntl, nts);
+static const void* pick(int tpw, int mode, bool ntl, bool nts, bool skew) {
+    if (skew) return tpw == 4 ? pick_mode<R, 4, true>(mode, ntl, nts) : pick_mode<R, 16, true>(mode, ntl, nts);
+    return tpw == 1 ? pick_mode<R, 1, false>(mode, ntl, nts)
+         : tpw == 4 ? pick_mode<R, 4, false>(mode, ntl, nts)
+                    : pick_mode<R, 16, false>(mode, ntl, nts);
 }
 
 }  // namespace rssm_probe
@@ -123,10 +128,11 @@ int64_t replayssm_probe_pass_floats(void) { return rssm_probe::kPassFloats; }
 //             the grid is n_floats / that (at most 2^31 - 1 workgroups)
 //   rows_per_thread in {1, 2, 8};  tiles_per_wg in {1, 4, 16}
 //   mode      0 read, 1 read+write;  nt_load / nt_store: nonzero for non-temporal accesses
+//   skew      nonzero: workgroup w starts at its tile w % tiles_per_wg (tiles_per_wg > 1)
 // Returns 0 on success, 1 for an invalid argument (nothing launched), 3 when the launch failed.
 int replayssm_probe_stream(const float* src, float* dst, float* sink, int64_t n_floats, int32_t rows_per_thread,
-                           int32_t tiles_per_wg, int32_t mode, int32_t nt_load, int32_t nt_store, float scale,
-                           hipStream_t stream) {
+                           int32_t tiles_per_wg, int32_t mode, int32_t nt_load, int32_t nt_store, int32_t skew,
+                           float scale, hipStream_t stream) {
     using namespace rssm_probe;
     if (!src || (reinterpret_cast<uintptr_t>(src) & 15) || n_floats <= 0) return 1;
     if (rows_per_thread != 1 && rows_per_thread != 2 && rows_per_thread != 8) return 1;
@@ -136,12 +142,14 @@ int replayssm_probe_stream(const float* src, float* dst, float* sink, int64_t n_
     if (mode == 0 && !sink) return 1;
     if (mode == 1 && (!dst || (reinterpret_cast<uintptr_t>(dst) & 15))) return 1;
     if (mode != 0 && mode != 1) return 1;
+    if (skew && tiles_per_wg == 1) return 1;
     const int64_t grid = n_floats / per_wg;
     if (grid > INT32_MAX) return 1;
     const bool ntl = nt_load != 0, nts = nt_store != 0;
-    const void* fn = rows_per_thread == 1 ? pick<1>(tiles_per_wg, mode, ntl, nts)
-                   : rows_per_thread == 2 ? pick<2>(tiles_per_wg, mode, ntl, nts)
-                                          : pick<8>(tiles_per_wg, mode, ntl, nts);
+    const bool sk = skew != 0;
+    const void* fn = rows_per_thread == 1 ? pick<1>(tiles_per_wg, mode, ntl, nts, sk)
+                   : rows_per_thread == 2 ? pick<2>(tiles_per_wg, mode, ntl, nts, sk)
+                                          : pick<8>(tiles_per_wg, mode, ntl, nts, sk);
     void* args[] = {(void*)&src, (void*)&dst, (void*)&sink, (void*)&scale};
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
     return e == hipSuccess ? 0 : 3;

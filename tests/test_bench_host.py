@@ -83,18 +83,90 @@ def test_source_hash_ignores_comments_only():
     assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
 
 
-def test_committed_counter_summary_parses():
-    traffic, src = bench.committed_traffic()
-    assert traffic is None or traffic > 1e9
-    assert isinstance(src, str)
-    traffic, src = bench.committed_traffic("gdn")
-    assert traffic is None or traffic > 1e8
-    assert isinstance(src, str)
+def test_committed_counter_summaries_parse():
+    for name in bench.PMC_FILES:
+        tr = bench.committed_traffic(name)
+        if tr is None:
+            assert isinstance(bench.committed_traffic_reason(name), str)
+        else:
+            assert tr["traffic"] > 1e8 and 0.5 < tr["ratio"] < 2.0 and tr["source"].startswith("profiles/")
 
 
-def test_gdn_window_bytes_matches_step_models():
+def test_gdn_flush_step_moves_the_state_twice():
     L = 16
     per = [bench.gdn_replay_bytes(256, 32, 16, 128, 128, L, 2, c) for c in range(L)]
-    assert bench.gdn_window_bytes() == sum(per) / L
     # the flush step reads and writes the state once: twice the state bytes of a read
     assert per[L - 1] - per[0] > 256 * 32 * 128 * 128 * 4 * 0.99
+
+
+class _FakeRunner(bench.Runner):
+    """Records dispatch indices; period L like a decode runner."""
+
+    def __init__(self, L):
+        self.period, self.B, self.launched = L, 4, []
+
+    def launch(self, i):
+        assert i == len(self.launched), "dispatches must be launched in order"
+        self.launched.append(i)
+
+    def bytes_of(self, i):
+        return 100 if i % self.period == self.period - 1 else 10
+
+
+@pytest.mark.parametrize("K,W,L", [(20, 5, 16), (1024, 32, 16), (7, 0, 4), (16, 16, 16), (1, 3, 16)])
+def test_headline_regions_start_at_a_flush(monkeypatch, K, W, L):
+    """Every timed region starts at the flush step and so holds ceil(K / L) flushes; the
+    warmup is W launches after the setup steps."""
+    calls = []
+
+    def fake_timed(torch, launch, first, n):
+        for i in range(first, first + n):
+            launch(i)
+        calls.append((first, n))
+        return 1e-3 * n
+
+    monkeypatch.setattr(bench, "timed_region", fake_timed)
+    r = _FakeRunner(L)
+    regions, setup, done = bench.measure(None, r, W, K, 3, start_at=L - 1)
+    assert (setup + W) % L == L - 1 and setup < L
+    assert [g["first"] % L for g in regions] == [L - 1] * 3
+    assert all(g["flushes"] == -(-K // L) for g in regions)
+    assert [c[1] for c in calls] == [K] * 3 and done == len(r.launched)
+    res = bench.summarize(regions, K)
+    assert res["value"] == pytest.approx(4 * K / (1e-3 * K))
+    assert res["flush_dispatches_per_region"] == -(-K // L)
+
+
+def test_summarize_takes_the_median_region():
+    regions = [dict(seconds=s, bytes=1000, tokens=10, flushes=1) for s in (3.0, 1.0, 2.0, 5.0, 4.0)]
+    res = bench.summarize(regions, 10)
+    assert res["value"] == pytest.approx(10 / 3.0)
+    assert sorted(res["values_per_region"]) == pytest.approx(sorted(10 / s for s in (3.0, 1.0, 2.0, 5.0, 4.0)))
+
+
+def test_pmc_summary_from_counter_files(tmp_path, monkeypatch):
+    """Two counter runs (FETCH_SIZE, WRITE_SIZE) of one variant become a summary scaled by
+    the calibration copy, and committed_traffic reads it back."""
+    def write_csv(d, counter, kern_val, copy_val):
+        d.mkdir()
+        with open(d / "x_counter_collection.csv", "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for i in range(4):
+                f.write(f'{i},"rssm::gdn_conventional_kernel<128, 128, unsigned short, false>(rssm::GdnArgs)",'
+                        f"{counter},{kern_val}\n")
+            f.write(f'9,"void at::native::vectorized_elementwise_kernel<4, MulFunctor>",{counter},{copy_val}\n')
+    write_csv(tmp_path / "f", "FETCH_SIZE", 1000.0, 524288.0)     # copy reads 1 GiB as 512 MiB
+    write_csv(tmp_path / "w", "WRITE_SIZE", 2000.0, 1048576.0)
+    info = dict(variant="gdn_hv32_conventional", kernel="gdn_conventional_kernel<128, 128, unsigned short, false>",
+                sources=bench.GDN_SOURCES, dispatches=4, algorithmic_bytes_per_dispatch=5000.0 * 1024)
+    ij = tmp_path / "info.json"
+    ij.write_text(bench.json.dumps(info))
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda sources=None: "feedfacefeedface")
+    bench.pmc_summarize(str(tmp_path / "f"), str(tmp_path / "w"), str(ij), "cmd")
+    tr = bench.committed_traffic("gdn_hv32_conventional")
+    assert tr["fetch"] == pytest.approx(2000.0 * 1024) and tr["write"] == pytest.approx(2000.0 * 1024)
+    assert tr["traffic"] == pytest.approx(4000.0 * 1024) and tr["ratio"] == pytest.approx(0.8)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda sources=None: "0000000000000000")
+    assert bench.committed_traffic("gdn_hv32_conventional") is None
