@@ -1,6 +1,6 @@
-// Emulated storage precision of a state ("ReplaySSM (a vLLM research fork)", README
-// section on the precision folders: the emulation kernels keep the read precision and
-// the recurrence precision apart and expose how each rounds).  An fp32 array is
+// Emulated storage precision of a state ("ReplaySSM" README, the paragraph on its two
+// precision folders: the emulation kernels keep the read precision and the recurrence
+// precision apart and expose how each rounds).  An fp32 array is
 // rounded in place to the values a narrower format holds, so that a recurrence that
 // keeps its state in that format can be run on the fp32 kernels: round the checkpoint
 // after every flush (replay) or the state after every step (conventional update).

@@ -414,8 +414,8 @@ replayssm_status replayssm_gdn_spec_baseline(const replayssm_gdn_desc* desc, flo
  * ====================================================================================== */
 
 /*
- * Emulated storage precision ("ReplaySSM (a vLLM research fork)", README section on
- * the precision folders: emulation kernels that keep the read precision apart from
+ * Emulated storage precision ("ReplaySSM" README, the paragraph on its two precision
+ * folders: emulation kernels that keep the read precision apart from
  * the recurrence precision and expose their rounding).  Rounds each of `rows` rows of
  * `row_len` fp32 values in `data` (device, 16-byte aligned, row-major) in place to
  * the value the format holds, so that a state kept in that format can be run through
