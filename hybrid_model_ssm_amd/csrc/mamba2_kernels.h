@@ -385,14 +385,19 @@ mamba2_replay_kernel(Mamba2Args a) {
             const int jn = min(kPosBatch, Tb - j0);
             const int elast = nstored + j0 + jn - 1;        // last row any of these windows uses
             const float Dh = sD[hl];
+            // z of these outputs and the window rows are requested before any of them is
+            // used, with no branch between the loads (rows past the window repeat its last
+            // row), so that their round trips overlap
+            Raw4 zr[kPosBatch];
+#pragma unroll
+            for (int jj = 0; jj < kPosBatch; ++jj) zr[jj] = io::ldraw4(zin, pos_x(h, j0 + min(jj, jn - 1)) + 4 * p4);
             float4 y[kPosBatch];
 #pragma unroll
             for (int jj = 0; jj < kPosBatch; ++jj) y[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int s0 = st; s0 <= elast; s0 += kRecBatch) {
                 Raw4 xr[kRecBatch];
 #pragma unroll
-                for (int i = 0; i < kRecBatch; ++i)
-                    if (s0 + i <= elast) xr[i] = io::ldraw4(xrow(h, s0 + i), 4 * p4);
+                for (int i = 0; i < kRecBatch; ++i) xr[i] = io::ldraw4(xrow(h, min(s0 + i, elast)), 4 * p4);
 #pragma unroll
                 for (int i = 0; i < kRecBatch; ++i) {
                     const int sr = s0 + i;
@@ -423,7 +428,7 @@ mamba2_replay_kernel(Mamba2Args a) {
                         yv = make_float4(Dh * xj.x, Dh * xj.y, Dh * xj.z, Dh * xj.w);
                     }
                     *reinterpret_cast<float4*>(sY + o) = yv;
-                    *reinterpret_cast<Raw4*>(sZ + o) = io::ldraw4(zin, pos_x(h, j) + 4 * p4);
+                    *reinterpret_cast<Raw4*>(sZ + o) = zr[jj];
                 }
             }
         }
