@@ -788,14 +788,20 @@ def precision_sweep(torch, rs, synth, batch=32):
 
 PROBE_LIB = os.path.join(ROOT, "hybrid_model_ssm_amd", "libreplayssm_probes.so")
 # (name, mode, rows per thread, tiles per workgroup, non-temporal loads, non-temporal stores,
-# in place, skewed tile order): mode 0 reads, mode 1 reads and writes
-PROBES = [(f"read_{'nt' if ntl else 'plain'}_r{r}_tpw{t}", 0, r, t, ntl, 0, False, False)
+# in place, tile order): mode 0 reads, modes 1 and 2 read and write; order 0 blocked (a workgroup's
+# tiles consecutive), 1 skewed, 2 interleaved (workgroup w's tile t at t * grid + w)
+PROBE_ORDERS = {1: "_skew", 2: "_ilv"}
+PROBES = [(f"read_{'nt' if ntl else 'plain'}_r{r}_tpw{t}", 0, r, t, ntl, 0, False, 0)
           for r in (1, 2, 8) for t in (1, 4, 16) for ntl in (0, 1)]
 PROBES += [(f"{'inplace' if ip else 'copy'}_{'nt' if ntl else 'plain'}_{'nt' if nts else 'plain'}_r{r}_tpw{t}",
-            1, r, t, ntl, nts, ip, False)
+            1, r, t, ntl, nts, ip, 0)
            for ip in (True, False) for r in (1, 2, 8) for t in (1, 4, 16) for ntl in (0, 1) for nts in (0, 1)]
-PROBES += [(f"{kind}_nt_nt_r{r}_tpw{t}_skew", 0 if kind == "read" else 1, r, t, 1, 1, kind == "inplace", True)
-           for kind in ("read", "inplace", "copy") for r in (1, 2, 8) for t in (4, 16)]
+PROBES += [(f"{kind}_nt_nt_r{r}_tpw{t}{PROBE_ORDERS[o]}", 0 if kind == "read" else 1, r, t, 1, 1,
+            kind == "inplace", o)
+           for o in (1, 2) for kind in ("read", "inplace", "copy") for r in (1, 2, 8) for t in (4, 16)]
+# mode 2: the next tile's loads alternate with the current tile's stores
+PROBES += [(f"{'inplace' if ip else 'copy'}_alt_nt_nt_r{r}_tpw{t}", 2, r, t, 1, 1, ip, 0)
+           for ip in (True, False) for r in (2, 8) for t in (4, 16)]
 
 
 def probe_lib():
@@ -848,12 +854,12 @@ def ceiling(torch, reps=20, repeats=3):
         return _median(secs)
 
     probes = {}
-    for name, mode, rpt, tpw, ntl, nts, inplace, skew in PROBES:
+    for name, mode, rpt, tpw, ntl, nts, inplace, order in PROBES:
         dst = a if inplace else b
 
         def launch():
             st = lib.replayssm_probe_stream(a.data_ptr(), dst.data_ptr(), sink.data_ptr(), n, rpt, tpw, mode,
-                                            ntl, nts, int(skew), 1.0, stream)
+                                            ntl, nts, order, 1.0, stream)
             if st:
                 raise RuntimeError(f"probe {name} failed with status {st}")
         secs = timed(launch)

@@ -12,11 +12,17 @@
 //   mode 0 (read):        sum each tile's values; one float per workgroup to `sink`
 //   mode 1 (read+write):  dst[tile] = scale * src[tile]; dst == src is the in-place
 //                         update of the flush and conventional steps, dst != src a copy
+//   mode 2 (read+write):  as mode 1, with the next tile's loads and the current tile's
+//                         stores alternating (load row k of tile t+1, store row k of tile
+//                         t) instead of all loads of tile t+1, then all stores of tile t
 //
 // Loads and stores are plain or non-temporal (the decode kernels stream the checkpoint
-// with non-temporal accesses).  SKEW: workgroup w walks its tiles starting at tile
-// w % TPW (and wraps), so that the workgroups in flight sit at different offsets of
-// their power-of-two-strided regions instead of all at the same one.
+// with non-temporal accesses).  ORDER places a workgroup's tiles:
+//   0 blocked:     workgroup w owns tiles [w TPW, (w + 1) TPW), walked in order
+//   1 skewed:      the same tiles, walked from tile w % TPW (and wrapping), so that the
+//                  workgroups in flight sit at different offsets of their regions
+//   2 interleaved: workgroup w's tile t is tile t G + w (G workgroups), so that the
+//                  workgroups in flight together touch one compact stretch of memory
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,7 +49,7 @@ __device__ __forceinline__ void store4(float* p, v4f v) {
     else *reinterpret_cast<v4f*>(p) = v;
 }
 
-template <int R, int TPW, bool NTL, bool NTS, int MODE, bool SKEW>
+template <int R, int TPW, bool NTL, bool NTS, int MODE, int ORDER>
 __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src, float* dst,
                                                                  float* sink, float scale) {
     constexpr int kR = R;
@@ -51,11 +57,14 @@ __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src
     const int tid = threadIdx.x;
     const int row0 = tid / kLpr;
     const int col4 = tid % kLpr;
-    const int64_t first = (int64_t)blockIdx.x * TPW;   // this workgroup's first tile
+    const int64_t first = (int64_t)blockIdx.x * TPW;   // this workgroup's first tile (blocked)
     const int64_t lane_off = (int64_t)row0 * kCols + 4 * col4;
     v4f va[kR], vb[kR];
-    const int rot = SKEW ? (int)(blockIdx.x % TPW) : 0;
-    auto tile = [&](int t) -> int64_t { return first + (t + rot < TPW ? t + rot : t + rot - TPW); };
+    const int rot = ORDER == 1 ? (int)(blockIdx.x % TPW) : 0;
+    auto tile = [&](int t) -> int64_t {
+        if constexpr (ORDER == 2) return (int64_t)t * gridDim.x + blockIdx.x;
+        return first + (t + rot < TPW ? t + rot : t + rot - TPW);
+    };
     auto issue = [&](int t, v4f (&v)[kR]) {
         const float* p = src + tile(t) * kTileFloats + lane_off;
 #pragma unroll
@@ -74,8 +83,18 @@ __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src
     };
     issue(0, va);
     for (int t = 0; t + 1 < TPW; ++t) {
-        issue(t + 1, vb);
-        finish(t, va);
+        if constexpr (MODE == 2) {
+            const float* ps = src + tile(t + 1) * kTileFloats + lane_off;
+            float* pd = dst + tile(t) * kTileFloats + lane_off;
+#pragma unroll
+            for (int k = 0; k < kR; ++k) {
+                vb[k] = load4<NTL>(ps + (int64_t)k * kRpp * kCols);
+                store4<NTS>(pd + (int64_t)k * kRpp * kCols, va[k] * scale);
+            }
+        } else {
+            issue(t + 1, vb);
+            finish(t, va);
+        }
 #pragma unroll
         for (int k = 0; k < kR; ++k) va[k] = vb[k];
     }
@@ -91,25 +110,30 @@ __global__ void __launch_bounds__(kThreads) stream_probe_kernel(const float* src
     }
 }
 
-template <int R, int TPW, int MODE, bool SKEW>
+template <int R, int TPW, int MODE, int ORDER>
 static const void* pick_nt(bool ntl, bool nts) {
-    if (ntl) return nts ? (const void*)&stream_probe_kernel<R, TPW, true, true, MODE, SKEW>
-                        : (const void*)&stream_probe_kernel<R, TPW, true, false, MODE, SKEW>;
-    return nts ? (const void*)&stream_probe_kernel<R, TPW, false, true, MODE, SKEW>
-               : (const void*)&stream_probe_kernel<R, TPW, false, false, MODE, SKEW>;
+    if (ntl) return nts ? (const void*)&stream_probe_kernel<R, TPW, true, true, MODE, ORDER>
+                        : (const void*)&stream_probe_kernel<R, TPW, true, false, MODE, ORDER>;
+    return nts ? (const void*)&stream_probe_kernel<R, TPW, false, true, MODE, ORDER>
+               : (const void*)&stream_probe_kernel<R, TPW, false, false, MODE, ORDER>;
 }
 
-template <int R, int TPW, bool SKEW>
+template <int R, int TPW, int ORDER>
 static const void* pick_mode(int mode, bool ntl, bool nts) {
-    return mode == 0 ? pick_nt<R, TPW, 0, SKEW>(ntl, false) : pick_nt<R, TPW, 1, SKEW>(ntl, nts);
+    return mode == 0 ? pick_nt<R, TPW, 0, ORDER>(ntl, false)
+         : mode == 1 ? pick_nt<R, TPW, 1, ORDER>(ntl, nts) : pick_nt<R, TPW, 2, ORDER>(ntl, nts);
+}
+
+template <int R, int ORDER>
+static const void* pick_tpw(int tpw, int mode, bool ntl, bool nts) {
+    return tpw == 4 ? pick_mode<R, 4, ORDER>(mode, ntl, nts) : pick_mode<R, 16, ORDER>(mode, ntl, nts);
 }
 
 template <int R>
-static const void* pick(int tpw, int mode, bool ntl, bool nts, bool skew) {
-    if (skew) return tpw == 4 ? pick_mode<R, 4, true>(mode, ntl, nts) : pick_mode<R, 16, true>(mode, ntl, nts);
-    return tpw == 1 ? pick_mode<R, 1, false>(mode, ntl, nts)
-         : tpw == 4 ? pick_mode<R, 4, false>(mode, ntl, nts)
-                    : pick_mode<R, 16, false>(mode, ntl, nts);
+static const void* pick(int tpw, int mode, bool ntl, bool nts, int order) {
+    if (order == 1) return pick_tpw<R, 1>(tpw, mode, ntl, nts);
+    if (order == 2) return pick_tpw<R, 2>(tpw, mode, ntl, nts);
+    return tpw == 1 ? pick_mode<R, 1, 0>(mode, ntl, nts) : pick_tpw<R, 0>(tpw, mode, ntl, nts);
 }
 
 }  // namespace rssm_probe
@@ -122,16 +146,17 @@ int64_t replayssm_probe_pass_floats(void) { return rssm_probe::kPassFloats; }
 
 // One probe launch on `stream`.
 //   src       device f32 [n_floats], 16-byte aligned (read by every mode)
-//   dst       mode 1: device f32 [n_floats], 16-byte aligned (may equal src); mode 0: ignored
-//   sink      mode 0: device f32 [number of workgroups] (one sum each); mode 1: ignored
+//   dst       modes 1, 2: device f32 [n_floats], 16-byte aligned (may equal src); mode 0: ignored
+//   sink      mode 0: device f32 [number of workgroups] (one sum each); modes 1, 2: ignored
 //   n_floats  > 0 and a multiple of pass_floats * rows_per_thread * tiles_per_wg;
 //             the grid is n_floats / that (at most 2^31 - 1 workgroups)
 //   rows_per_thread in {1, 2, 8};  tiles_per_wg in {1, 4, 16}
-//   mode      0 read, 1 read+write;  nt_load / nt_store: nonzero for non-temporal accesses
-//   skew      nonzero: workgroup w starts at its tile w % tiles_per_wg (tiles_per_wg > 1)
+//   mode      0 read, 1 read+write, 2 read+write with alternating loads and stores;
+//             nt_load / nt_store: nonzero for non-temporal accesses
+//   order     0 blocked, 1 skewed, 2 interleaved (1 and 2 need tiles_per_wg > 1)
 // Returns 0 on success, 1 for an invalid argument (nothing launched), 3 when the launch failed.
 int replayssm_probe_stream(const float* src, float* dst, float* sink, int64_t n_floats, int32_t rows_per_thread,
-                           int32_t tiles_per_wg, int32_t mode, int32_t nt_load, int32_t nt_store, int32_t skew,
+                           int32_t tiles_per_wg, int32_t mode, int32_t nt_load, int32_t nt_store, int32_t order,
                            float scale, hipStream_t stream) {
     using namespace rssm_probe;
     if (!src || (reinterpret_cast<uintptr_t>(src) & 15) || n_floats <= 0) return 1;
@@ -140,16 +165,15 @@ int replayssm_probe_stream(const float* src, float* dst, float* sink, int64_t n_
     const int64_t per_wg = kPassFloats * rows_per_thread * tiles_per_wg;
     if (n_floats % per_wg) return 1;
     if (mode == 0 && !sink) return 1;
-    if (mode == 1 && (!dst || (reinterpret_cast<uintptr_t>(dst) & 15))) return 1;
-    if (mode != 0 && mode != 1) return 1;
-    if (skew && tiles_per_wg == 1) return 1;
+    if (mode != 0 && (!dst || (reinterpret_cast<uintptr_t>(dst) & 15))) return 1;
+    if (mode < 0 || mode > 2) return 1;
+    if (order < 0 || order > 2 || (order != 0 && tiles_per_wg == 1)) return 1;
     const int64_t grid = n_floats / per_wg;
     if (grid > INT32_MAX) return 1;
     const bool ntl = nt_load != 0, nts = nt_store != 0;
-    const bool sk = skew != 0;
-    const void* fn = rows_per_thread == 1 ? pick<1>(tiles_per_wg, mode, ntl, nts, sk)
-                   : rows_per_thread == 2 ? pick<2>(tiles_per_wg, mode, ntl, nts, sk)
-                                          : pick<8>(tiles_per_wg, mode, ntl, nts, sk);
+    const void* fn = rows_per_thread == 1 ? pick<1>(tiles_per_wg, mode, ntl, nts, order)
+                   : rows_per_thread == 2 ? pick<2>(tiles_per_wg, mode, ntl, nts, order)
+                                          : pick<8>(tiles_per_wg, mode, ntl, nts, order);
     void* args[] = {(void*)&src, (void*)&dst, (void*)&sink, (void*)&scale};
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
     return e == hipSuccess ? 0 : 3;
