@@ -275,6 +275,41 @@ mamba2_replay_kernel(Mamba2Args a) {
         }
     };
 
+    // ---- prologue 1 requests ----------------------------------------------------------
+    // The values the staging below needs (up to kPre1 tasks of each kind per thread; a
+    // longer window takes the rest in a loop) are requested before the first checkpoint
+    // tile, with clamped indices and no branch between the loads: the loads retire in
+    // order, so staging then waits on these alone and not on the tile requested after them.
+    constexpr int kPre1 = 2;
+    const int nBt = nrec * N4;          // staging tasks of the window's B rows
+    const int nDt = nh * nrec;          // staging tasks of the window's dt values
+    Raw4 preB[kPre1];
+    float preRec[kPre1], preIn[kPre1], preBias[kPre1];
+#pragma unroll
+    for (int i = 0; i < kPre1; ++i) {
+        const int task = min(tid + i * kThreads, max(nBt - 1, 0));
+        const int s = task / N4, n4 = task - (task / N4) * N4;
+        // the explicit flush has no inputs: its rows (none, for an empty buffer) are records
+        const IO* src = (MODE == kFold || s < nstored) ? recB + (size_t)slot_of(min(s, L - 1)) * N
+                                                       : Bin + pos_g(s - nstored);
+        preB[i] = io::ldraw4(src, 4 * n4);
+    }
+    Raw4 preC{};
+    if constexpr (MODE != kFold) preC = io::ldraw4(Cin, pos_g(min(tid / N4, max(Tb - 1, 0))) + 4 * (tid % N4));
+#pragma unroll
+    for (int i = 0; i < kPre1; ++i) {
+        const int task = min(tid + i * kThreads, max(nDt - 1, 0));
+        const int s = task / nh, h = h0 + (task - (task / nh) * nh);
+        preRec[i] = a.rec_dt[((size_t)sb * L + slot_of(min(s, L - 1))) * H + h];
+        preIn[i] = preBias[i] = 0.f;
+        if constexpr (MODE != kFold) {
+            preIn[i] = io::ld(dtin, pos_h(h, min(max(s - nstored, 0), max(Tb - 1, 0))));
+            preBias[i] = a.dt_bias[h];
+        }
+    }
+    const float preA = a.A[h0 + min(tid, nh - 1)];
+    const float preD = (MODE != kFold) ? a.D[h0 + min(tid, nh - 1)] : 0.f;
+
     float4 va[R], vb[R];
     uint4 qa[RQ], qb[RQ];
     float sqa = 0.f, sqb = 0.f;
@@ -299,29 +334,47 @@ mamba2_replay_kernel(Mamba2Args a) {
     }
 
     // ---- prologue 1: stage the group's window -------------------------------------------
-    for (int task = tid; task < nrec * N4; task += kThreads) {
+    auto dt_of = [&](float rec, float in, float bias, bool stored) {
+        if (stored) return rec;                         // records keep the prepared dt
+        const float dt = in + bias;
+        return a.dt_softplus ? softplus_f32(dt) : dt;
+    };
+#pragma unroll
+    for (int i = 0; i < kPre1; ++i) {
+        const int task = tid + i * kThreads;
+        if (task < nBt) *reinterpret_cast<Raw4*>(sB + task * 4) = preB[i];   // row task / N4, column 4 (task % N4)
+    }
+    for (int task = tid + kPre1 * kThreads; task < nBt; task += kThreads) {
         const int s = task / N4, n4 = task % N4;
         const Raw4 r = (s < nstored) ? io::ldraw4(recB, (size_t)slot_of(s) * N + 4 * n4)
                                      : io::ldraw4(Bin, pos_g(s - nstored) + 4 * n4);
         *reinterpret_cast<Raw4*>(sB + s * N + 4 * n4) = r;
     }
-    for (int task = tid; task < Tb * N4; task += kThreads) {
+    if (tid < Tb * N4) *reinterpret_cast<float4*>(sC + tid * 4) = io::cvt4(preC);
+    for (int task = tid + kThreads; task < Tb * N4; task += kThreads) {
         const int j = task / N4, n4 = task % N4;
         *reinterpret_cast<float4*>(sC + j * N + 4 * n4) = io::cvt4(io::ldraw4(Cin, pos_g(j) + 4 * n4));
     }
-    for (int task = tid; task < nh * nrec; task += kThreads) {
-        const int s = task / nh, hl = task - s * nh;   // a slot's heads are contiguous in rec_dt
-        const int h = h0 + hl;
-        float dt;
-        if (s < nstored) {
-            dt = a.rec_dt[((size_t)sb * L + slot_of(s)) * H + h];
-        } else {
-            dt = io::ld(dtin, pos_h(h, s - nstored)) + a.dt_bias[h];
-            if (a.dt_softplus) dt = softplus_f32(dt);
+    // a slot's heads are contiguous in rec_dt: task = s * nh + head
+#pragma unroll
+    for (int i = 0; i < kPre1; ++i) {
+        const int task = tid + i * kThreads;
+        if (task < nDt) {
+            const int s = task / nh, hl = task - s * nh;
+            sdt[hl * NR + s] = dt_of(preRec[i], preIn[i], preBias[i], s < nstored);
         }
-        sdt[hl * NR + s] = dt;
     }
-    for (int hl = tid; hl < nh; hl += kThreads) {
+    for (int task = tid + kPre1 * kThreads; task < nDt; task += kThreads) {
+        const int s = task / nh, hl = task - s * nh;
+        const int h = h0 + hl;
+        sdt[hl * NR + s] = dt_of(s < nstored ? a.rec_dt[((size_t)sb * L + slot_of(s)) * H + h] : 0.f,
+                                 s < nstored ? 0.f : io::ld(dtin, pos_h(h, s - nstored)), a.dt_bias[h], s < nstored);
+    }
+    if (tid < nh) {
+        sA[tid] = preA;
+        if (MODE != kFold) sD[tid] = preD;
+    }
+    for (int hl = tid + kThreads; hl < nh; hl += kThreads) {
         sA[hl] = a.A[h0 + hl];
         if (MODE != kFold) sD[hl] = a.D[h0 + hl];
     }
