@@ -82,7 +82,7 @@ struct GdnSmem {
 //               is position j; if committed + n_pos > L the committed rows are folded
 //               first and every position's chain starts after them.
 template <int DK, int DV, typename IO, int MODE>
-__global__ void __launch_bounds__(kGdnThreads, MODE == kGdnSpec ? 4 : 1) gdn_replay_kernel(GdnArgs a) {
+__global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_replay_kernel(GdnArgs a) {
     using io = Io<IO>;
     using Raw4 = typename io::Raw4;
     using S = GdnShape<DK>;
@@ -194,12 +194,8 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnSpec ? 4 : 1) gdn_rep
     };
     const int nunit = nv * NTILE;
     float4 va[R], vb[R];
-    if (!idle) {
-        if (fold) issue_tile_f(0, va);
-        else issue_tile(0, va);
-    }
 
-    // ---- stage the window -------------------------------------------------------------
+    // ---- window sources ----------------------------------------------------------------
     auto slot_of = [&](int s) {
         if constexpr (MODE == kGdnSpec) {
             const int t = hd + s;
@@ -219,32 +215,85 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnSpec ? 4 : 1) gdn_rep
     const IO* qin = reinterpret_cast<const IO*>(a.q);
     const IO* vin = reinterpret_cast<const IO*>(a.v);
     const IO* recV = reinterpret_cast<const IO*>(a.rec_v);
-    for (int task = tid; task < nrec * DK4; task += kGdnThreads) {
-        const int s = task / DK4, j4 = task % DK4;
-        const Raw4 r = (s < nstored) ? io::ldraw4(recK, (size_t)slot_of(s) * DK + 4 * j4)
-                                     : io::ldraw4(kin, pos_qk(s - nstored) + 4 * j4);
-        *reinterpret_cast<Raw4*>(sK + s * DK + 4 * j4) = r;
+    // window row s of each kind: a ring record (the explicit fold has no inputs, so its rows
+    // -- none, for an empty buffer -- are records) or one of this call's positions
+    auto rec_row = [&](int s) { return MODE == kGdnFold || s < nstored; };
+    auto k_src = [&](int s) -> const IO* {
+        return rec_row(s) ? recK + (size_t)slot_of(min(s, L - 1)) * DK : kin + pos_qk(s - nstored);
+    };
+    auto v_src = [&](int vl, int s) -> const IO* {
+        return rec_row(s) ? recV + ((sHV + hv0 + vl) * L + slot_of(min(s, L - 1))) * DV
+                          : vin + pos_h(vl, s - nstored) * DV;
+    };
+    auto ab_src = [&](const float* rec, const float* in, int vl, int s) -> const float* {
+        return rec_row(s) ? rec + ((size_t)sb * L + slot_of(min(s, L - 1))) * HV + hv0 + vl : in + pos_h(vl, s - nstored);
+    };
+
+    // ---- staging requests ----------------------------------------------------------------
+    // Up to a fixed number of staging tasks of each kind per thread (a longer window takes
+    // the rest in loops below) are requested before the first checkpoint tile, with
+    // clamped indices and no branch between the loads: loads retire in order, so staging
+    // then waits on these alone and not on the tile requested after them.
+    constexpr int kPreK = (MODE == kGdnSpec) ? 3 : 2;   // k rows: nrec * DK / 4 tasks
+    constexpr int kPreV = (MODE == kGdnSpec) ? 5 : 4;   // v rows: nv * nrec * DV / 4 tasks
+    const int nKt = nrec * DK4, nVt = nv * nrec * DV4, nAt = nv * nrec;
+    Raw4 preK[kPreK], preV[kPreV], preQ{};
+    float preAl, preBe;
+#pragma unroll
+    for (int i = 0; i < kPreK; ++i) {
+        const int task = min(tid + i * kGdnThreads, max(nKt - 1, 0));
+        preK[i] = io::ldraw4(k_src(task / DK4), 4 * (task % DK4));
     }
-    for (int task = tid; task < nv * nrec * DV4; task += kGdnThreads) {
-        const int i4 = task % DV4;
-        const int vs = task / DV4;
-        const int vl = vs / nrec, s = vs - vl * nrec;
-        const size_t hv = sHV + hv0 + vl;
-        const Raw4 r = (s < nstored) ? io::ldraw4(recV, (hv * L + slot_of(s)) * DV + 4 * i4)
-                                     : io::ldraw4(vin, pos_h(vl, s - nstored) * DV + 4 * i4);
-        *reinterpret_cast<Raw4*>(sV + (vl * NR + s) * DV + 4 * i4) = r;
+#pragma unroll
+    for (int i = 0; i < kPreV; ++i) {
+        const int task = min(tid + i * kGdnThreads, max(nVt - 1, 0));
+        const int vs = task / DV4, vl = vs / max(nrec, 1);
+        preV[i] = io::ldraw4(v_src(vl, vs - vl * max(nrec, 1)), 4 * (task % DV4));
     }
-    for (int task = tid; task < nv * nrec; task += kGdnThreads) {
+    {
+        const int task = min(tid, max(nAt - 1, 0));
         const int s = task / nv, vl = task - s * nv;   // a slot's value heads are contiguous
-        const size_t g = ((size_t)sb * L + slot_of(s)) * HV + hv0 + vl;
-        const bool rec = s < nstored;
-        sAl[vl * NR + s] = rec ? a.rec_alpha[g] : a.alpha[pos_h(vl, s - nstored)];
-        sBe[vl * NR + s] = rec ? a.rec_beta[g] : a.beta[pos_h(vl, s - nstored)];
+        preAl = *ab_src(a.rec_alpha, a.alpha, vl, s);
+        preBe = *ab_src(a.rec_beta, a.beta, vl, s);
     }
-    for (int task = tid; task < Tb * DK4; task += kGdnThreads) {
-        const int j = task / DK4, j4 = task % DK4;
-        *reinterpret_cast<float4*>(sQ + j * DK + 4 * j4) = io::cvt4(io::ldraw4(qin, pos_qk(j) + 4 * j4));
+    if constexpr (MODE != kGdnFold) {
+        const int task = min(tid, max(Tb * DK4 - 1, 0));
+        preQ = io::ldraw4(qin, pos_qk(task / DK4) + 4 * (task % DK4));
     }
+    if (!idle) {
+        if (fold) issue_tile_f(0, va);
+        else issue_tile(0, va);
+    }
+
+    // ---- stage the window -------------------------------------------------------------
+#pragma unroll
+    for (int i = 0; i < kPreK; ++i) {
+        const int task = tid + i * kGdnThreads;
+        if (task < nKt) *reinterpret_cast<Raw4*>(sK + 4 * task) = preK[i];   // row task / DK4
+    }
+    for (int task = tid + kPreK * kGdnThreads; task < nKt; task += kGdnThreads)
+        *reinterpret_cast<Raw4*>(sK + 4 * task) = io::ldraw4(k_src(task / DK4), 4 * (task % DK4));
+    auto stage_v = [&](int task, Raw4 r) {
+        const int vs = task / DV4, vl = vs / nrec, s = vs - vl * nrec;
+        *reinterpret_cast<Raw4*>(sV + (vl * NR + s) * DV + 4 * (task % DV4)) = r;
+    };
+#pragma unroll
+    for (int i = 0; i < kPreV; ++i) {
+        const int task = tid + i * kGdnThreads;
+        if (task < nVt) stage_v(task, preV[i]);
+    }
+    for (int task = tid + kPreV * kGdnThreads; task < nVt; task += kGdnThreads) {
+        const int vs = task / DV4, vl = vs / nrec;
+        stage_v(task, io::ldraw4(v_src(vl, vs - vl * nrec), 4 * (task % DV4)));
+    }
+    for (int task = tid; task < nAt; task += kGdnThreads) {
+        const int s = task / nv, vl = task - s * nv;
+        sAl[vl * NR + s] = task == tid ? preAl : *ab_src(a.rec_alpha, a.alpha, vl, s);
+        sBe[vl * NR + s] = task == tid ? preBe : *ab_src(a.rec_beta, a.beta, vl, s);
+    }
+    if (tid < Tb * DK4) *reinterpret_cast<float4*>(sQ + 4 * tid) = io::cvt4(preQ);   // row tid / DK4
+    for (int task = tid + kGdnThreads; task < Tb * DK4; task += kGdnThreads)
+        *reinterpret_cast<float4*>(sQ + 4 * task) = io::cvt4(io::ldraw4(qin, pos_qk(task / DK4) + 4 * (task % DK4)));
     __syncthreads();
 
     const int q = tid % LPR;
