@@ -98,11 +98,11 @@ struct GroupSmem {
 };
 
 // LP: kind of low-precision read copy (kLpNone, kLpBF16, kLpF16, kLpFP8).  Decode steps
-// that read a copy stream half or a quarter of the fp32 bytes per tile and are held to
-// four waves per SIMD (measured faster despite a few spilled registers); the other
-// instances keep the register budget the compiler picks.
+// that read a copy stream half or a quarter of the fp32 bytes per tile, keep two copy
+// tiles in flight and are held to three waves per SIMD (the register budget of those three
+// buffers without spills); the other instances keep the budget the compiler picks.
 template <int P, int N, typename IO, int LP, int MODE>
-__global__ void __launch_bounds__(kThreads, (LP != kLpNone && MODE == kDecode) ? 4 : 1)
+__global__ void __launch_bounds__(kThreads, (LP != kLpNone && MODE == kDecode) ? 3 : 1)
 mamba2_replay_kernel(Mamba2Args a) {
     constexpr bool LOWP = LP != kLpNone;
     using io = Io<IO>;
@@ -583,8 +583,33 @@ mamba2_replay_kernel(Mamba2Args a) {
         }
     };
 
-    if (!fold && use_lp) {
-        // tile hl+1 is loaded while head hl is reduced
+    if (!fold && use_lp && nh >= 3) {
+        // copy tiles are small: heads hl+1 and hl+2 stream while head hl is reduced.  Three
+        // buffers in fixed roles (unrolled by three): a register copy of a tile still in
+        // flight would wait for it.
+        uint4 qc[RQ];
+        float sqc = 0.f;
+        issue_tile_lp(1, qb, sqb);
+        issue_tile_lp(2, qc, sqc);
+        int hl = 0;
+        for (; hl + 5 < nh; hl += 3) {
+            outputs_lp(hl, qa, sqa);
+            issue_tile_lp(hl + 3, qa, sqa);
+            outputs_lp(hl + 1, qb, sqb);
+            issue_tile_lp(hl + 4, qb, sqb);
+            outputs_lp(hl + 2, qc, sqc);
+            issue_tile_lp(hl + 5, qc, sqc);
+        }
+        const int rest = nh - hl;       // 3, 4 or 5 heads remain
+        outputs_lp(hl, qa, sqa);
+        if (rest > 3) issue_tile_lp(hl + 3, qa, sqa);
+        outputs_lp(hl + 1, qb, sqb);
+        if (rest > 4) issue_tile_lp(hl + 4, qb, sqb);
+        outputs_lp(hl + 2, qc, sqc);
+        if (rest > 3) outputs_lp(hl + 3, qa, sqa);
+        if (rest > 4) outputs_lp(hl + 4, qb, sqb);
+    } else if (!fold && use_lp) {
+        // one or two heads: tile hl+1 is loaded while head hl is reduced
         for (int hl = 0; hl + 1 < nh; ++hl) {
             issue_tile_lp(hl + 1, qb, sqb);
             outputs_lp(hl, qa, sqa);
