@@ -122,7 +122,13 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_rep
     if constexpr (MODE == kGdnSpec) {
         const SpecSeq q = spec_sequence_heavy_first<kGdnThreads>(bk / HK, a.batch, L, T, a.slot, a.n_pos_seq,
                                                                  a.cursor_in, a.committed);
-        b = q.b; sb = q.sb; Tb = q.Tb; hd = q.hd; cm = q.cm;
+        // the pick is the same in every lane (it comes through LDS): keep it in scalar
+        // registers, with everything derived from it
+        b = __builtin_amdgcn_readfirstlane(q.b);
+        sb = __builtin_amdgcn_readfirstlane(q.sb);
+        Tb = __builtin_amdgcn_readfirstlane(q.Tb);
+        hd = __builtin_amdgcn_readfirstlane(q.hd);
+        cm = __builtin_amdgcn_readfirstlane(q.cm);
     } else {
         b = bk / HK;
         sb = a.slot ? a.slot[b] : b;

@@ -138,7 +138,13 @@ mamba2_replay_kernel(Mamba2Args a) {
     if constexpr (MODE == kSpec) {
         const SpecSeq q = spec_sequence_heavy_first<kThreads>(bg / G, a.batch, L, T, a.slot, a.n_pos_seq,
                                                               a.cursor_in, a.committed);
-        b = q.b; sb = q.sb; Tb = q.Tb; hd = q.hd; cm = q.cm;
+        // the pick is the same in every lane (it comes through LDS): keep it in scalar
+        // registers, with everything derived from it
+        b = __builtin_amdgcn_readfirstlane(q.b);
+        sb = __builtin_amdgcn_readfirstlane(q.sb);
+        Tb = __builtin_amdgcn_readfirstlane(q.Tb);
+        hd = __builtin_amdgcn_readfirstlane(q.hd);
+        cm = __builtin_amdgcn_readfirstlane(q.cm);
     } else {
         b = bg / G;
         sb = a.slot ? a.slot[b] : b;
