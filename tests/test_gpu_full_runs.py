@@ -126,6 +126,8 @@ def test_mamba2_every_step_of_the_run(name, kinds):
     worst_rms = {k: 0.0 for k in kinds}
     n_flush = 0
     for t in range(1, w["steps"] + 1):
+        if t % (w["steps"] // 4) == 0:
+            print(f"[full run] {name} step {t} of {w['steps']}", flush=True)
         dev, s, _ = steps.step(t - 1)
         ref, flushed = rep.step(**s)
         args = [dev[k] for k in ("x", "z", "B", "C", "dt_raw")]
@@ -200,6 +202,8 @@ def test_mamba2_spec_every_round_of_the_run():
     cm_all = np.zeros(B, np.int64)
     n_flush = 0
     for r in range(w["rounds"]):
+        if (r + 1) % (w["rounds"] // 4) == 0:
+            print(f"[full run] {name} round {r + 1} of {w['rounds']}", flush=True)
         dev, s, keep = rounds.step(r)
         ck_before = state.ckpt[idx].clone()
         ref, fl_ref = spec.verify(**s)
@@ -242,7 +246,8 @@ def _gdn_pooled(name, n_pos=None):
 
 @pytest.mark.timeout(900)
 def test_gdn_every_step_of_the_run():
-    w, gen, steps = _gdn_pooled("gdn_hv32")
+    name = "gdn_hv32"
+    w, gen, steps = _gdn_pooled(name)
     st = gen.static
     B, HV, HK, dk, dv, L = (w[k] for k in ("batch", "num_v_heads", "num_k_heads", "dk", "dv", "buffer_len"))
     desc = rs.GdnDesc(B, HV, HK, dk, dv, L, rs.BF16)
@@ -254,6 +259,8 @@ def test_gdn_every_step_of_the_run():
     idx = torch.from_numpy(SAMPLE).to(DEV)
     n_flush = 0
     for t in range(1, w["steps"] + 1):
+        if t % (w["steps"] // 4) == 0:
+            print(f"[full run] {name} step {t} of {w['steps']}", flush=True)
         dev, s, _ = steps.step(t - 1)
         ref, flushed = rep.step(**s)
         rs.gdn_decode(desc, state, cur[(t - 1) % 2], cur[t % 2], *(dev[k] for k in ("q", "k", "v", "alpha", "beta")),
@@ -288,6 +295,8 @@ def test_gdn_spec_every_round_of_the_run():
     cm_all = np.zeros(B, np.int64)
     n_flush = 0
     for r in range(w["rounds"]):
+        if (r + 1) % (w["rounds"] // 4) == 0:
+            print(f"[full run] {name} round {r + 1} of {w['rounds']}", flush=True)
         dev, s, keep = rounds.step(r)
         ck_before = state.ckpt[idx].clone()
         ref, fl_ref = spec.verify(**s)
