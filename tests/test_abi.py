@@ -257,3 +257,29 @@ def test_emulate_precision_validation(L):
     # documented to launch nothing
     assert E(fake(1), 8, 8, rs.F32, None, None) == rs.OK
     assert E(fake(1), 0, 8, rs.FP8_E4M3, None, None) == rs.OK
+
+
+def test_probe_library_rejects_invalid_arguments_before_launching():
+    """The benchmark's streaming probes (libreplayssm_probes.so, not part of the C ABI
+    above): one 16-byte access per thread per pass, and every invalid argument returns 1
+    before anything is launched (fake, never dereferenced pointers)."""
+    import bench
+    if not os.path.exists(bench.PROBE_LIB):
+        from hybrid_model_ssm_amd import build
+        build.build()
+    P = bench.probe_lib()
+    pf = P.replayssm_probe_pass_floats()
+    assert pf == 256 * 4
+    src, dst, sink = 0x100000, 0x200000, 0x300000
+    n = pf * 8 * 16            # one workgroup of 16 tiles of 8 rows per thread
+
+    def call(**kw):
+        a = dict(src=src, dst=dst, sink=sink, n=n, rpt=8, tpw=16, mode=1, ntl=1, nts=1, order=0)
+        a.update(kw)
+        return P.replayssm_probe_stream(a["src"], a["dst"], a["sink"], a["n"], a["rpt"], a["tpw"], a["mode"],
+                                        a["ntl"], a["nts"], a["order"], 1.0, None)
+
+    for bad in (dict(src=0), dict(src=src + 4), dict(n=0), dict(n=n + 4), dict(rpt=3), dict(tpw=2),
+                dict(mode=3), dict(mode=-1), dict(mode=0, sink=0), dict(mode=1, dst=0), dict(mode=2, dst=dst + 8),
+                dict(order=3), dict(order=1, tpw=1, n=pf * 8)):
+        assert call(**bad) == 1, bad
