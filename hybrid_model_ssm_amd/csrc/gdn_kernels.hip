@@ -240,8 +240,10 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_rep
     // the rest in loops below) are requested before the first checkpoint tile, with
     // clamped indices and no branch between the loads: loads retire in order, so staging
     // then waits on these alone and not on the tile requested after them.
-    constexpr int kPreK = (MODE == kGdnSpec) ? 3 : 2;   // k rows: nrec * DK / 4 tasks
-    constexpr int kPreV = (MODE == kGdnSpec) ? 5 : 4;   // v rows: nv * nrec * DV / 4 tasks
+    // Speculative rounds request one of each up front: their windows are longer, and
+    // registers held for more spill in the fold (measured slower).
+    constexpr int kPreK = (MODE == kGdnSpec) ? 1 : 2;   // k rows: nrec * DK / 4 tasks
+    constexpr int kPreV = (MODE == kGdnSpec) ? 1 : 4;   // v rows: nv * nrec * DV / 4 tasks
     const int nKt = nrec * DK4, nVt = nv * nrec * DV4, nAt = nv * nrec;
     Raw4 preK[kPreK], preV[kPreV], preQ{};
     float preAl, preBe;
