@@ -13,7 +13,8 @@ before a region starts: a pool of 2L pre-drawn steps is cycled.  ``roofline`` gi
 the replay kernel's algorithmic HBM bytes per launch divided by its average launch
 time (HIP events on the launch stream) against the 8 TB/s peak; ``traffic`` is the
 counter-measured HBM bytes per launch from the committed rocprofv3 summary when it
-matches the current kernel source, else null.  ``step_split`` times two further
+matches the current kernel source, else null (``traffic_gbps`` and ``traffic_frac``: those
+bytes over the same launch time, against the peak).  ``step_split`` times two further
 windows launch by launch: flush and non-flush steps.  ``cpu_baseline`` times the fp64
 CPU oracle (replay and conventional forms, three workloads) on a sample of each, its
 sequences sharded over worker processes on the host's cores (forked before the GPU is
@@ -611,8 +612,9 @@ def time_variant(torch, rs, synth, name, K, W, repeats):
     res.update(unit=r.unit, workload=workload, kernel=f"rssm::{r.tag}")
     tr = committed_traffic(name)
     if tr is not None:
+        tg = tr["traffic"] / (res["ms_per_dispatch"] * 1e-3) / 1e9
         res.update(traffic_bytes_per_launch=tr["traffic"], traffic_over_algorithmic=tr["ratio"],
-                   traffic_source=tr["source"])
+                   traffic_gbps=tg, traffic_frac_of_peak=tg / PEAK_GBPS, traffic_source=tr["source"])
     else:
         res.update(traffic_bytes_per_launch=None, traffic_source=committed_traffic_reason(name))
     del r
@@ -1283,11 +1285,13 @@ def main(argv=None):
                     frac=nbytes_per_launch / avg_s / 1e9 / PEAK_GBPS, traffic=tr["traffic"] if tr else None,
                     traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                     traffic_over_algorithmic=tr["ratio"] if tr else None,
+                    traffic_gbps=tr["traffic"] / avg_s / 1e9 if tr else None,
+                    traffic_frac=tr["traffic"] / avg_s / 1e9 / PEAK_GBPS if tr else None,
                     traffic_source=tr["source"] if tr else committed_traffic_reason("headline"),
                     kernel=f"rssm::{REPLAY_KERNEL_TAG}", algorithmic_bytes_per_launch=nbytes_per_launch,
                     avg_launch_us=avg_s * 1e6, launches=args.steps)
 
-    groups = set(GROUPS) if args.only == "all" else set() if args.only == "headline" else set(args.only.split(","))
+    groups = set(GROUPS) if args.only == "all" else set(args.only.split(",")) - {"headline"}   # the headline always runs
     unknown = groups - set(GROUPS)
     if unknown:
         print(f"unknown --only groups: {sorted(unknown)}", file=sys.stderr)
