@@ -34,6 +34,7 @@ Auxiliary modes used to make the committed rocprofv3 summaries:
     --profile-variant NAME   W+K untimed dispatches of one variant and the 1 GiB
                              calibration copy (run under rocprofv3 --pmc)
     --pmc-summarize FETCH_DIR WRITE_DIR PROFILE_JSON   two --pmc runs into a summary
+    --sq-summarize PROFILE_JSON PASS_DIR...   SQ instruction-counter passes into a summary
     --stats-summarize STATS_DIR BENCH_JSON   a --kernel-trace --stats run of the default
                              command into a summary
     --precision-sweep        output error of emulated read and recurrence precisions
@@ -1078,6 +1079,49 @@ def _avg_counter(rows, name_pred, counter):
     return sum(per.values()) / len(per), len(per)
 
 
+SQ_SIMDS = 1024          # 256 CUs x 4 SIMDs
+SQ_CLOCK_HZ = 2.4e9
+
+
+def sq_summarize(info_path, dirs, command):
+    """Summary of rocprofv3 --pmc runs of SQ instruction counters (one run per pass, each
+    directory one pass) of one profiled variant: counts per dispatch and per wave, and the
+    time the vector ALUs and the matrix cores would need for them if the work were spread
+    evenly over the chip's 1024 SIMDs (one wave64 vector instruction per 4 cycles at
+    2.4 GHz; matrix-core busy cycles as counted), to set against the kernel's time."""
+    info = json.load(open(info_path))
+    name = info["variant"]
+    out_path = os.path.join(ROOT, "profiles", PMC_FILES[name].replace("_pmc.txt", "_sq.txt"))
+    rows = []
+    for d in dirs:
+        rows.extend(_read_counter_csv(d))
+    is_kernel = lambda n: info["kernel"] in n  # noqa: E731
+    names = sorted({r["Counter_Name"] for r in rows if is_kernel(r.get("Kernel_Name", ""))})
+    avg = {}
+    for c in names:
+        v, n = _avg_counter(rows, is_kernel, c)
+        avg[c] = (v, n)
+    waves = avg.get("SQ_WAVES", (None, 0))[0]
+    lines = [f"# rocprofv3 SQ instruction counters: {name} ({VARIANTS[name][2] if name in VARIANTS else HEADLINE})",
+             f"command: {command}",
+             f"kernel: {info['kernel']}",
+             f"kernel_source_sha256_16: {kernel_source_hash(info['sources'])}",
+             "counter | per dispatch | per wave | dispatches"]
+    for c in names:
+        v, n = avg[c]
+        lines.append(f"{c} | {v:.4g} | {v / waves:.1f} | {n}" if waves else f"{c} | {v:.4g} | - | {n}")
+    if "SQ_INSTS_VALU" in avg:
+        lines.append(f"vector ALU issue time if spread over {SQ_SIMDS} SIMDs: "
+                     f"{avg['SQ_INSTS_VALU'][0] * 4 / SQ_SIMDS / SQ_CLOCK_HZ * 1e6:.1f} us per dispatch")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        lines.append(f"matrix-core busy time if spread over {SQ_SIMDS} SIMDs: "
+                     f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'][0] / SQ_SIMDS / SQ_CLOCK_HZ * 1e6:.1f} us per dispatch")
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def pmc_summarize(fetch_dir, write_dir, info_path, command):
     """Summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of one profiled
     variant, scaled by what the same counters read for the 1 GiB calibration copy."""
@@ -1217,6 +1261,8 @@ def main(argv=None):
                     help="run W+K dispatches of one variant untimed and the calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--profile-out", default=os.path.join("gpurun_out", "profile_variant.json"))
     ap.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROFILE_JSON"))
+    ap.add_argument("--sq-summarize", nargs="+", metavar="PROFILE_JSON PASS_DIR",
+                    help="SQ instruction-counter passes of one profiled variant into a summary")
     ap.add_argument("--pmc-command", default="")
     ap.add_argument("--stats-summarize", nargs=2, metavar=("STATS_DIR", "BENCH_JSON"))
     ap.add_argument("--precision-sweep", action="store_true",
@@ -1228,6 +1274,9 @@ def main(argv=None):
         return 0
     if args.pmc_summarize:
         pmc_summarize(*args.pmc_summarize, args.pmc_command)
+        return 0
+    if args.sq_summarize:
+        sq_summarize(args.sq_summarize[0], args.sq_summarize[1:], args.pmc_command)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the decode path has no cross-GPU exchange); "
