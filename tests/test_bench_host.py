@@ -170,3 +170,35 @@ def test_pmc_summary_from_counter_files(tmp_path, monkeypatch):
     assert tr["traffic"] == pytest.approx(4000.0 * 1024) and tr["ratio"] == pytest.approx(0.8)
     monkeypatch.setattr(bench, "kernel_source_hash", lambda sources=None: "0000000000000000")
     assert bench.committed_traffic("gdn_hv32_conventional") is None
+
+
+def test_sq_summary_from_counter_passes(tmp_path, monkeypatch):
+    """SQ instruction-counter passes of one variant become per-dispatch and per-wave counts
+    and the ALU time they would need spread over the chip's SIMDs."""
+    kern = "rssm::gdn_replay_kernel<128, 128, unsigned short, 2>(rssm::GdnArgs)"
+
+    def write_pass(d, counters):
+        d.mkdir()
+        with open(d / "x_counter_collection.csv", "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for i in range(3):
+                for c, v in counters.items():
+                    # two rows per dispatch and counter (the tool splits some counters): they add up
+                    f.write(f'{i},"{kern}",{c},{v / 2}\n{i},"{kern}",{c},{v / 2}\n')
+            f.write('7,"void other_kernel()",SQ_WAVES,5\n')
+    write_pass(tmp_path / "p1", {"SQ_WAVES": 1000.0, "SQ_INSTS_VALU": 614.4e6 / 1000})
+    write_pass(tmp_path / "p2", {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 2.4e3})
+    info = dict(variant="gdn_spec_hv32_verify", kernel="gdn_replay_kernel<128, 128, unsigned short, 2>",
+                sources=bench.GDN_SOURCES, dispatches=3)
+    ij = tmp_path / "info.json"
+    ij.write_text(bench.json.dumps(info))
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda sources=None: "feedfacefeedface")
+    bench.sq_summarize(str(ij), [str(tmp_path / "p1"), str(tmp_path / "p2")], "cmd")
+    text = (tmp_path / "profiles" / "gdn_spec_verify_hv32_sq.txt").read_text()
+    assert "SQ_WAVES | 1000 | 1.0 | 3" in text
+    assert "SQ_INSTS_VALU | 6.144e+05 | 614.4 | 3" in text
+    # 614400 wave instructions x 4 cycles / 1024 SIMDs / 2.4 GHz = 1.0 us
+    assert "vector ALU issue time if spread over 1024 SIMDs: 1.0 us per dispatch" in text
+    assert "matrix-core busy time if spread over 1024 SIMDs: 1.0 us per dispatch" in text
