@@ -28,7 +28,9 @@ verification (4 positions, commit) against the per-position snapshot baseline, a
 Gated DeltaNet layer (replay decode and conventional; speculative verification against
 its snapshot baseline).  Each variant carries its counter traffic when a matching
 summary is committed.  ``ceiling`` reports the device's streaming limits from the
-hand-written probes (read, in-place read+write, copy).
+hand-written probes (read, in-place read+write, copy, and reads followed by a block of
+writes, which prices writes inside a read stream); ``device_model`` times the headline's
+bytes at those rates and gives the measured steps as a fraction of it.
 
 Auxiliary modes used to make the committed rocprofv3 summaries:
     --profile-variant NAME   W+K untimed dispatches of one variant and the 1 GiB
@@ -104,6 +106,27 @@ def mamba2_replay_bytes(B, H, P, N, G, L, io, c, lowp=False):
     per_h = state + 2 * P * io + io + P * 4 + c * (P * io + 4) + (0 if fold else P * io + 4)
     per_g = 2 * N * io + c * N * io + (0 if fold else N * io)
     return B * H * per_h + B * G * per_g
+
+
+def mamba2_replay_rw(B, H, P, N, G, L, io, c):
+    """The bytes of ``mamba2_replay_bytes`` (fp32 reads) split as (read, written, flushed
+    checkpoint): the last is the part of both that is the checkpoint read and written back
+    in place (0 unless the step folds)."""
+    fold = c + 1 == L
+    ck = P * N * 4
+    rd_h = ck + 2 * P * io + io + c * (P * io + 4)
+    wr_h = P * 4 + (ck if fold else P * io + 4)
+    rd_g = 2 * N * io + c * N * io
+    wr_g = 0 if fold else N * io
+    return B * H * rd_h + B * G * rd_g, B * H * wr_h + B * G * wr_g, (B * H * ck if fold else 0)
+
+
+def step_model_seconds(read, written, inplace, read_bps, inplace_bps, write_seconds):
+    """A step's time at the device's own rates: reads at the read probe's rate, the flushed
+    checkpoint read and written at the in-place probe's rate (bytes read plus written), and
+    every other write at the measured cost of writes inside a read stream
+    (``write_seconds(bytes)``)."""
+    return (read - inplace) / read_bps + 2 * inplace / inplace_bps + write_seconds(written - inplace)
 
 
 def mamba2_conventional_bytes(B, H, P, N, G, io):
@@ -818,7 +841,31 @@ def probe_lib():
     lib.replayssm_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+    lib.replayssm_probe_rtw_read_floats.restype = ctypes.c_int64
+    lib.replayssm_probe_read_then_write.restype = ctypes.c_int
+    lib.replayssm_probe_read_then_write.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                    ctypes.c_int64, ctypes.c_void_p]
     return lib
+
+
+# floats each workgroup of the read-then-write probe stores after reading its 512 KiB
+# (2048 workgroups: 0 to 128 MiB written per launch)
+RTW_WRITE_FLOATS = (0, 256, 512, 1024, 2048, 4096, 16384)
+
+
+def write_cost_seconds(nbytes, points):
+    """Seconds that ``nbytes`` written inside a read stream add, interpolated linearly in
+    the read-then-write probe's (MiB written, seconds) points (the first at 0 MiB; past
+    the last point, its last segment's slope): the cost per byte is not constant -- the
+    first MiB written cost the most."""
+    pts = sorted(points)
+    x = nbytes / MiB
+    x0, t0 = pts[0]
+    for x1, t1 in pts[1:]:
+        if x <= x1 or (x1, t1) == pts[-1]:
+            return (t0 + (t1 - t0) * (x - x0) / (x1 - x0)) - pts[0][1]
+        x0, t0 = x1, t1
+    return 0.0
 
 
 def _median(xs):
@@ -868,6 +915,15 @@ def ceiling(torch, reps=20, repeats=3):
         secs = timed(launch)
         moved = COPY_BYTES * (1 if mode == 0 else 2)
         probes[name] = dict(gbps=moved / secs / 1e9, us=secs * 1e6)
+    # a byte written inside a read stream: the read-then-write probe at several block sizes
+    rtw_grid = n // lib.replayssm_probe_rtw_read_floats()
+    rtw = []
+    for wf in RTW_WRITE_FLOATS:
+        def launch_rtw(wf=wf):
+            st = lib.replayssm_probe_read_then_write(a.data_ptr(), b.data_ptr(), sink.data_ptr(), n, wf, stream)
+            if st:
+                raise RuntimeError(f"read-then-write probe failed with status {st}")
+        rtw.append((rtw_grid * wf * 4 / MiB, timed(launch_rtw)))
     torch_copy = timed(lambda: torch.mul(a, 1.0, out=b))
     torch_inplace = timed(lambda: a.mul_(1.0))
     del a, b, sink
@@ -877,6 +933,9 @@ def ceiling(torch, reps=20, repeats=3):
                 copy_gbps=c[0], copy_probe=c[1], torch_copy_gbps=2 * COPY_BYTES / torch_copy / 1e9,
                 torch_inplace_gbps=2 * COPY_BYTES / torch_inplace / 1e9,
                 probes=probes,
+                read_then_write=dict(written_MiB=[p[0] for p in rtw], us=[p[1] * 1e6 for p in rtw],
+                                     note="1 GiB read in the replay shape (16 tiles of 32 KiB per workgroup), "
+                                          "then a block stored by each workgroup (non-temporal)"),
                 note="hand-written HIP streaming probes (libreplayssm_probes.so), 1 GiB fp32 in [64,128] tiles, "
                      "256 threads, tpw = tiles per workgroup (16: replay decode shape, 1: conventional shape); "
                      "rw GB/s counts read + written bytes; median of 3 timed regions of 20 launches")
@@ -1246,6 +1305,39 @@ def stats_summarize(stats_dir, out_path, command, bench_json):
 
 # ------------------------------------------------------------------------------------
 
+def headline_device_model(synth, ceil, split, head, K):
+    """The headline's steps timed at the device's own rates from this run's probes (see
+    ``step_model_seconds``), against the measured per-step split and timed regions."""
+    w = synth.WORKLOADS[HEADLINE]
+    B, H, P, N, G, L = w["batch"], w["nheads"], w["headdim"], w["dstate"], w["ngroups"], w["buffer_len"]
+    io = 2 if w["io"] == "bf16" else 4
+    read_bps = ceil["read_gbps"] * 1e9
+    inplace_name = "inplace_nt_nt_r8_tpw16"          # the replay kernel's shape
+    inplace_bps = ceil["probes"][inplace_name]["gbps"] * 1e9
+    rtw = ceil["read_then_write"]
+    points = [(m, us * 1e-6) for m, us in zip(rtw["written_MiB"], rtw["us"])]
+    wsec = lambda nbytes: write_cost_seconds(nbytes, points)  # noqa: E731
+    steps = [mamba2_replay_rw(B, H, P, N, G, L, io, c) for c in range(L)]
+    secs = [step_model_seconds(r, wr, ip, read_bps, inplace_bps, wsec) for r, wr, ip in steps]
+    nonflush = sum(secs[:-1]) / (L - 1)
+    flushes = head["flush_dispatches_per_region"]
+    region = (flushes * secs[-1] + (K - flushes) * nonflush) / K
+    window = sum(secs) / L
+    window_bytes = sum(r + wr for r, wr, _ in steps) / L
+    return dict(read_gbps=ceil["read_gbps"], read_probe=ceil["read_probe"], inplace_gbps=inplace_bps / 1e9,
+                inplace_probe=inplace_name,
+                nonflush_written_MiB=steps[0][1] / MiB, nonflush_write_us=wsec(steps[0][1]) * 1e6,
+                nonflush_us=nonflush * 1e6, flush_us=secs[-1] * 1e6, window_us_per_step=window * 1e6,
+                window_frac_of_peak=window_bytes / window / 1e9 / PEAK_GBPS,
+                region_us_per_step=region * 1e6,
+                measured_of_model=dict(nonflush=nonflush * 1e6 / split["nonflush_us"],
+                                       flush=secs[-1] * 1e6 / split["flush_us"],
+                                       region=region * 1e3 / head["ms_per_dispatch"]),
+                note="reads at the best read probe, the flushed checkpoint at the in-place probe in the "
+                     "replay kernel's shape, other writes at the read-then-write probe's extra time for "
+                     "their volume")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1362,6 +1454,7 @@ def main(argv=None):
         if not cpu["gpu_parity_ok"]:
             raise RuntimeError(f"GPU outputs disagree with the oracle: {cpu['gpu_parity_max_violation']}")
 
+    model = headline_device_model(synth, ceil, split, head, args.steps) if ceil else None
     conv = variants.get("mamba2_h128_conventional")
     ratios = {}
     pairs = [("mamba2_h128", None, "mamba2_h128_conventional"),
@@ -1413,6 +1506,7 @@ def main(argv=None):
         "replay_vs_conventional": ratios,
         "variants": variants,
         "ceiling": ceil,
+        "device_model": model,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -23,6 +23,11 @@
 //                  workgroups in flight sit at different offsets of their regions
 //   2 interleaved: workgroup w's tile t is tile t G + w (G workgroups), so that the
 //                  workgroups in flight together touch one compact stretch of memory
+//
+// A second probe reads in the replay kernels' shape (16 tiles of [64, 128] per workgroup,
+// non-temporal) and then stores a block of its own, as the decode kernels store their
+// outputs and records after streaming the checkpoint; timed at several block sizes against
+// the same stream with no block, it prices a byte written inside a read stream.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -136,6 +141,38 @@ static const void* pick(int tpw, int mode, bool ntl, bool nts, int order) {
     return tpw == 1 ? pick_mode<R, 1, 0>(mode, ntl, nts) : pick_tpw<R, 0>(tpw, mode, ntl, nts);
 }
 
+__global__ void __launch_bounds__(kThreads) read_then_write_kernel(const float* src, float* dst, float* sink,
+                                                                    int64_t write_floats) {
+    constexpr int kR = 8, kTpw = 16;
+    constexpr int64_t kTileFloats = kR * kPassFloats;
+    const int tid = threadIdx.x;
+    const int64_t lane_off = (int64_t)(tid / kLpr) * kCols + 4 * (tid % kLpr);
+    const float* base = src + (int64_t)blockIdx.x * kTpw * kTileFloats + lane_off;
+    v4f va[kR], vb[kR];
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kR; ++k) va[k] = load4<true>(base + (int64_t)k * kRpp * kCols);
+    for (int t = 0; t + 1 < kTpw; ++t) {
+#pragma unroll
+        for (int k = 0; k < kR; ++k) vb[k] = load4<true>(base + (int64_t)(t + 1) * kTileFloats + (int64_t)k * kRpp * kCols);
+#pragma unroll
+        for (int k = 0; k < kR; ++k) acc += va[k];
+#pragma unroll
+        for (int k = 0; k < kR; ++k) va[k] = vb[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kR; ++k) acc += va[k];
+    // the block depends on every value read, like the decode kernels' outputs
+    float* d = dst + (int64_t)blockIdx.x * write_floats;
+    for (int64_t i = 4 * (int64_t)tid; i < write_floats; i += 4 * kThreads) store4<true>(d + i, acc);
+    __shared__ float part[kThreads / 64];
+    float s = acc.x + acc.y + acc.z + acc.w;
+    for (int dd = 32; dd >= 1; dd >>= 1) s += __shfl_xor(s, dd);
+    if ((tid & 63) == 0) part[tid / 64] = s;
+    __syncthreads();
+    if (tid == 0) sink[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
 }  // namespace rssm_probe
 
 extern "C" {
@@ -176,6 +213,32 @@ int replayssm_probe_stream(const float* src, float* dst, float* sink, int64_t n_
                                           : pick<8>(tiles_per_wg, mode, ntl, nts, order);
     void* args[] = {(void*)&src, (void*)&dst, (void*)&sink, (void*)&scale};
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), args, 0, stream);
+    return e == hipSuccess ? 0 : 3;
+}
+
+// Floats one workgroup of the read-then-write probe reads (16 tiles of [64, 128]).
+int64_t replayssm_probe_rtw_read_floats(void) { return rssm_probe::kPassFloats * 8 * 16; }
+
+// One launch of the read-then-write probe on `stream`.
+//   src           device f32 [n_floats], 16-byte aligned; n_floats > 0 and a multiple of
+//                 replayssm_probe_rtw_read_floats() (the grid is n_floats / that)
+//   dst           device f32 [grid * write_floats], 16-byte aligned; may be null when
+//                 write_floats is 0
+//   sink          device f32 [grid] (one sum per workgroup)
+//   write_floats  floats each workgroup stores after its reads: >= 0, a multiple of 4
+// Returns 0 on success, 1 for an invalid argument (nothing launched), 3 when the launch failed.
+int replayssm_probe_read_then_write(const float* src, float* dst, float* sink, int64_t n_floats,
+                                    int64_t write_floats, hipStream_t stream) {
+    using namespace rssm_probe;
+    const int64_t per_wg = replayssm_probe_rtw_read_floats();
+    if (!src || (reinterpret_cast<uintptr_t>(src) & 15) || !sink || n_floats <= 0 || n_floats % per_wg) return 1;
+    if (write_floats < 0 || write_floats % 4) return 1;
+    if (write_floats > 0 && (!dst || (reinterpret_cast<uintptr_t>(dst) & 15))) return 1;
+    const int64_t grid = n_floats / per_wg;
+    if (grid > INT32_MAX) return 1;
+    void* args[] = {(void*)&src, (void*)&dst, (void*)&sink, (void*)&write_floats};
+    const hipError_t e = hipLaunchKernel((const void*)&read_then_write_kernel, dim3((unsigned)grid), dim3(kThreads),
+                                         args, 0, stream);
     return e == hipSuccess ? 0 : 3;
 }
 

@@ -283,3 +283,25 @@ def test_probe_library_rejects_invalid_arguments_before_launching():
                 dict(mode=3), dict(mode=-1), dict(mode=0, sink=0), dict(mode=1, dst=0), dict(mode=2, dst=dst + 8),
                 dict(order=3), dict(order=1, tpw=1, n=pf * 8)):
         assert call(**bad) == 1, bad
+
+
+def test_read_then_write_probe_rejects_invalid_arguments_before_launching():
+    """The read-then-write probe reads 16 tiles of [64, 128] fp32 per workgroup; each
+    invalid argument returns 1 before anything is launched (fake pointers)."""
+    import bench
+    if not os.path.exists(bench.PROBE_LIB):
+        from hybrid_model_ssm_amd import build
+        build.build()
+    P = bench.probe_lib()
+    per_wg = P.replayssm_probe_rtw_read_floats()
+    assert per_wg == 64 * 128 * 16
+    src, dst, sink = 0x100000, 0x200000, 0x300000
+
+    def call(**kw):
+        a = dict(src=src, dst=dst, sink=sink, n=per_wg, wf=1024)
+        a.update(kw)
+        return P.replayssm_probe_read_then_write(a["src"], a["dst"], a["sink"], a["n"], a["wf"], None)
+
+    for bad in (dict(src=0), dict(src=src + 4), dict(sink=0), dict(n=0), dict(n=per_wg + 4), dict(wf=-1024),
+                dict(wf=1022), dict(dst=0), dict(dst=dst + 8)):
+        assert call(**bad) == 1, bad

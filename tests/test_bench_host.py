@@ -202,3 +202,34 @@ def test_sq_summary_from_counter_passes(tmp_path, monkeypatch):
     # 614400 wave instructions x 4 cycles / 1024 SIMDs / 2.4 GHz = 1.0 us
     assert "vector ALU issue time if spread over 1024 SIMDs: 1.0 us per dispatch" in text
     assert "matrix-core busy time if spread over 1024 SIMDs: 1.0 us per dispatch" in text
+
+
+def test_headline_byte_split_adds_up():
+    # reads plus writes are the byte model's total at every cursor; only the folding step
+    # moves the checkpoint in place, 1 GiB each way
+    for c in range(16):
+        rd, wr, ip = bench.mamba2_replay_rw(256, 128, 64, 128, 8, 16, 2, c)
+        assert rd + wr == bench.mamba2_replay_bytes(256, 128, 64, 128, 8, 16, 2, c)
+        assert ip == (1 << 30 if c == 15 else 0)
+    rd, wr, _ = bench.mamba2_replay_rw(256, 128, 64, 128, 8, 16, 2, 0)
+    assert wr == 256 * 128 * (64 * 4 + 64 * 2 + 4) + 256 * 8 * 128 * 2     # outputs and the appended records
+
+
+def test_step_model_at_the_measured_rates():
+    # reads at 7.12 TB/s, the flushed checkpoint at 5.52 TB/s, other writes at 0.65 us/MiB:
+    # 160.3 us at cursor 0, 405.8 us for the flush, 180.2 us per step over a window
+    wsec = lambda nbytes: nbytes / MiB * 0.65e-6  # noqa: E731
+    secs = [bench.step_model_seconds(*bench.mamba2_replay_rw(256, 128, 64, 128, 8, 16, 2, c), 7.12e12, 5.52e12, wsec)
+            for c in range(16)]
+    assert secs[0] * 1e6 == pytest.approx(160.3, abs=0.1)
+    assert secs[15] * 1e6 == pytest.approx(405.8, abs=0.1)
+    assert sum(secs) / 16 * 1e6 == pytest.approx(180.2, abs=0.1)
+
+
+def test_write_cost_interpolates_the_probe_points():
+    pts = [(0.0, 1.0e-4), (8.0, 1.12e-4), (32.0, 1.22e-4), (128.0, 1.58e-4)]
+    assert bench.write_cost_seconds(0, pts) == 0.0
+    assert bench.write_cost_seconds(4 * MiB, pts) == pytest.approx(6.0e-6)          # half of the first segment
+    assert bench.write_cost_seconds(20 * MiB, pts) == pytest.approx(1.7e-5)         # within the second
+    assert bench.write_cost_seconds(256 * MiB, pts) == pytest.approx(1.06e-4)       # past the last: its slope
+    assert bench.write_cost_seconds(4 * MiB, list(reversed(pts))) == pytest.approx(6.0e-6)   # any order
