@@ -31,6 +31,7 @@ constexpr int kGdnFold = 1;
 constexpr int kGdnSpec = 2;
 constexpr int kGdnMaxVHeads = 4;   // value heads per workgroup
 constexpr int kGdnFoldChunk = 16;  // records folded together in matrix form
+constexpr int kGdnXStride = 36;     // floats per row of a wave's exchange buffer (32 + 4 against bank conflicts)
 constexpr size_t kGdnMaxSmemBytes = 64 * 1024;
 
 template <int DK>
@@ -45,7 +46,7 @@ struct GdnShape {
 // records plus this call's positions), T1 the positions.
 struct GdnSmem {
     int NR, T1, oK, oV, oAl, oBe, oQ, oU, oAcc;
-    int oGr, oNm, oGW, oDd, oDc, total;
+    int oGr, oNm, oGW, oDd, oDc, oX, total;
     __host__ __device__ GdnSmem(int DK, int DV, int L, int T, int mode, int NV, int io_bytes) {
         NR = (mode == kGdnSpec) ? L + T : L;
         T1 = T > 1 ? T : 1;
@@ -63,7 +64,8 @@ struct GdnSmem {
         oGW = oNm + NV * L * CH;                   // [NV][L][CH]   G (I + Nm)^-1 of each chunk
         oDd = oGW + NV * L * CH;                   // [NV][L]       a_s beta_s prod_{u<s} a_u
         oDc = oDd + NV * L;                        // [NV][L/CH+1]  decay of each chunk
-        total = oDc + NV * (L / CH + 1);
+        oX = (oDc + NV * (L / CH + 1) + 3) & ~3;   // [4 waves][16][36]  fold tiles' re-layout (16-byte aligned)
+        total = oX + 4 * 16 * kGdnXStride;
     }
 };
 
@@ -81,8 +83,14 @@ struct GdnSmem {
 //               window row s < committed is ring slot (head + s) % L, row committed + j
 //               is position j; if committed + n_pos > L the committed rows are folded
 //               first and every position's chain starts after them.
+//
+// Waves per SIMD: decode steps hold three (a flush step's fold re-lays its tiles through
+// LDS, which fits in registers only at that occupancy, and the flush steps gain more than
+// the others lose), speculative rounds four (their workgroups are shorter and need the
+// occupancy more than a few spilled registers cost), the explicit fold is unbounded.
 template <int DK, int DV, typename IO, int MODE>
-__global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_replay_kernel(GdnArgs a) {
+__global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : (MODE == kGdnDecode ? 3 : 4))
+gdn_replay_kernel(GdnArgs a) {
     using io = Io<IO>;
     using Raw4 = typename io::Raw4;
     using S = GdnShape<DK>;
@@ -184,19 +192,57 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_rep
 #pragma unroll
         for (int k = 0; k < R; ++k) v[k] = ld_stream(a.ckpt + t + (size_t)k * RPP * DK);
     };
-    // Fold steps hold a tile in the lane mapping of the 16x16x4 matrix instructions:
-    // wave w takes rows 16w..16w+15 of the 64, lane l row 16w + (l & 15) and, in each
-    // 16-column block cb, columns 16cb + 4(l >> 4) .. +3 (R = DK/16 blocks).
+    // Fold steps compute on a tile in the lane mapping of the 16x16x4 matrix
+    // instructions: wave w takes rows 16w..16w+15 of the 64, lane l row 16w + (l & 15)
+    // and, in each 16-column block cb, columns 16cb + 4(l >> 4) .. +3 (R = DK/16 blocks).
+    // That mapping touches 64 bytes of 16 rows per access, which streams 10-12% slower
+    // than whole 128-byte lines, so fold tiles move in a chunk mapping instead -- registers
+    // 2cc and 2cc+1 hold 32-column chunk cc of the wave's rows 0-7 and 8-15, lane l row
+    // (l >> 3) of the eight and columns 32cc + 4(l & 7) .. +3, eight lanes a line -- and are
+    // re-laid between the two through a buffer of the wave's own in LDS, one chunk (the
+    // same two registers in both mappings) at a time.
     const int fr = lane & 15, fg = lane >> 4;
     static_assert(R * 16 == DK, "fold mapping: one 16-column block per tile register");
-    auto tile_base_f = [&](int u) -> size_t {
+    constexpr int NCC = DK / 32;                      // 32-column chunks
+    float* sX = smem + lay.oX + wave * 16 * kGdnXStride;
+    // a lane's accesses to a fold tile, from one address between its two row halves (row
+    // 16w + 4 + (l >> 3), column 4 (l & 7)): every access is then that address plus a
+    // constant that fits the instructions' offset field
+    auto tile_mid_c = [&](int u) -> const float* {
         const int vl = u / NTILE, tl = u % NTILE;
-        return ((sHV + hv0 + vl) * DV + tl * DVT + 16 * wave + fr) * (size_t)DK + 4 * fg;
+        return a.ckpt + ((sHV + hv0 + vl) * DV + tl * DVT + 16 * wave + 4 + (lane >> 3)) * (size_t)DK + 4 * (lane & 7);
     };
     auto issue_tile_f = [&](int u, float4 (&v)[R]) {
-        const size_t t = tile_base_f(u);
+        const float* m = tile_mid_c(u);
 #pragma unroll
-        for (int k = 0; k < R; ++k) v[k] = ld_stream(a.ckpt + t + 16 * k);
+        for (int cc = 0; cc < NCC; ++cc) {
+            v[2 * cc] = ld_stream(m - 4 * DK + 32 * cc);
+            v[2 * cc + 1] = ld_stream(m + 4 * DK + 32 * cc);
+        }
+    };
+    // chunk mapping -> matrix mapping, in place (the wave's LDS accesses run in order, so
+    // a chunk's reads come back before the next chunk's writes land)
+    auto to_matrix = [&](float4 (&v)[R]) {
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) {
+            *reinterpret_cast<float4*>(sX + (lane >> 3) * kGdnXStride + 4 * (lane & 7)) = v[2 * cc];
+            *reinterpret_cast<float4*>(sX + (8 + (lane >> 3)) * kGdnXStride + 4 * (lane & 7)) = v[2 * cc + 1];
+            v[2 * cc] = *reinterpret_cast<const float4*>(sX + fr * kGdnXStride + 4 * fg);
+            v[2 * cc + 1] = *reinterpret_cast<const float4*>(sX + fr * kGdnXStride + 16 + 4 * fg);
+        }
+    };
+    // matrix mapping -> chunk mapping, in place, each chunk then stored as whole lines
+    auto store_tile_f = [&](int u, float4 (&v)[R]) {
+        float* m = const_cast<float*>(tile_mid_c(u));
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) {
+            *reinterpret_cast<float4*>(sX + fr * kGdnXStride + 4 * fg) = v[2 * cc];
+            *reinterpret_cast<float4*>(sX + fr * kGdnXStride + 16 + 4 * fg) = v[2 * cc + 1];
+            v[2 * cc] = *reinterpret_cast<const float4*>(sX + (lane >> 3) * kGdnXStride + 4 * (lane & 7));
+            v[2 * cc + 1] = *reinterpret_cast<const float4*>(sX + (8 + (lane >> 3)) * kGdnXStride + 4 * (lane & 7));
+            st_stream(m - 4 * DK + 32 * cc, v[2 * cc]);
+            st_stream(m + 4 * DK + 32 * cc, v[2 * cc + 1]);
+        }
     };
     const int nunit = nv * NTILE;
     float4 va[R], vb[R];
@@ -531,6 +577,7 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_rep
             const int vl = u / NTILE, tl = u % NTILE;
             const int i = tl * DVT + 16 * wave + fr;          // this lane's row of the value head
             const float* be = sBe + vl * NR;
+            to_matrix(va);
             for (int ch = 0; ch < nch; ++ch) {
                 const int s0 = ch * CH, nc = min(CH, nf - s0);
                 // w[s][row] = k_s . row for the chunk's records s < 16 (rows past nc read as
@@ -575,10 +622,8 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_rep
                     va[cb] = make_float4(acc[0], acc[1], acc[2], acc[3]);
                 }
             }
-            const size_t tb = tile_base_f(u);
-#pragma unroll
-            for (int k = 0; k < R; ++k) st_stream(a.ckpt + tb + 16 * k, va[k]);
-            // outputs from the new rows: each row is spread over the 4 lanes l, l^16, l^32, l^48
+            // outputs from the new rows (each row is spread over the 4 lanes l, l^16, l^32,
+            // l^48), then the rows go back to the chunk mapping and are stored
             if constexpr (MODE != kGdnFold) {
                 for (int j = 0; j < Tb; ++j) {
                     float part = 0.f;
@@ -590,6 +635,7 @@ __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : 4) gdn_rep
                     if (fg == 0) sAcc[(vl * T1 + j) * DV + i] = scale * (part + sAcc[(vl * T1 + j) * DV + i]);
                 }
             }
+            store_tile_f(u, va);
         };
         for (int u = 0; u + 2 < nunit; ++u) {
             body(u);
