@@ -87,7 +87,7 @@ struct GdnSmem {
 // Waves per SIMD: decode steps hold three (a flush step's fold re-lays its tiles through
 // LDS, which fits in registers only at that occupancy, and the flush steps gain more than
 // the others lose), speculative rounds four (their workgroups are shorter and need the
-// occupancy more than a few spilled registers cost), the explicit fold is unbounded.
+// occupancy), the explicit fold is unbounded.
 template <int DK, int DV, typename IO, int MODE>
 __global__ void __launch_bounds__(kGdnThreads, MODE == kGdnFold ? 1 : (MODE == kGdnDecode ? 3 : 4))
 gdn_replay_kernel(GdnArgs a) {
@@ -99,9 +99,11 @@ gdn_replay_kernel(GdnArgs a) {
     constexpr int UPL = DK / kWave;  // u elements per lane in a carry-back wave
     constexpr int DK4 = DK / 4, DV4 = DV / 4;
     constexpr int NWAVE = kGdnThreads / kWave;
-    // chains a wave runs in lockstep, and positions reduced together per tile
+    // chains a wave runs in lockstep, and positions reduced together per tile (one: two
+    // at a time spill registers in speculative rounds, which costs more than the extra
+    // reductions)
     constexpr int TC = (MODE == kGdnSpec) ? 2 : 1;
-    constexpr int TB = (MODE == kGdnSpec) ? (LPR / R >= 2 ? 2 : 1) : 1;
+    constexpr int TB = 1;
     extern __shared__ float smem[];
 
     const int tid = threadIdx.x;
