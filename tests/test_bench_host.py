@@ -233,3 +233,21 @@ def test_write_cost_interpolates_the_probe_points():
     assert bench.write_cost_seconds(20 * MiB, pts) == pytest.approx(1.7e-5)         # within the second
     assert bench.write_cost_seconds(256 * MiB, pts) == pytest.approx(1.06e-4)       # past the last: its slope
     assert bench.write_cost_seconds(4 * MiB, list(reversed(pts))) == pytest.approx(6.0e-6)   # any order
+
+
+def test_headline_device_model_from_probe_numbers():
+    """The bench line's device model, from a ceiling section shaped like the probes' output
+    (reads 7.12 TB/s, in place 5.52 TB/s in the replay shape, 0.65 us per MiB written) and a
+    measured split: the window average is the 180.2 us of the hand calculation."""
+    from hybrid_model_ssm_amd import synth
+    ceil = dict(read_gbps=7120.0, read_probe="read_nt_r8_tpw4",
+                probes={"inplace_nt_nt_r8_tpw16": dict(gbps=5520.0, us=0.0)},
+                read_then_write=dict(written_MiB=[0.0, 128.0], us=[150.0, 150.0 + 128 * 0.65]))
+    split = dict(nonflush_us=175.0, flush_us=413.0)
+    head = dict(flush_dispatches_per_region=2, ms_per_dispatch=0.2)
+    m = bench.headline_device_model(synth, ceil, split, head, 20)
+    assert m["window_us_per_step"] == pytest.approx(180.2, abs=0.1)
+    assert m["flush_us"] == pytest.approx(405.8, abs=0.1)
+    assert m["region_us_per_step"] == pytest.approx((2 * m["flush_us"] + 18 * m["nonflush_us"]) / 20)
+    assert m["measured_of_model"]["flush"] == pytest.approx(405.8 / 413.0, abs=1e-3)
+    assert 0.8 < m["window_frac_of_peak"] < 0.84
