@@ -98,9 +98,10 @@ struct GroupSmem {
 };
 
 // LP: kind of low-precision read copy (kLpNone, kLpBF16, kLpF16, kLpFP8).  Decode steps
-// that read a copy stream half or a quarter of the fp32 bytes per tile, keep two copy
-// tiles in flight and are held to three waves per SIMD (the register budget of those three
-// buffers without spills); the other instances keep the budget the compiler picks.
+// that read a copy stream half or a quarter of the fp32 bytes per tile, keep two (bf16,
+// fp16) or three (fp8) copy tiles in flight, request the first tiles before the prologue,
+// and are held to three waves per SIMD (the register budget of those buffers without
+// spills); the other instances keep the budget the compiler picks.
 template <int P, int N, typename IO, int LP, int MODE>
 __global__ void __launch_bounds__(kThreads, (LP != kLpNone && MODE == kDecode) ? 3 : 1)
 mamba2_replay_kernel(Mamba2Args a) {
@@ -317,10 +318,19 @@ mamba2_replay_kernel(Mamba2Args a) {
     const float preD = (MODE != kFold) ? a.D[h0 + min(tid, nh - 1)] : 0.f;
 
     float4 va[R], vb[R];
-    uint4 qa[RQ], qb[RQ];
-    float sqa = 0.f, sqb = 0.f;
-    if (use_lp) issue_tile_lp(0, qa, sqa);
-    else issue_tile(0, va);
+    // copy tiles: NQ buffers in fixed roles; in decode steps the first NQ heads are
+    // requested before the prologue so that they stream while the window is staged (the
+    // speculative instance would lose a wave per SIMD holding them)
+    constexpr int NQ = (LP == kLpFP8 && MODE == kDecode) ? 4 : 3;
+    constexpr int NQE = (MODE == kDecode) ? NQ : 1;
+    uint4 qr[NQ][RQ];
+    float sqr[NQ];
+    if (use_lp) {
+#pragma unroll
+        for (int u = 0; u < NQE; ++u) issue_tile_lp(min(u, nh - 1), qr[u], sqr[u]);
+    } else {
+        issue_tile(0, va);
+    }
     if (fold && !idle) issue_foldx(0);
 
     // this call's records, loaded now and stored after every head has read the ring
@@ -589,41 +599,39 @@ mamba2_replay_kernel(Mamba2Args a) {
         }
     };
 
-    if (!fold && use_lp && nh >= 3) {
-        // copy tiles are small: heads hl+1 and hl+2 stream while head hl is reduced.  Three
-        // buffers in fixed roles (unrolled by three): a register copy of a tile still in
-        // flight would wait for it.
-        uint4 qc[RQ];
-        float sqc = 0.f;
-        issue_tile_lp(1, qb, sqb);
-        issue_tile_lp(2, qc, sqc);
-        int hl = 0;
-        for (; hl + 5 < nh; hl += 3) {
-            outputs_lp(hl, qa, sqa);
-            issue_tile_lp(hl + 3, qa, sqa);
-            outputs_lp(hl + 1, qb, sqb);
-            issue_tile_lp(hl + 4, qb, sqb);
-            outputs_lp(hl + 2, qc, sqc);
-            issue_tile_lp(hl + 5, qc, sqc);
-        }
-        const int rest = nh - hl;       // 3, 4 or 5 heads remain
-        outputs_lp(hl, qa, sqa);
-        if (rest > 3) issue_tile_lp(hl + 3, qa, sqa);
-        outputs_lp(hl + 1, qb, sqb);
-        if (rest > 4) issue_tile_lp(hl + 4, qb, sqb);
-        outputs_lp(hl + 2, qc, sqc);
-        if (rest > 3) outputs_lp(hl + 3, qa, sqa);
-        if (rest > 4) outputs_lp(hl + 4, qb, sqb);
-    } else if (!fold && use_lp) {
-        // one or two heads: tile hl+1 is loaded while head hl is reduced
-        for (int hl = 0; hl + 1 < nh; ++hl) {
-            issue_tile_lp(hl + 1, qb, sqb);
-            outputs_lp(hl, qa, sqa);
+    if (!fold && use_lp && nh >= NQ) {
+        // copy tiles are small: heads hl+1 .. hl+NQ-1 stream while head hl is reduced.
+        // The buffers keep fixed roles (the loop is unrolled by NQ): a register copy of a
+        // tile still in flight would wait for it.
 #pragma unroll
-            for (int k = 0; k < RQ; ++k) qa[k] = qb[k];
-            sqa = sqb;
+        for (int u = NQE; u < NQ; ++u) issue_tile_lp(u, qr[u], sqr[u]);
+        int hl = 0;
+        for (; hl + 2 * NQ - 1 < nh; hl += NQ) {
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) {
+                outputs_lp(hl + u, qr[u], sqr[u]);
+                issue_tile_lp(hl + u + NQ, qr[u], sqr[u]);
+            }
         }
-        outputs_lp(nh - 1, qa, sqa);
+        const int rest = nh - hl;       // NQ .. 2 NQ - 1 heads remain
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            outputs_lp(hl + u, qr[u], sqr[u]);
+            if (u + NQ < rest) issue_tile_lp(hl + u + NQ, qr[u], sqr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < NQ - 1; ++u)
+            if (u + NQ < rest) outputs_lp(hl + NQ + u, qr[u], sqr[u]);
+    } else if (!fold && use_lp) {
+        // fewer heads than buffers: tile hl+1 is loaded while head hl is reduced
+        for (int hl = 0; hl + 1 < nh; ++hl) {
+            issue_tile_lp(hl + 1, qr[1], sqr[1]);
+            outputs_lp(hl, qr[0], sqr[0]);
+#pragma unroll
+            for (int k = 0; k < RQ; ++k) qr[0][k] = qr[1][k];
+            sqr[0] = sqr[1];
+        }
+        outputs_lp(nh - 1, qr[0], sqr[0]);
     } else if (!fold) {
         // tile hl+1 is loaded while head hl is reduced
         for (int hl = 0; hl + 1 < nh; ++hl) {
