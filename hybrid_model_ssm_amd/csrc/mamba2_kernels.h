@@ -1,12 +1,12 @@
 // Mamba2 ReplaySSM kernels for gfx950.
 //
 // The method ("ReplaySSM Caches Inputs Instead of State to Speed Up Hybrid-Model
-// Decoding", section "How ReplaySSM works"): the state is a checkpoint plus a buffer of
-// recent input records.  A non-flush step appends its record and computes the output
-// from the checkpoint and the buffer without storing a state; the step that fills the
-// buffer folds the records into the checkpoint and stores it once.  Unrolling the
-// Mamba2 recurrence h = exp(dt A) h + dt x B^T over a window of records s (oldest
-// first) gives, with lam_s = sum of dt over the window records after s:
+// Decoding", section "How ReplaySSM works"): the state is held as a checkpoint and a
+// ring of the latest input records.  On a non-flush step the record is appended and y
+// is evaluated from the checkpoint plus the records, with no state written back; the
+// step that fills the buffer merges the records into the checkpoint, written once per
+// window.  Unrolling the Mamba2 recurrence h = exp(dt A) h + dt x B^T over a window of
+// records s (oldest first) gives, with lam_s = sum of dt over the window records after s:
 //
 //     decay = exp(A * sum_s dt_s),   w_s = dt_s * exp(A * lam_s)
 //     y     = decay * (Hc . C_t) + sum_s w_s (B_s . C_t) x_s + D x_t

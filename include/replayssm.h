@@ -4,9 +4,9 @@
  * ReplaySSM keeps the recurrent state of a state-space (SSM) layer as a checkpoint
  * plus a bounded buffer of recent input records ("ReplaySSM Caches Inputs Instead of
  * State to Speed Up Hybrid-Model Decoding", section "How ReplaySSM works").  On a
- * non-flush step the kernel appends the step's record and computes the output from
- * the checkpoint and the buffer without storing a state; when the buffer of L
- * records fills, the flush step folds the records into the checkpoint and stores it
+ * non-flush step the kernel appends the step's record and evaluates the output from
+ * the checkpoint plus the stored records, writing no state back; the step that brings
+ * the buffer to L records merges them into the checkpoint, which it writes back
  * once.  Speculative verification appends draft records and is output-only; rollback
  * moves a cursor ("ReplaySSM" README, benefit "Cheap rollback").  An optional
  * low-precision read copy of the checkpoint (bf16, fp16 or fp8) serves non-flush reads
@@ -143,9 +143,9 @@ typedef struct {
 
 /*
  * One autoregressive decode step, output-only route ("How ReplaySSM works":
- * non-flush steps append the inputs and compute the output from the checkpoint
- * and the buffer without storing a state; the step that fills the buffer folds
- * it into the checkpoint and stores the checkpoint once).
+ * non-flush steps append their inputs and evaluate the output from the checkpoint
+ * plus the records, with no state written; the step that fills the buffer merges
+ * the records into the checkpoint and writes it back once).
  *
  * For every sequence b with c = cursor_in[b] (0 <= c < L):
  *   window = the c stored records followed by this step's record (x_t, B_t, dt_t);
@@ -273,8 +273,8 @@ replayssm_status replayssm_reset_cursors(int32_t batch, int32_t* head, int32_t* 
 
 /*
  * Conventional read-update-write decode step, the baseline the method is measured
- * against ("Why SSM layers slow down hybrid models": each step loads and stores the
- * full state).  state f32 [batch, nheads, headdim, dstate] is updated in place:
+ * against ("Why SSM layers slow down hybrid models": every step reads the whole state
+ * from HBM and writes it back).  state f32 [batch, nheads, headdim, dstate] is updated in place:
  *   h = exp(dt*A) h + dt outer(x, B);  y = h . C + D x;  out = y * z * sigmoid(z).
  * desc->buffer_len is ignored.  Other arguments as in replayssm_mamba2_decode.
  */
@@ -286,8 +286,8 @@ replayssm_status replayssm_selective_state_update(const replayssm_mamba2_desc* d
 
 /*
  * Conventional speculative baseline: one state snapshot per position ("Why SSM
- * layers slow down hybrid models": engines store a snapshot after every draft
- * token, one read and T writes per step).  Reads snapshot slot_in[b] of
+ * layers slow down hybrid models": engines keep the state after every draft token,
+ * so a verify step reads one state and writes T of them).  Reads snapshot slot_in[b] of
  * snapshots f32 [batch, n_pos, nheads, headdim, dstate], runs the n_pos updates in
  * order and writes the state after position j into slot j; outputs as
  * replayssm_mamba2_spec_verify.  The next round passes slot_in[b] = n_keep[b] - 1.

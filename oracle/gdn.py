@@ -12,8 +12,8 @@ with a state ``S`` of shape ``[dv, dk]`` per value head::
 
 Value head ``hv`` reads the q/k head ``hv // (HV // HK)``.
 
-Replay form ("How ReplaySSM works": keep a checkpoint and a buffer of records,
-compute the output without storing a state, fold the buffer into the
+Replay form ("How ReplaySSM works": a checkpoint and a buffer of records,
+outputs evaluated with no state written back, the records merged into the
 checkpoint once per window).  Writing ``M_s = alpha_s (I - beta_s k_s k_s^T)``,
 ``S_t = S_ckpt M_1 ... M_t + sum_s beta_s v_s k_s^T M_{s+1} ... M_t``, so::
 

@@ -15,11 +15,11 @@ Three pieces, each written from its source and kept separate from the others:
 
   ``B`` and ``C`` belong to the group ``g = h // (nheads // ngroups)``.
 
-* ``Mamba2Replay`` -- the replay form ("How ReplaySSM works"): a checkpoint plus
-  a buffer of recent input records.  Each step appends its record and computes
-  the output from the checkpoint and the buffer without storing a state; when
-  the buffer holds L records the records are folded into the checkpoint, the
-  checkpoint is stored once and the buffer is cleared.  Unrolling the
+* ``Mamba2Replay`` -- the replay form ("How ReplaySSM works"): the state held as
+  a checkpoint and a ring of the latest input records.  Each step appends its record and evaluates
+  y from the checkpoint plus the records, writing no state back; once the
+  buffer holds L records they are merged into the checkpoint, which is written
+  once, and the buffer starts empty again.  Unrolling the
   recurrence over the window (records ``s`` oldest first, the current step
   last) gives, with ``lam_s = sum of dt_r over the records after s``::
 
