@@ -127,6 +127,15 @@ def test_decode_reads_the_copy_within_its_rounding(kind):
     _run(kind)
 
 
+# heads per workgroup that take every path of the copy-tile ring: fewer heads than
+# buffers, the unrolled loop, and each count of heads left for its tail (3 buffers for
+# bf16 and fp16, 4 for fp8)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("heads", [3, 5, 6, 7, 11, 13])
+def test_copy_ring_heads_per_workgroup(kind, heads):
+    _run(kind, B=2, H=heads, P=64, N=128, G=1, L=4, seed=64 + heads)
+
+
 @pytest.mark.parametrize("shape", [(2, 4, 64, 16, 1, 4), (2, 4, 128, 64, 2, 5), (2, 4, 32, 256, 2, 4)],
                          ids=lambda s: "P{}N{}".format(s[2], s[3]))
 def test_fp8_copy_other_tile_shapes(shape):
