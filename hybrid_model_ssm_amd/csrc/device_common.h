@@ -189,33 +189,36 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Longest-first order of the sequences of a speculative round.  A round folds the
-// buffer of some sequences only (committed + positions > L), and their workgroups run
-// much longer than the rest.  Every workgroup computes the same permutation of the
-// batch -- the folding sequences first, then the others, each part in batch order --
-// and takes the sequence at position `rank`.  The hardware starts workgroups in id
-// order, so the long ones start first and the short ones fill the gaps they leave,
-// instead of a few long ones running alone at the end of the launch.
+// Order of the sequences of a speculative round.  A round folds the buffer of some
+// sequences only (committed + positions > L); their workgroups run much longer than the
+// rest and write their checkpoint in place.  Every workgroup computes the same
+// permutation of the batch -- the first lead_num/lead_den of the other sequences, then
+// the folding ones, then the rest of the others, each part in batch order -- and takes
+// the sequence at position `rank`.  The hardware starts workgroups in id order, so the
+// folding workgroups start once the reading ones stream and end while the last reading
+// ones still keep the memory busy.  Folding first makes their writes share the whole
+// launch with reads and, in GDN rounds, their fold preparation coincide with the
+// launch's start; folding last leaves them to run alone at the end.
 //
 // Each thread loads the cursors of one sequence (all loads issued together, so a
 // batch of up to NT sequences costs the one global round trip that loading this
 // workgroup's own cursors costs anyway); the thread holding the chosen sequence hands
 // its cursors to the workgroup through LDS.  Every workgroup reads every sequence's
-// cursors, so batches above kHeavyFirstMaxBatch keep batch order (the work would grow
+// cursors, so batches above kRankedMaxBatch keep batch order (the work would grow
 // with the square of the batch, and a large grid leaves a short tail anyway).  The
 // values are returned unchecked.  Called by all NT threads (it holds barriers); returns
 // the same value in all of them.
 // ---------------------------------------------------------------------------------------
-constexpr int kHeavyFirstMaxBatch = 1024;
+constexpr int kRankedMaxBatch = 1024;
 
 struct SpecSeq {
     int b, sb, Tb, hd, cm;   // batch row, state row, positions, ring head, committed records
 };
 
 template <int NT>
-__device__ SpecSeq spec_sequence_heavy_first(int rank, int batch, int L, int T, const int32_t* slot,
-                                             const int32_t* n_pos_seq, const int32_t* head,
-                                             const int32_t* committed) {
+__device__ SpecSeq spec_sequence_ranked(int rank, int batch, int L, int T, const int32_t* slot,
+                                        const int32_t* n_pos_seq, const int32_t* head,
+                                        const int32_t* committed, int lead_num, int lead_den) {
     constexpr int NW = NT / kWave;
     __shared__ int s_cnt[NW];
     __shared__ SpecSeq s_pick;
@@ -231,7 +234,7 @@ __device__ SpecSeq spec_sequence_heavy_first(int rank, int batch, int L, int T, 
         r.cm = committed[i];
         return r;
     };
-    if (batch > kHeavyFirstMaxBatch) return load(rank);
+    if (batch > kRankedMaxBatch) return load(rank);
     int nheavy = 0;
     if (batch > NT) {   // more than one chunk: count the folding sequences first
         for (int c0 = 0; c0 < batch; c0 += NT) {
@@ -261,7 +264,9 @@ __device__ SpecSeq spec_sequence_heavy_first(int rank, int batch, int L, int T, 
         }
         if (batch <= NT) nheavy = hc;
         const int hb = hw + __popcll(m & __lanemask_lt());   // folding ones before i in the chunk
-        const int pos = h ? before_h + hb : nheavy + before_l + (tid - hb);
+        const int lead = ((batch - nheavy) * lead_num) / lead_den;   // others ranked first
+        const int li = before_l + (tid - hb);                         // index among the others
+        const int pos = h ? lead + before_h + hb : (li < lead ? li : nheavy + li);
         if (in && pos == rank) s_pick = mine;
         before_h += hc;
         before_l += min(NT, batch - c0) - hc;

@@ -126,12 +126,13 @@ gdn_replay_kernel(GdnArgs a) {
     // A pad row (state slot -1, or no positions) is skipped; a slot or position count
     // out of range, or a bad cursor, is flagged and skipped.  Skipped rows keep their
     // cursors (cursor_out = cursor_in) and report no flush.
-    // Speculative rounds take the sequences that fold first (their workgroups run
-    // longest); the ordering hands over the chosen sequence's cursors.
+    // Speculative rounds rank the folding sequences after three quarters of the others
+    // (measured best between first and last); the ordering hands over the chosen
+    // sequence's cursors.
     int b, sb, Tb, c = 0, hd = 0, cm = 0;
     if constexpr (MODE == kGdnSpec) {
-        const SpecSeq q = spec_sequence_heavy_first<kGdnThreads>(bk / HK, a.batch, L, T, a.slot, a.n_pos_seq,
-                                                                 a.cursor_in, a.committed);
+        const SpecSeq q = spec_sequence_ranked<kGdnThreads>(bk / HK, a.batch, L, T, a.slot, a.n_pos_seq,
+                                                            a.cursor_in, a.committed, 3, 4);
         // the pick is the same in every lane (it comes through LDS): keep it in scalar
         // registers, with everything derived from it
         b = __builtin_amdgcn_readfirstlane(q.b);

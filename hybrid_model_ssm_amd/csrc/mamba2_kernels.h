@@ -133,12 +133,13 @@ mamba2_replay_kernel(Mamba2Args a) {
     // A pad row (state slot -1, or no positions) is skipped; a slot or position count
     // out of range, or a bad cursor, is flagged and skipped.  Skipped rows keep their
     // cursors (cursor_out = cursor_in) and report no flush.
-    // Speculative rounds take the sequences that fold first (their workgroups run
-    // longest); the ordering hands over the chosen sequence's cursors.
+    // Speculative rounds rank the folding sequences after two thirds of the others
+    // (measured best between first and last); the ordering hands over the chosen
+    // sequence's cursors.
     int b, sb, Tb, c = 0, hd = 0, cm = 0;
     if constexpr (MODE == kSpec) {
-        const SpecSeq q = spec_sequence_heavy_first<kThreads>(bg / G, a.batch, L, T, a.slot, a.n_pos_seq,
-                                                              a.cursor_in, a.committed);
+        const SpecSeq q = spec_sequence_ranked<kThreads>(bg / G, a.batch, L, T, a.slot, a.n_pos_seq,
+                                                         a.cursor_in, a.committed, 2, 3);
         // the pick is the same in every lane (it comes through LDS): keep it in scalar
         // registers, with everything derived from it
         b = __builtin_amdgcn_readfirstlane(q.b);

@@ -228,7 +228,7 @@ def test_gdn_spec_full_batch_small_heads(B):
 
 
 def test_gdn_spec_batch_above_ranking_limit():
-    """A batch above the longest-first ranking's limit (1024 sequences) keeps batch order:
+    """A batch above the speculative ranking's limit (1024 sequences) keeps batch order:
     B=1100 (2 value heads, 1 q/k head, dk = dv = 64, L=16, 4 positions) for 6 rounds with
     folds against the oracle."""
     B, HV, HK, dk, dv, L, T = 1100, 2, 1, 64, 64, 16, 4

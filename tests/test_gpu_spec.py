@@ -236,7 +236,7 @@ def test_spec_full_batch_small_heads(B):
 
 
 def test_spec_batch_above_ranking_limit():
-    """A batch above the longest-first ranking's limit (1024 sequences) keeps batch order:
+    """A batch above the speculative ranking's limit (1024 sequences) keeps batch order:
     B=1100 (H=2, G=1, P=N=16, L=16, 4 positions) for 6 rounds with folds, every output,
     flushed flag and cursor against the oracle."""
     B, H, P, N, G, L, T = 1100, 2, 16, 16, 1, 16, 4
