@@ -305,3 +305,13 @@ def test_read_then_write_probe_rejects_invalid_arguments_before_launching():
     for bad in (dict(src=0), dict(src=src + 4), dict(sink=0), dict(n=0), dict(n=per_wg + 4), dict(wf=-1024),
                 dict(wf=1022), dict(dst=0), dict(dst=dst + 8)):
         assert call(**bad) == 1, bad
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """With no built library the binding raises on first use; there is no other route."""
+    monkeypatch.setattr(rs, "_lib", None)
+    monkeypatch.setattr(rs, "LIB_PATH", str(tmp_path / "libreplayssm.so"))
+    with pytest.raises(rs.ReplaySSMLibraryMissing, match="missing"):
+        rs.lib()
+    with pytest.raises(rs.ReplaySSMLibraryMissing):      # every wrapper loads through lib()
+        rs.version()
