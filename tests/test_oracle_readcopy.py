@@ -77,3 +77,34 @@ def test_bf16_and_f16_copies():
         err = np.abs(fn(h) - h)
         bound = rc.copy_error_bound(h, kind)
         assert np.all(err <= bound) and np.max(err / bound) > 0.5, kind
+
+
+
+def test_e4m3_matches_torch_cast():
+    # independent pin: torch's CPU cast to float8_e4m3fn rounds to nearest, ties to even;
+    # it turns values past the largest finite into NaN instead of saturating, so the
+    # inputs stay within +-448
+    import pytest
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal(40000) * np.exp(rng.uniform(-14, 6, 40000))).astype(np.float32)
+    x = np.concatenate([x[np.abs(x) <= 448], np.float32([0.0, -0.0, 448.0, -448.0, 2.0 ** -10])])
+    lib8 = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(rc.e4m3_encode(x), lib8)
+
+
+def test_bf16_and_f16_copies_match_bitwise_rounding():
+    # independent forms: bf16 keeps the upper 16 bits of the fp32 word after adding
+    # 0x7FFF plus the kept part's lowest bit (round to nearest, ties to even); fp16 rounds
+    # |x| to its binade's grid (10 mantissa bits, subnormal step 2**-24) half to even
+    rng = np.random.default_rng(7)
+    y = (rng.standard_normal(40000) * np.exp(rng.uniform(-20, 20, 40000))).astype(np.float32)
+    y = np.concatenate([y, np.float32([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -0.0, 2.0 ** -130])])
+    u = y.view(np.uint32).astype(np.uint64)
+    bf = (((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)).view(np.float32)
+    assert np.array_equal(np.asarray(rc.bf16_copy(y), np.float32), bf)
+    z = y[np.abs(y) < 65504].astype(np.float64)
+    e = np.maximum(np.floor(np.log2(np.where(z != 0, np.abs(z), 1.0))), -14)
+    step = np.ldexp(1.0, (e - 10).astype(int))
+    f16 = np.round(z / step) * step
+    assert np.array_equal(np.asarray(rc.f16_copy(z.astype(np.float32)), np.float64), f16)
