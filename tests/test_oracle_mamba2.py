@@ -376,3 +376,41 @@ def test_round_bf16_matches_library_cast():
                         np.array([0.0, -0.0, 1.0, 3.0e38, 1e-40, 1.00390625, 1.01171875], np.float32)])
     ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(synth.round_bf16(a), ref)
+
+
+def test_constant_dt_is_a_first_order_iir_filter():
+    """With dt fixed per head, every state element is a first-order IIR filter of its
+    input dt * x_t[p] * B_t[n] with pole exp(dt * A): scipy's lfilter (a library routine
+    the oracle does not use) gives the state sequence from the initial state, and the
+    output follows from it.  Both oracle forms, across several flushes, must match it."""
+    from scipy.signal import lfilter
+    rng = np.random.default_rng(21)
+    Bt, H, P, N, G, L, T = 1, 3, 4, 5, 1, 4, 11
+    A, D, dt_bias, h0 = _rand_case(rng, Bt, H, P, N, G)
+    dt_raw = rng.standard_normal((Bt, H))
+    steps = []
+    for _ in range(T):
+        s = _rand_step(rng, Bt, H, P, N, G)
+        s["dt_raw"] = dt_raw
+        steps.append(s)
+    dt = om.softplus(dt_raw[0] + dt_bias)                       # [H]
+    pole = np.exp(dt * A)
+    u = np.stack([dt[:, None, None] * s["x"][0][:, :, None] * s["B"][0, 0][None, None, :]
+                  for s in steps])                              # [T,H,P,N]
+    hs = np.empty_like(u)
+    for h in range(H):
+        # zi carries h0 into the first output: y_0 = pole * h0 + u_0
+        zi = (pole[h] * h0[0, h])[None]
+        hs[:, h], _ = lfilter([1.0], [1.0, -pole[h]], u[:, h], axis=0, zi=zi)
+    hc = h0.copy()
+    rep = om.Mamba2Replay(h0, L, A, D, dt_bias, G)
+    for t, s in enumerate(steps):
+        y = np.einsum("hpn,n->hp", hs[t], s["C"][0, 0]) + D[:, None] * s["x"][0]
+        ref = y * s["z"][0] / (1 + np.exp(-s["z"][0]))
+        hc, out = om.conventional_step(hc, **s, dt_bias=dt_bias, A=A, D=D)
+        assert np.allclose(hc[0], hs[t], rtol=0, atol=1e-13)
+        assert np.allclose(out[0], ref, rtol=0, atol=1e-13)
+        rout, flushed = rep.step(**s)
+        assert np.allclose(rout[0], ref, rtol=0, atol=1e-13)
+        if flushed[0]:
+            assert np.allclose(rep.ckpt[0], hs[t], rtol=0, atol=1e-13)
