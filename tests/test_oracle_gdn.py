@@ -224,3 +224,47 @@ def test_gdn_spec_reset_starts_a_fresh_sequence():
     spec.ckpt[1] = S_new                    # the caller supplies the new sequence's checkpoint
     S_kept[1] = S_new
     _spec_rounds_vs_conventional(rng, spec, S_kept, 6, Bt, HV, HK, dk, dv, T)
+
+
+def test_fixed_key_and_gates_reduce_to_an_iir_filter():
+    """With a fixed unit key k and fixed alpha, beta, the state's component along k,
+    s_t = S_t k, obeys s_t = alpha (1 - beta) s_{t-1} + beta v_t (a first-order IIR filter
+    that scipy's lfilter, unused by the oracle, computes), and the rest decays by alpha
+    per step: S_t = s_t k^T + alpha^t S_0 (I - k k^T).  Both oracle forms, across
+    flushes, must match it for varying q and v."""
+    from scipy.signal import lfilter
+    rng = np.random.default_rng(31)
+    Bt, HV, HK, dk, dv, L, T = 1, 4, 2, 6, 5, 4, 11
+    S0 = 0.3 * rng.standard_normal((Bt, HV, dv, dk))
+    k = rng.standard_normal((Bt, HK, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    alpha = rng.uniform(0.5, 0.99, (Bt, HV))
+    beta = rng.uniform(0.05, 0.95, (Bt, HV))
+    steps = []
+    for _ in range(T):
+        s = _rand_step(rng, Bt, HV, HK, dk, dv)
+        s.update(k=k, alpha=alpha, beta=beta)
+        steps.append(s)
+    kh = og.heads_of_kgroups(k, HV)[0]                           # [HV, dk]
+    vs = np.stack([s["v"][0] for s in steps])                    # [T, HV, dv]
+    ref_S = np.empty((T, HV, dv, dk))
+    for h in range(HV):
+        pole = alpha[0, h] * (1 - beta[0, h])
+        s0 = S0[0, h] @ kh[h]
+        sk, _ = lfilter([1.0], [1.0, -pole], beta[0, h] * vs[:, h], axis=0, zi=(pole * s0)[None])
+        perp = S0[0, h] - np.outer(s0, kh[h])
+        for t in range(T):
+            ref_S[t, h] = np.outer(sk[t], kh[h]) + alpha[0, h] ** (t + 1) * perp
+    scale = og.default_scale(dk)
+    S = S0.copy()
+    rep = og.GDNReplay(S0, L, HK)
+    for t, s in enumerate(steps):
+        qh = og.heads_of_kgroups(s["q"], HV)[0]
+        ref_o = scale * np.einsum("hij,hj->hi", ref_S[t], qh)
+        S, o = og.conventional_step(S, **s)
+        assert np.allclose(S[0], ref_S[t], rtol=0, atol=1e-13)
+        assert np.allclose(o[0], ref_o, rtol=0, atol=1e-13)
+        ro, flushed = rep.step(**s)
+        assert np.allclose(ro[0], ref_o, rtol=0, atol=1e-13)
+        if flushed[0]:
+            assert np.allclose(rep.ckpt[0], ref_S[t], rtol=0, atol=1e-13)
