@@ -1351,7 +1351,7 @@ def main(argv=None):
     ap.add_argument("--cpu-steps", type=int, default=32)
     ap.add_argument("--profile-variant", metavar="NAME", choices=["headline"] + sorted(VARIANTS),
                     help="run W+K dispatches of one variant untimed and the calibration copy (for rocprofv3 --pmc)")
-    ap.add_argument("--profile-out", default=os.path.join("gpurun_out", "profile_variant.json"))
+    ap.add_argument("--profile-out", default="profile_variant.json")
     ap.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROFILE_JSON"))
     ap.add_argument("--sq-summarize", nargs="+", metavar="PROFILE_JSON PASS_DIR",
                     help="SQ instruction-counter passes of one profiled variant into a summary")
